@@ -1,0 +1,97 @@
+"""Byte account of a decode-attention step (host arithmetic only).
+
+The KV read of one layer is ``2 * h_kv * d_h * elem * n`` bytes: keys and values
+of every kv head, ``4096 n`` bytes for Llama-3.1-8B in fp16/bf16 ("Where
+Activation Sparsity and KV-Cache Sparsity Cross in LLM Decoding", section "The
+Byte Crossover").  The same section gives the projection parameter count
+``P = 3 d d_ff + 2 d^2 + 2 d h_kv d_h``, the crossover length
+``n* = P (1 - r_P) / (2 h_kv d_h (1 - r_KV))`` and the bandwidth-bound speedup
+limit ``B / (B - dB)``; the Sparse-to-Dense paper (Sec. 3.3 I/O complexity
+analysis) gives the per-token I/O of a draft/verify round.
+
+"Algorithmic bytes" of a call are the bytes the method itself must move:
+cache rows it reads, the query, the indices of a kept set, and its outputs.
+Scratch traffic (partials, logits, histograms) is excluded, so it counts
+against the achieved fraction of the roofline.
+"""
+from __future__ import annotations
+
+HBM_PEAK_BYTES_PER_S = 8.0e12  # MI355X HBM3E, published peak
+
+
+def elem_bytes(dtype: str) -> int:
+    return {"bf16": 2, "f32": 4}[dtype]
+
+
+# ---------------------------------------------------------------------------
+# the pages' byte account (host formulas, pinned against printed values)
+# ---------------------------------------------------------------------------
+def kv_bytes_per_layer(n: int, h_kv: int = 8, d_h: int = 128, elem: int = 2) -> int:
+    """Bytes of K and V one decode step reads for one layer at context n."""
+    return 2 * h_kv * d_h * elem * n
+
+
+def projection_params(d: int, d_ff: int, h_kv: int = 8, d_h: int = 128) -> int:
+    """Parameters of the seven projections of a layer (3 feed-forward, 4 attention)."""
+    return 3 * d * d_ff + 2 * d * d + 2 * d * h_kv * d_h
+
+
+def crossover_tokens(d: int, d_ff: int, r_p: float, r_kv: float, h_kv: int = 8,
+                     d_h: int = 128, ff_only: bool = False) -> float:
+    """Context length where projection and KV savings are equal (element size cancels)."""
+    p = 3 * d * d_ff if ff_only else projection_params(d, d_ff, h_kv, d_h)
+    return p * (1.0 - r_p) / (2.0 * h_kv * d_h * (1.0 - r_kv))
+
+
+def speedup_bound(total_bytes: float, saved_bytes: float) -> float:
+    """Upper bound on a bandwidth-bound step's speedup when saved_bytes are skipped."""
+    return total_bytes / (total_bytes - saved_bytes)
+
+
+def std_io_average(gamma: int, k: int, m_t: int, m_v: int, alpha: float) -> float:
+    """Per accepted token I/O (in cache entries) of a Sparse-to-Dense round."""
+    return (gamma * (k + m_t) + m_v + m_t) / (alpha * gamma)
+
+
+def std_break_even_alpha(gamma: int, k: int, m_t: int, m_v: int) -> float:
+    """Acceptance ratio above which the round reads less than vanilla decoding."""
+    return (k + m_t) / (m_v + m_t) + 1.0 / gamma
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes of each library call
+# ---------------------------------------------------------------------------
+def dense_step_bytes(hq: int, hkv: int, d: int, n: int, dtype: str) -> int:
+    e = elem_bytes(dtype)
+    return 2 * hkv * n * d * e + hq * d * e + hq * d * 4 + hq * 4
+
+
+def sparse_step_bytes(hq: int, hkv: int, d: int, rows_per_head, n_indexed_per_head,
+                      dtype: str) -> int:
+    """rows_per_head: kept rows read per kv head (indexed + tail), summed over heads
+    if a sequence is given; n_indexed_per_head: how many of them came by index."""
+    e = elem_bytes(dtype)
+    rows = sum(rows_per_head) if hasattr(rows_per_head, "__iter__") else rows_per_head * hkv
+    nidx = (sum(n_indexed_per_head) if hasattr(n_indexed_per_head, "__iter__")
+            else n_indexed_per_head * hkv)
+    return 2 * rows * d * e + 4 * nidx + 4 * hkv + hq * d * e + hq * d * 4 + hq * 4
+
+
+def score_bytes(hq: int, hkv: int, d: int, n: int, n_obs: int, dtype: str) -> int:
+    """One read of K, the window queries and the fp32 score output."""
+    e = elem_bytes(dtype)
+    return hkv * n * d * e + n_obs * hq * d * e + hkv * n * 4
+
+
+def select_bytes(hkv: int, n: int, kept_indices: int) -> int:
+    """One read of the score array plus the written indices and counts."""
+    return hkv * n * 4 + 4 * kept_indices + 4 * hkv
+
+
+def verify_bytes(hq: int, hkv: int, d: int, n: int, gamma: int, dtype: str) -> int:
+    e = elem_bytes(dtype)
+    return 2 * hkv * n * d * e + gamma * hq * d * e + gamma * hq * (d + 1) * 4
+
+
+def roofline_fraction(nbytes: float, seconds: float, peak: float = HBM_PEAK_BYTES_PER_S) -> float:
+    return nbytes / seconds / peak
