@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Decode-attention bench for libsparsekv on one MI355X.
+
+Headline (the JSON `value`): microseconds per top-K sparse decode-attention
+step for the Llama-3.1-8B shape at 32K context (32 query heads, 8 kv heads,
+head dim 128, bf16), 30 % of the cache kept (4 sinks + 64 recent + 9762
+entries per kv head chosen once by the 32-query observation-window score).
+The same step over the whole cache (dense split-K) runs beside it.
+
+Timing: W untimed warm-up steps, then K steps back to back on one stream
+between two HIP events, with a device synchronise on both sides; each step
+reads a different one of L "layers" (distinct caches, about 1 GB at 32K) so
+the 256 MB Infinity Cache cannot serve the working set.  Inputs are resident
+in HBM before the timed region.  The headline step is a single kernel launch,
+so its events also time the dominant kernel.
+
+Also reported in `details` (default sections): dense steps at 2K-128K, the
+per-step top-K pipeline at 128K (score -> select -> gathered attention), the
+Sparse-to-Dense round of the Qwen2-7B video workload (5 sparse drafts + one
+gamma=5 verify), one-time selection costs, and the byte-count speedup bounds.
+`--sections all` adds the 1024-head SparseMM batched step (17 GB of cache).
+
+cpu_baseline: the fp64 oracle (test infrastructure) timed on this host on a
+bounded sample of the headline step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn µs/step and % HBM roofline at 32K/128K ctx, dense vs top-K"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=8, help="distinct caches rotated at 32K")
+    ap.add_argument("--blocks", type=int, default=5, help="timed blocks (median reported)")
+    ap.add_argument("--sections", default="default", help="headline | default | all")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
+              "(the decode step shards by kv head with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import sparse_top_kv_amd as skv
+    from sparse_top_kv_amd import roofline as rf
+    import synth
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    details = {}
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    def time_steps(step, nsteps, warmup, blocks):
+        """Median over blocks of (elapsed / nsteps) in microseconds, HIP events on
+        the launch stream; step(i) enqueues step i."""
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        per = []
+        for b in range(blocks):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(nsteps):
+                step(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1000.0 / nsteps)
+        per.sort()
+        return per[len(per) // 2], per
+
+    # ------------------------------------------------------------------
+    # headline: Llama-3.1-8B shape, 32K, 30 % kept via window score once
+    # ------------------------------------------------------------------
+    L = args.layers
+    log(f"generating {L} layers of the 32K Llama-shape workload")
+    layers = []
+    for l in range(L):
+        w = synth.llama_obs(layer=l)
+        layers.append(dict(q=dev(w.q), qo=dev(w.q_obs), k=dev(w.k), v=dev(w.v)))
+    n, S, R, K = w.n, w.n_sink, w.n_recent, w.k_top
+    hq, hkv, d = w.n_q_heads, w.n_kv_heads, w.head_dim
+    p = skv.problem_for(layers[0]["qo"], layers[0]["k"])
+    ws = skv.Workspace.for_problem(p, 131072, 512)
+    for lay in layers:
+        lay["score"] = torch.empty((hkv, n), device="cuda")
+        lay["idx"] = torch.empty((hkv, S + K), dtype=torch.int32, device="cuda")
+        lay["cnt"] = torch.empty(hkv, dtype=torch.int32, device="cuda")
+        lay["out"] = torch.empty((hq, d), device="cuda")
+        lay["lse"] = torch.empty(hq, device="cuda")
+
+    def select_once(i):
+        lay = layers[i % L]
+        skv.skv_score(lay["qo"], lay["k"], n, lay["score"], ws)
+        skv.skv_select(lay["score"], n, S, R, K, lay["idx"], lay["cnt"], ws)
+
+    sel_us, _ = time_steps(select_once, L, 1, 1)
+    details["llama32k_window_score_plus_select_once_us"] = round(sel_us, 2)
+    tail = n - R
+
+    def sparse_step(i):
+        lay = layers[i % L]
+        skv.skv_attend_sparse(lay["q"], lay["k"], lay["v"], n, lay["idx"], lay["cnt"], tail,
+                              lay["out"], lay["lse"], ws)
+
+    def dense_step(i):
+        lay = layers[i % L]
+        skv.skv_attend_dense(lay["q"], lay["k"], lay["v"], n, lay["out"], lay["lse"], ws)
+
+    log("timing the 32K sparse and dense steps")
+    sp_us, sp_blocks = time_steps(sparse_step, args.steps, args.warmup, args.blocks)
+    de_us, de_blocks = time_steps(dense_step, args.steps, args.warmup, args.blocks)
+    rows = S + K + R
+    sp_bytes = rf.sparse_step_bytes(hq, hkv, d, rows, S + K, "bf16")
+    de_bytes = rf.dense_step_bytes(hq, hkv, d, n, "bf16")
+    details["llama32k_sparse_us"] = round(sp_us, 3)
+    details["llama32k_sparse_blocks_us"] = [round(x, 3) for x in sp_blocks]
+    details["llama32k_dense_us"] = round(de_us, 3)
+    details["llama32k_dense_blocks_us"] = [round(x, 3) for x in de_blocks]
+    details["llama32k_dense_hbm_frac"] = round(rf.roofline_fraction(de_bytes, de_us * 1e-6), 4)
+    details["llama32k_sparse_hbm_frac"] = round(rf.roofline_fraction(sp_bytes, sp_us * 1e-6), 4)
+    details["llama32k_speedup_measured"] = round(de_us / sp_us, 3)
+    details["llama32k_speedup_byte_bound"] = round(de_bytes / sp_bytes, 3)
+    details["llama32k_bytes"] = {"sparse": sp_bytes, "dense": de_bytes}
+
+    if args.sections != "headline":
+        del layers
+        torch.cuda.empty_cache()
+        # ------------------------------------------------------------------
+        # 128K: dense sweep and the per-step top-K pipeline with a needle
+        # ------------------------------------------------------------------
+        log("generating 2 layers of the 128K Llama-shape workload")
+        big = []
+        for l in range(2):
+            w3 = synth.llama_needle(layer=l)
+            big.append(dict(q=dev(w3.q), k=dev(w3.k), v=dev(w3.v)))
+        n3, K3 = w3.n, w3.k_top
+        out = torch.empty((hq, d), device="cuda")
+        lse = torch.empty(hq, device="cuda")
+        sweep = {}
+        for nn in (2048, 8192, 32768, 131072):
+            # windows at different offsets of the two 128K caches: distinct memory per step
+            nwin = max(1, min(64, n3 // nn))
+
+            def dstep(i, nn=nn, nwin=nwin):
+                b = big[i % 2]
+                off = ((i // 2) % nwin) * nn
+                skv.skv_attend_dense(b["q"], b["k"][:, off:], b["v"][:, off:], nn, out, lse, ws)
+
+            us, _ = time_steps(dstep, args.steps, args.warmup, 3)
+            by = rf.dense_step_bytes(hq, hkv, d, nn, "bf16")
+            sweep[str(nn)] = {"us": round(us, 3), "hbm_frac": round(rf.roofline_fraction(by, us * 1e-6), 4)}
+        details["dense_sweep"] = sweep
+        score3 = torch.empty((hkv, n3), device="cuda")
+        idx3 = torch.empty((hkv, S + K3), dtype=torch.int32, device="cuda")
+        cnt3 = torch.empty(hkv, dtype=torch.int32, device="cuda")
+
+        def topk_step(i):
+            b = big[i % 2]
+            skv.skv_score(b["q"], b["k"], n3, score3, ws)
+            skv.skv_select(score3, n3, S, R, K3, idx3, cnt3, ws)
+            skv.skv_attend_sparse(b["q"], b["k"], b["v"], n3, idx3, cnt3, n3 - R, out, lse, ws)
+
+        log("timing the 128K per-step top-K pipeline")
+        ts_us, _ = time_steps(topk_step, max(20, args.steps // 4), 5, 3)
+        ts_bytes = (hkv * n3 * d * 2 + rf.sparse_step_bytes(hq, hkv, d, S + K3 + R, S + K3, "bf16"))
+        details["llama128k_topk_step_us"] = round(ts_us, 2)
+        details["llama128k_topk_step_hbm_frac"] = round(rf.roofline_fraction(ts_bytes, ts_us * 1e-6), 4)
+        details["llama128k_topk_speedup_measured"] = round(sweep["131072"]["us"] / ts_us, 3)
+        details["llama128k_topk_speedup_byte_bound"] = round(
+            rf.dense_step_bytes(hq, hkv, d, n3, "bf16") / ts_bytes, 3)
+        del big, score3
+        torch.cuda.empty_cache()
+        # ------------------------------------------------------------------
+        # Qwen2-7B video Sparse-to-Dense round: 5 sparse drafts + 1 verify
+        # ------------------------------------------------------------------
+        log("generating the Qwen2-7B video workload")
+        wq = synth.qwen_std()
+        m_v, m_t, gamma = wq.extra["m_v"], wq.extra["m_t"], wq.extra["gamma"]
+        m = m_v + m_t
+        hq4, hkv4 = wq.n_q_heads, wq.n_kv_heads
+        L4 = 12  # 12 x 52 MB of K+V: beyond the Infinity Cache
+        kv4 = [(dev(wq.k), dev(wq.v))] + [(dev(np.roll(wq.k, l, axis=1)), dev(np.roll(wq.v, l, axis=1)))
+                                          for l in range(1, L4)]
+        qo4 = dev(wq.q_obs)
+        qd4 = [dev(np.ascontiguousarray(wq.extra["q_draft"][t])) for t in range(gamma)]
+        qv4 = dev(wq.extra["q_verify"])
+        ws4 = skv.Workspace.for_problem(skv.problem_for(qo4, kv4[0][0]), m + gamma, m_t)
+        sc4 = torch.empty((hkv4, m), device="cuda")
+        idx4 = torch.empty((hkv4, wq.k_top), dtype=torch.int32, device="cuda")
+        cnt4 = torch.empty(hkv4, dtype=torch.int32, device="cuda")
+
+        def sel4(i):
+            k4 = kv4[i % L4][0]
+            skv.skv_score(qo4, k4, m, sc4, ws4)
+            skv.skv_select(sc4, m, 0, m_t, wq.k_top, idx4, cnt4, ws4)
+
+        sel4_us, _ = time_steps(sel4, 4, 1, 1)
+        o4 = torch.empty((hq4, d), device="cuda")
+        l4 = torch.empty(hq4, device="cuda")
+        ov = torch.empty((gamma, hq4, d), device="cuda")
+        lv = torch.empty((gamma, hq4), device="cuda")
+
+        def round_std(i):
+            k4, v4 = kv4[i % L4]
+            for t in range(gamma):
+                skv.skv_attend_sparse(qd4[t], k4, v4, m + t + 1, idx4, cnt4, m_v, o4, l4, ws4)
+            skv.skv_verify(qv4, k4, v4, m + gamma, ov, lv, ws4)
+
+        def round_dense(i):
+            k4, v4 = kv4[i % L4]
+            for t in range(gamma):
+                skv.skv_attend_dense(qd4[t], k4, v4, m + t + 1, o4, l4, ws4)
+
+        def verify_only(i):
+            k4, v4 = kv4[i % L4]
+            skv.skv_verify(qv4, k4, v4, m + gamma, ov, lv, ws4)
+
+        log("timing the Sparse-to-Dense round")
+        r_us, _ = time_steps(round_std, max(20, args.steps // 4), 5, 3)
+        rd_us, _ = time_steps(round_dense, max(20, args.steps // 4), 5, 3)
+        v_us, _ = time_steps(verify_only, args.steps, args.warmup, 3)
+        v_bytes = rf.verify_bytes(hq4, hkv4, d, m + gamma, gamma, "bf16")
+        draft_bytes = sum(rf.sparse_step_bytes(hq4, hkv4, d, wq.k_top + m_t + t + 1, wq.k_top, "bf16")
+                          for t in range(gamma))
+        dense_round_bytes = sum(rf.dense_step_bytes(hq4, hkv4, d, m + t + 1, "bf16") for t in range(gamma))
+        details["qwen_std"] = {
+            "text_window_score_plus_select_once_us": round(sel4_us, 1),
+            "round_5_drafts_plus_verify_us": round(r_us, 2),
+            "dense_5_steps_us": round(rd_us, 2),
+            "verify_us": round(v_us, 3),
+            "verify_hbm_frac": round(rf.roofline_fraction(v_bytes, v_us * 1e-6), 4),
+            "round_speedup_measured_alpha1": round(rd_us / r_us, 3),
+            "round_speedup_byte_bound_alpha1": round(dense_round_bytes / (draft_bytes + v_bytes), 3),
+        }
+        del kv4
+        torch.cuda.empty_cache()
+
+    if args.sections == "all":
+        log("generating the 1024-head SparseMM workload (17 GB)")
+        w5 = synth.sparsemm_heads()
+        n5, H5, R5 = w5.n, w5.n_q_heads, w5.n_recent
+        ex = w5.extra
+        q5, qo5, k5, v5 = dev(w5.q), dev(w5.q_obs), dev(w5.k), dev(w5.v)
+        del w5
+        ws5 = skv.Workspace.for_problem(skv.problem_for(qo5, k5), n5, ex["W"])
+        kb, _ = skv.skv_budgets(ex["head_scores"], ex["total_budget"], ex["window"], ex["rho"], n5 - R5)
+        kdev = dev(kb)
+        sc5 = torch.empty((H5, n5), device="cuda")
+        idx5 = torch.empty((H5, int(kb.max())), dtype=torch.int32, device="cuda")
+        cnt5 = torch.empty(H5, dtype=torch.int32, device="cuda")
+
+        def sel5(i):
+            skv.skv_score(qo5, k5, n5, sc5, ws5)
+            skv.skv_select(sc5, n5, 0, R5, 0, idx5, cnt5, ws5, k_per_head=kdev, k_max=int(kb.max()))
+
+        s5_us, _ = time_steps(sel5, 2, 1, 1)
+        o5 = torch.empty((H5, d), device="cuda")
+        l5 = torch.empty(H5, device="cuda")
+
+        def step5(i):
+            skv.skv_attend_sparse(q5, k5, v5, n5, idx5, cnt5, n5 - R5, o5, l5, ws5)
+
+        st5_us, _ = time_steps(step5, args.steps, args.warmup, 3)
+        b5 = rf.sparse_step_bytes(H5, H5, d, [int(x) + R5 for x in kb], [int(x) for x in kb], "bf16")
+        details["sparsemm_1024h"] = {
+            "window_score_plus_select_once_us": round(s5_us, 1),
+            "batched_sparse_step_us": round(st5_us, 2),
+            "hbm_frac": round(rf.roofline_fraction(b5, st5_us * 1e-6), 4),
+            "byte_bound_vs_dense": round(rf.dense_step_bytes(H5, H5, d, n5, "bf16") / b5, 1),
+        }
+
+    # ------------------------------------------------------------------
+    # CPU baseline: the oracle on a bounded sample of the headline step
+    # ------------------------------------------------------------------
+    import oracle
+    log("timing the fp64 oracle on the host")
+    w0 = synth.llama_obs(layer=0)
+    _, s32 = oracle.score(w0.q_obs, w0.k, n)
+    oi, oc = oracle.select(s32, S, R, K)
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.attend_sparse(w0.q, w0.k, w0.v, n, oi, oc, tail, nthreads=threads)
+        reps += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds:
+            break
+    cpu_us = (time.perf_counter() - t0) / reps * 1e6
+
+    line = {
+        "metric": METRIC,
+        "value": round(sp_us, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sp_us / 1000.0, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-3.1-8B-shape single-sequence decode attention, 32K context, top-K sparse "
+                        "step over 30% of the cache (4 sinks + 64 recent + 9762 by 32-query window score)",
+            "q_heads": hq, "kv_heads": hkv, "head_dim": d, "context": n, "kept_rows_per_kv_head": rows,
+            "layers_rotated": L, "timing": f"median of {args.blocks} blocks x {args.steps} steps",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(sp_bytes / (sp_us * 1e-6) / 1e9, 1),
+            "peak": 8000.0,
+            "unit": "GB/s",
+            "frac": round(rf.roofline_fraction(sp_bytes, sp_us * 1e-6), 4),
+            "traffic": None,
+            "kernel": "attend_kernel<bf16, d=128, G=4, sparse>",
+            "algorithmic_bytes_per_launch": sp_bytes,
+        },
+        "cpu_baseline": {
+            "value": round(cpu_us, 1),
+            "unit": "us/step",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"{reps} fp64 oracle runs of the headline sparse step (32 heads x {rows} kept rows) "
+                      f"on one layer, {args.cpu_seconds:.0f} s budget",
+        },
+        "details": details,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+/* sparsekv.h -- C ABI of libsparsekv: single-sequence decode attention over a
+ * long KV cache with sparse top-K KV selection, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [StD] "Sparse-to-Dense: A Free Lunch for Lossless Acceleration of Video
+ *         Understanding in LLMs": Sec. 3.1 Decoding Procedures (gamma drafted
+ *         tokens verified in one dense pass), Sec. 3.2 Model with Sparse
+ *         Attention (Cache_s[l] = argTopK of text-query attention averaged over
+ *         the text tokens; GQA scores summed within each group; selection per
+ *         kv head), Sec. 3.3 I/O complexity analysis, App. A Preliminary.
+ *   [BX]  "Where Activation Sparsity and KV-Cache Sparsity Cross in LLM
+ *         Decoding": "Speedup Across Context" (cache scored once by the last
+ *         prompt queries, four sinks, highest-scoring entries per kv head,
+ *         every step read by a split-K decoding kernel), header figure (sinks,
+ *         scored history, run of recent entries), "The Attention Baseline".
+ *   [SMM] blog on SparseMM, "Head Sparsity Emerges from Visual Concept
+ *         Responses in MLLMs": method section (Local Window Cache w,
+ *         Uniform-Based Cache rho, Score-Preferred Cache; observation window of
+ *         the last 32 queries; K = r + b_score per head).
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or retains them.  Host pointers are marked (host).
+ *   - dtype of q, K and V: SKV_BF16 (raw bf16, 2 bytes) or SKV_F32.  Outputs
+ *     (out, lse, score) are always fp32.
+ *   - K and V share one layout: element (h, j, t) of kv head h, position j,
+ *     channel t is at base[h * kv_head_stride + j * kv_pos_stride + t]
+ *     (strides in elements; channels contiguous; base and both strides must be
+ *     multiples of 16 bytes).
+ *   - Query rows are contiguous [rows][Hq][d]; query head g reads kv head
+ *     g / G with G = Hq / Hkv.
+ *   - Scratch: a caller-provided device workspace of at least
+ *     skv_workspace_size() bytes, 256-byte aligned.  Its first
+ *     SKV_WS_HEADER_BYTES hold completion counters that must be zero before
+ *     the first call (skv_workspace_init does that) and that every call
+ *     returns to zero; two calls that share one workspace must not overlap
+ *     in time (same stream, or ordered by events).
+ *   - Streams: every call only enqueues work on `stream` (a hipStream_t; NULL
+ *     is the null stream) and returns without synchronising.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; on a validation error nothing is enqueued.  A failed launch
+ *     returns SKV_ERR_HIP.
+ *   - Determinism: identical inputs give bit-identical outputs (fixed
+ *     reduction orders, no floating-point atomics).
+ */
+#ifndef SPARSEKV_H
+#define SPARSEKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SKV_OK = 0,
+  SKV_ERR_INVALID_ARG = 1, /* null pointer, bad size, stride, range or alignment */
+  SKV_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, group size not supported */
+  SKV_ERR_WORKSPACE = 3,   /* workspace smaller than skv_workspace_size() */
+  SKV_ERR_HIP = 4          /* a HIP launch failed */
+} skv_status;
+
+typedef enum { SKV_F32 = 0, SKV_BF16 = 1 } skv_dtype;
+
+#define SKV_WS_HEADER_BYTES 65536
+
+typedef struct {
+  int32_t n_q_heads;      /* Hq (layers x heads may be flattened into heads)     */
+  int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0; G = Hq / Hkv in {1,2,4,7,8}    */
+  int32_t head_dim;       /* d in {64, 128}                                       */
+  int32_t dtype;          /* skv_dtype of q, K, V                                 */
+  float scale;            /* softmax scale on q.k; <= 0 selects 1/sqrt(d)         */
+  int32_t reserved;       /* must be 0                                            */
+  int64_t kv_head_stride; /* elements between kv heads (>= n_cap * kv_pos_stride) */
+  int64_t kv_pos_stride;  /* elements between positions (>= d)                    */
+} skv_problem;
+
+/* Bytes of workspace every call below needs for caches of length <= n_max and
+ * at most rows_max query rows per call (n_obs for skv_score, gamma for
+ * skv_verify, 1 otherwise).  Returns 0 for an invalid problem. */
+size_t skv_workspace_size(const skv_problem* p, int64_t n_max, int32_t rows_max);
+
+/* Zero the workspace's completion counters (enqueued on `stream`).  Needed
+ * once after the workspace is allocated. */
+skv_status skv_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Score ([StD] Sec. 3.2 equation and GQA rule; [SMM] observation window;
+ * [BX] scoring by the last prompt queries).  q: [n_obs][Hq][d]; window query i
+ * sits at position n - n_obs + i and sees keys j <= n - n_obs + i.  With
+ * l = scale * q.k and P the row's softmax over its visible keys,
+ *   score[h * score_stride + j] = (1/n_obs) * sum_{g in group h} sum_i P_{g,i}(j)
+ * for j < n (0 for keys no window query sees).  n_obs = 1 is the per-step score
+ * of the decode query at position n - 1.  Requires 1 <= n_obs <= n,
+ * score_stride >= n. */
+skv_status skv_score(const skv_problem* p, const void* q, int32_t n_obs, const void* k,
+                     int64_t n, float* score, int64_t score_stride, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Select ([BX] sinks + highest-scoring entries + recent run; [SMM] top-K by
+ * window score with the local window kept apart; [StD] argTopK per kv head).
+ *   recent window = [max(n - n_recent, 0), n): not written, attended as the tail
+ *   sinks         = [0, min(n_sink, max(n - n_recent, 0)))
+ *   candidates    = [n_sink, n - n_recent) (empty if n_sink >= n - n_recent)
+ * Keeps K_h = clamp(k_per_head ? k_per_head[h] : k_uniform, 0, #candidates)
+ * candidates, ordered by (score descending, index ascending) on the fp32 bits
+ * (-0.0 equals +0.0).  Writes idx[h * idx_stride + i], i < count[h], the sinks
+ * and kept candidates in ascending order, and count[h] = #sinks + K_h.
+ * k_per_head is a device array or NULL; k_max (host) bounds every K_h and
+ * idx_stride >= n_sink + k_max.  Scores must be finite. */
+skv_status skv_select(const skv_problem* p, const float* score, int64_t score_stride,
+                      int64_t n, int32_t n_sink, int32_t n_recent,
+                      const int32_t* k_per_head, int32_t k_uniform, int32_t k_max,
+                      int32_t* idx, int64_t idx_stride, int32_t* count, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Sparse decode attention ([StD] Sec. 3.2 top-K attention, Sec. 3.3 draft
+ * reads K selected entries plus the text run; [BX] kept set read by one
+ * split-K kernel call).  The decode query q [Hq][d] attends, per kv head h, to
+ * idx[h * idx_stride + i] for i < count[h] followed by the contiguous tail
+ * [tail_start, n).  Every idx entry must be unique and < tail_start;
+ * 0 <= count[h] <= idx_stride (device values, checked by the kernel only
+ * against idx_stride).  Writes out [Hq][d] and lse [Hq] (natural-log
+ * normaliser of scale * q.k over the set; -inf and out = 0 for an empty set;
+ * lse may be NULL). */
+skv_status skv_attend_sparse(const skv_problem* p, const void* q, const void* k,
+                             const void* v, int64_t n, const int32_t* idx,
+                             int64_t idx_stride, const int32_t* count, int64_t tail_start,
+                             float* out, float* lse, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* Dense decode attention ([BX] "The Attention Baseline": the dense step reads
+ * the whole cache through the same split-K kernel): q [Hq][d] over keys
+ * [0, n).  out [Hq][d], lse [Hq] (may be NULL). */
+skv_status skv_attend_dense(const skv_problem* p, const void* q, const void* k,
+                            const void* v, int64_t n, float* out, float* lse, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Verify ([StD] Sec. 3.1: the dense model checks all gamma drafted tokens in
+ * one pass over the full cache).  The gamma new entries already occupy
+ * positions n - gamma .. n - 1; query t (q [gamma][Hq][d]) sits at n - gamma + t
+ * and sees keys [0, n - gamma + t].  out [gamma][Hq][d], lse [gamma][Hq] (may be
+ * NULL).  Requires bf16 and 1 <= gamma <= min(n, 16). */
+skv_status skv_verify(const skv_problem* p, const void* q, int32_t gamma, const void* k,
+                      const void* v, int64_t n, float* out, float* lse, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Per-head budgets ([SMM] method section), host only.  For N heads with
+ * visual scores s (host), total budget B, local window w and share rho:
+ *   r = rho (B - N w) / N,  B_remain = B - N w - rho (B - N w),
+ *   b_score_i = B_remain s_i / sum s,   b_i = w + r + b_score_i.
+ * Writes k_out[i] = floor(r + b_score_i) clamped to [0, n_cand] (host) and,
+ * if b_out is not NULL, b_i (host). */
+skv_status skv_budgets(const double* s, int32_t n_heads, double total_budget, int32_t window,
+                       double rho, int64_t n_cand, int32_t* k_out, double* b_out);
+
+const char* skv_status_string(skv_status s);
+int32_t skv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSEKV_H */

@@ -1,0 +1,46 @@
+"""Build libsparsekv.so in-tree with hipcc for gfx950 (no torch extension)."""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libsparsekv.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+SOURCES = ["api.hip", "attend.hip", "score_step.hip", "score_obs.hip", "select.hip",
+           "verify.hip", "util.hip"]
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _compile(src: str, extra_sources=()) -> str:
+    path = src if os.path.isabs(src) else os.path.join(CSRC, src)
+    obj = os.path.join(OBJ, os.path.basename(path) + ".o")
+    cmd = [HIPCC, *FLAGS, "-c", path, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed on {src}")
+    return obj
+
+
+def build(sources=None, jobs: int | None = None) -> str:
+    """Compile every source and link libsparsekv.so; returns its path."""
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = list(sources or SOURCES)
+    jobs = jobs or min(8, len(srcs), max(1, len(os.sched_getaffinity(0))))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(sys.argv[1:] or None))

@@ -1,0 +1,425 @@
+// api.hip -- the C ABI of libsparsekv: argument validation (before anything is
+// enqueued), workspace carving, launch planning and status mapping.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/sparsekv.h"
+#include "skv_kernels.h"
+
+namespace skv {
+int attend_max_chunk();
+int attend_max_merge_slots();
+int verify_max_rows();
+int verify_chunk_granule();
+int verify_max_merge_slots(int d);
+int score_obs_block_keys();
+}
+
+namespace {
+
+using skv::AttendArgs;
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kCounterSlots = SKV_WS_HEADER_BYTES / 4;
+constexpr int kVerifyMaxGamma = 16;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool group_supported(int g) { return g == 1 || g == 2 || g == 4 || g == 7 || g == 8; }
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return v && *v ? atoi(v) : dflt;
+}
+
+// Workgroup count the split-K attention aims for (4 per CU on 256 CUs).
+int target_wgs() {
+  static const int t = env_int("SKV_TARGET_WGS", 1024);
+  return t;
+}
+
+struct ChunkPlan {
+  int chunk;  // rows per workgroup
+  int cph;    // chunks per kv head
+};
+
+// Split rows_bound rows per kv head into chunks: about target_wgs() workgroups
+// in total, chunk a multiple of `granule`, at most `max_chunk`.
+ChunkPlan plan_chunks(int64_t rows_bound, int hkv, int granule, int max_chunk) {
+  const int64_t want = (target_wgs() + hkv - 1) / hkv;
+  int64_t chunk = (rows_bound + want - 1) / (want < 1 ? 1 : want);
+  chunk = (chunk + granule - 1) / granule * granule;
+  if (chunk < granule) chunk = granule;
+  if (chunk > max_chunk) chunk = max_chunk;
+  int64_t cph = (rows_bound + chunk - 1) / chunk;
+  if (cph < 1) cph = 1;
+  return {(int)chunk, (int)cph};
+}
+
+float scale_log2(const skv_problem* p) {
+  const float sc = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+  return sc * 1.4426950408889634f;
+}
+
+int elem_size(const skv_problem* p) { return p->dtype == SKV_BF16 ? 2 : 4; }
+
+skv_status check_problem(const skv_problem* p) {
+  if (!p) return SKV_ERR_INVALID_ARG;
+  if (p->n_q_heads <= 0 || p->n_kv_heads <= 0 || p->n_q_heads % p->n_kv_heads != 0)
+    return SKV_ERR_INVALID_ARG;
+  if (p->dtype != SKV_F32 && p->dtype != SKV_BF16) return SKV_ERR_INVALID_ARG;
+  if (p->reserved != 0) return SKV_ERR_INVALID_ARG;
+  if (!(p->scale == p->scale) || isinf(p->scale)) return SKV_ERR_INVALID_ARG;
+  if (p->head_dim != 64 && p->head_dim != 128) return SKV_ERR_UNSUPPORTED;
+  if (!group_supported(p->n_q_heads / p->n_kv_heads)) return SKV_ERR_UNSUPPORTED;
+  if (p->n_kv_heads > kCounterSlots) return SKV_ERR_UNSUPPORTED;
+  return SKV_OK;
+}
+
+bool aligned16(const void* x) { return ((uintptr_t)x & 15u) == 0; }
+
+// Cache pointer, strides and length n: rows of one head must not run into the
+// next head, and every 16-byte lane slice must be aligned.
+skv_status check_cache(const skv_problem* p, const void* kv, int64_t n) {
+  if (!kv || !aligned16(kv)) return SKV_ERR_INVALID_ARG;
+  if (p->kv_pos_stride < p->head_dim) return SKV_ERR_INVALID_ARG;
+  if ((p->kv_pos_stride * elem_size(p)) % 16 != 0) return SKV_ERR_INVALID_ARG;
+  if ((p->kv_head_stride * elem_size(p)) % 16 != 0) return SKV_ERR_INVALID_ARG;
+  if (p->n_kv_heads > 1 && p->kv_head_stride < n * p->kv_pos_stride) return SKV_ERR_INVALID_ARG;
+  if (p->kv_head_stride < 0) return SKV_ERR_INVALID_ARG;
+  return SKV_OK;
+}
+
+skv_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (!ws || ((uintptr_t)ws % kAlign) != 0) return SKV_ERR_INVALID_ARG;
+  if (ws_bytes < need) return SKV_ERR_WORKSPACE;
+  return SKV_OK;
+}
+
+skv_status hip_status(hipError_t e) { return e == hipSuccess ? SKV_OK : SKV_ERR_HIP; }
+
+// ---- per-call workspace requirements (header of counters + scratch) --------
+
+int attend_granule(const skv_problem* p) {
+  return 4 * skv::attend_rows_per_iter(p->dtype, p->head_dim);
+}
+
+ChunkPlan attend_plan(const skv_problem* p, int64_t rows_bound, bool sparse) {
+  const int max_chunk = sparse ? 512 : skv::attend_max_chunk();
+  return plan_chunks(rows_bound, p->n_kv_heads, attend_granule(p), max_chunk);
+}
+
+size_t attend_scratch(const skv_problem* p, const ChunkPlan& cp) {
+  const int G = p->n_q_heads / p->n_kv_heads;
+  const size_t slots = (size_t)p->n_kv_heads * cp.cph * G;
+  return align_up(slots * 2 * sizeof(float)) + align_up(slots * p->head_dim * sizeof(float));
+}
+
+bool attend_plan_ok(const skv_problem* p, const ChunkPlan& cp) {
+  const int G = p->n_q_heads / p->n_kv_heads;
+  return (int64_t)cp.cph * G <= skv::attend_max_merge_slots();
+}
+
+ChunkPlan score_step_plan(const skv_problem* p, int64_t n) {
+  return plan_chunks(n, p->n_kv_heads, attend_granule(p), skv::attend_max_chunk());
+}
+
+size_t score_step_scratch(const skv_problem* p, int64_t n) {
+  const ChunkPlan cp = score_step_plan(p, n);
+  const int G = p->n_q_heads / p->n_kv_heads;
+  return align_up((size_t)p->n_q_heads * n * sizeof(float)) +
+         align_up((size_t)p->n_kv_heads * cp.cph * G * 2 * sizeof(float));
+}
+
+size_t score_obs_scratch(const skv_problem* p, int64_t n, int32_t n_obs) {
+  const int G = p->n_q_heads / p->n_kv_heads;
+  const int64_t R = (int64_t)n_obs * G;
+  const int64_t nkb = (n + skv::score_obs_block_keys() - 1) / skv::score_obs_block_keys();
+  return align_up((size_t)p->n_kv_heads * nkb * R * 2 * sizeof(float)) +
+         align_up((size_t)p->n_kv_heads * R * sizeof(float));
+}
+
+ChunkPlan verify_plan(const skv_problem* p, int64_t n) {
+  return plan_chunks(n, p->n_kv_heads, skv::verify_chunk_granule(), 2048);
+}
+
+size_t verify_scratch(const skv_problem* p, int64_t n, int32_t gamma) {
+  const ChunkPlan cp = verify_plan(p, n);
+  const int G = p->n_q_heads / p->n_kv_heads;
+  const size_t slots = (size_t)p->n_kv_heads * cp.cph * gamma * G;
+  return align_up(slots * 2 * sizeof(float)) + align_up(slots * p->head_dim * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t skv_version(void) { return 1; }
+
+const char* skv_status_string(skv_status s) {
+  switch (s) {
+    case SKV_OK: return "ok";
+    case SKV_ERR_INVALID_ARG: return "invalid argument";
+    case SKV_ERR_UNSUPPORTED: return "unsupported problem (head_dim or group size)";
+    case SKV_ERR_WORKSPACE: return "workspace too small";
+    case SKV_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t skv_workspace_size(const skv_problem* p, int64_t n_max, int32_t rows_max) {
+  if (check_problem(p) != SKV_OK || n_max < 1 || rows_max < 1) return 0;
+  size_t s = attend_scratch(p, attend_plan(p, n_max, false));
+  size_t t = attend_scratch(p, attend_plan(p, n_max, true));
+  s = s > t ? s : t;
+  t = score_step_scratch(p, n_max);
+  s = s > t ? s : t;
+  if (p->dtype == SKV_BF16) {
+    const int32_t w = rows_max < n_max ? rows_max : (int32_t)n_max;
+    t = score_obs_scratch(p, n_max, w);
+    s = s > t ? s : t;
+    const int32_t g = w < kVerifyMaxGamma ? w : kVerifyMaxGamma;
+    t = verify_scratch(p, n_max, g);
+    s = s > t ? s : t;
+  }
+  return SKV_WS_HEADER_BYTES + s;
+}
+
+skv_status skv_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || ((uintptr_t)ws % kAlign) != 0) return SKV_ERR_INVALID_ARG;
+  if (ws_bytes < SKV_WS_HEADER_BYTES) return SKV_ERR_WORKSPACE;
+  return hip_status(skv::launch_zero_u32((uint32_t*)ws, kCounterSlots, (hipStream_t)stream));
+}
+
+skv_status skv_attend_dense(const skv_problem* p, const void* q, const void* k, const void* v,
+                            int64_t n, float* out, float* lse, void* ws, size_t ws_bytes,
+                            void* stream) {
+  skv_status st = check_problem(p);
+  if (st != SKV_OK) return st;
+  if (n < 1 || !q || !out || !aligned16(q) || !aligned16(out)) return SKV_ERR_INVALID_ARG;
+  if ((st = check_cache(p, k, n)) != SKV_OK || (st = check_cache(p, v, n)) != SKV_OK) return st;
+  const ChunkPlan cp = attend_plan(p, n, false);
+  if (!attend_plan_ok(p, cp)) return SKV_ERR_UNSUPPORTED;
+  if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + attend_scratch(p, cp))) != SKV_OK)
+    return st;
+  const int G = p->n_q_heads / p->n_kv_heads;
+  char* base = (char*)ws;
+  const size_t slots = (size_t)p->n_kv_heads * cp.cph * G;
+  AttendArgs a{};
+  a.q = q;
+  a.k = (const char*)k;
+  a.v = (const char*)v;
+  a.head_stride_b = p->kv_head_stride * elem_size(p);
+  a.pos_stride_b = p->kv_pos_stride * elem_size(p);
+  a.n = n;
+  a.n_kv_heads = p->n_kv_heads;
+  a.chunk = cp.chunk;
+  a.chunks_per_head = cp.cph;
+  a.scale_log2 = scale_log2(p);
+  a.part_ml = (float*)(base + SKV_WS_HEADER_BYTES);
+  a.part_acc = (float*)(base + SKV_WS_HEADER_BYTES + align_up(slots * 2 * sizeof(float)));
+  a.counters = (uint32_t*)base;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(skv::launch_attend(p->dtype, p->head_dim, G, false, a, (hipStream_t)stream));
+}
+
+skv_status skv_attend_sparse(const skv_problem* p, const void* q, const void* k, const void* v,
+                             int64_t n, const int32_t* idx, int64_t idx_stride,
+                             const int32_t* count, int64_t tail_start, float* out, float* lse,
+                             void* ws, size_t ws_bytes, void* stream) {
+  skv_status st = check_problem(p);
+  if (st != SKV_OK) return st;
+  if (n < 1 || !q || !out || !aligned16(q) || !aligned16(out)) return SKV_ERR_INVALID_ARG;
+  if (!count || (!idx && idx_stride > 0) || idx_stride < 0) return SKV_ERR_INVALID_ARG;
+  if (tail_start < 0 || tail_start > n) return SKV_ERR_INVALID_ARG;
+  if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
+  if ((st = check_cache(p, k, n)) != SKV_OK || (st = check_cache(p, v, n)) != SKV_OK) return st;
+  int64_t idx_rows = idx_stride < tail_start ? idx_stride : tail_start;
+  const ChunkPlan cp = attend_plan(p, idx_rows + (n - tail_start), true);
+  if (!attend_plan_ok(p, cp)) return SKV_ERR_UNSUPPORTED;
+  if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + attend_scratch(p, cp))) != SKV_OK)
+    return st;
+  const int G = p->n_q_heads / p->n_kv_heads;
+  char* base = (char*)ws;
+  const size_t slots = (size_t)p->n_kv_heads * cp.cph * G;
+  AttendArgs a{};
+  a.q = q;
+  a.k = (const char*)k;
+  a.v = (const char*)v;
+  a.head_stride_b = p->kv_head_stride * elem_size(p);
+  a.pos_stride_b = p->kv_pos_stride * elem_size(p);
+  a.n = n;
+  a.idx = idx;
+  a.idx_stride = idx_stride;
+  a.count = count;
+  a.count_max = idx_rows;  // unique entries below tail_start: never more than this
+  a.tail_start = tail_start;
+  a.n_kv_heads = p->n_kv_heads;
+  a.chunk = cp.chunk;
+  a.chunks_per_head = cp.cph;
+  a.scale_log2 = scale_log2(p);
+  a.part_ml = (float*)(base + SKV_WS_HEADER_BYTES);
+  a.part_acc = (float*)(base + SKV_WS_HEADER_BYTES + align_up(slots * 2 * sizeof(float)));
+  a.counters = (uint32_t*)base;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(skv::launch_attend(p->dtype, p->head_dim, G, true, a, (hipStream_t)stream));
+}
+
+skv_status skv_score(const skv_problem* p, const void* q, int32_t n_obs, const void* k, int64_t n,
+                     float* score, int64_t score_stride, void* ws, size_t ws_bytes, void* stream) {
+  skv_status st = check_problem(p);
+  if (st != SKV_OK) return st;
+  if (n < 1 || n_obs < 1 || n_obs > n || !q || !score || score_stride < n || !aligned16(q))
+    return SKV_ERR_INVALID_ARG;
+  if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
+  if ((st = check_cache(p, k, n)) != SKV_OK) return st;
+  const int G = p->n_q_heads / p->n_kv_heads;
+  char* base = (char*)ws;
+  if (n_obs == 1) {
+    const ChunkPlan cp = score_step_plan(p, n);
+    if (!attend_plan_ok(p, cp)) return SKV_ERR_UNSUPPORTED;
+    if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + score_step_scratch(p, n))) != SKV_OK)
+      return st;
+    skv::ScoreStepArgs a{};
+    a.q = q;
+    a.k = (const char*)k;
+    a.head_stride_b = p->kv_head_stride * elem_size(p);
+    a.pos_stride_b = p->kv_pos_stride * elem_size(p);
+    a.n = n;
+    a.n_kv_heads = p->n_kv_heads;
+    a.chunk = cp.chunk;
+    a.chunks_per_head = cp.cph;
+    a.scale_log2 = scale_log2(p);
+    a.logits = (float*)(base + SKV_WS_HEADER_BYTES);
+    a.part_ml = (float*)(base + SKV_WS_HEADER_BYTES +
+                         align_up((size_t)p->n_q_heads * n * sizeof(float)));
+    a.score = score;
+    a.score_stride = score_stride;
+    return hip_status(skv::launch_score_step(p->dtype, p->head_dim, G, a, (hipStream_t)stream));
+  }
+  if (p->dtype != SKV_BF16) return SKV_ERR_UNSUPPORTED;  // window scoring runs on bf16 MFMA
+  if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + score_obs_scratch(p, n, n_obs))) != SKV_OK)
+    return st;
+  const int64_t R = (int64_t)n_obs * G;
+  const int64_t nkb = (n + skv::score_obs_block_keys() - 1) / skv::score_obs_block_keys();
+  skv::ScoreObsArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const char*)k;
+  a.head_stride_b = p->kv_head_stride * 2;
+  a.pos_stride_b = p->kv_pos_stride * 2;
+  a.n = n;
+  a.n_obs = n_obs;
+  a.n_kv_heads = p->n_kv_heads;
+  a.group = G;
+  a.n_kblocks = (int32_t)nkb;
+  a.scale_log2 = scale_log2(p);
+  a.part_ml = (float*)(base + SKV_WS_HEADER_BYTES);
+  a.row_lse2 = (float*)(base + SKV_WS_HEADER_BYTES +
+                        align_up((size_t)p->n_kv_heads * nkb * R * 2 * sizeof(float)));
+  a.score = score;
+  a.score_stride = score_stride;
+  return hip_status(skv::launch_score_obs(p->head_dim, a, (hipStream_t)stream));
+}
+
+skv_status skv_select(const skv_problem* p, const float* score, int64_t score_stride, int64_t n,
+                      int32_t n_sink, int32_t n_recent, const int32_t* k_per_head,
+                      int32_t k_uniform, int32_t k_max, int32_t* idx, int64_t idx_stride,
+                      int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  skv_status st = check_problem(p);
+  if (st != SKV_OK) return st;
+  (void)ws;
+  (void)ws_bytes;
+  if (n < 1 || !score || score_stride < n || n_sink < 0 || n_recent < 0 || !count)
+    return SKV_ERR_INVALID_ARG;
+  if (k_max < 0 || (!k_per_head && (k_uniform < 0 || k_uniform > k_max)))
+    return SKV_ERR_INVALID_ARG;
+  if (idx_stride < (int64_t)n_sink + k_max || (idx_stride > 0 && !idx)) return SKV_ERR_INVALID_ARG;
+  if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
+  skv::SelectArgs a{};
+  a.score = score;
+  a.score_stride = score_stride;
+  a.n = n;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  a.k_per_head = k_per_head;
+  a.k_uniform = k_uniform;
+  a.k_max = k_max;
+  a.idx = idx;
+  a.idx_stride = idx_stride;
+  a.count = count;
+  a.n_kv_heads = p->n_kv_heads;
+  return hip_status(skv::launch_select(a, (hipStream_t)stream));
+}
+
+skv_status skv_verify(const skv_problem* p, const void* q, int32_t gamma, const void* k,
+                      const void* v, int64_t n, float* out, float* lse, void* ws,
+                      size_t ws_bytes, void* stream) {
+  skv_status st = check_problem(p);
+  if (st != SKV_OK) return st;
+  if (p->dtype != SKV_BF16) return SKV_ERR_UNSUPPORTED;
+  if (gamma < 1 || gamma > kVerifyMaxGamma || n < gamma || !q || !out || !aligned16(q) ||
+      !aligned16(out))
+    return SKV_ERR_INVALID_ARG;
+  const int G = p->n_q_heads / p->n_kv_heads;
+  if (gamma * G > skv::verify_max_rows()) return SKV_ERR_UNSUPPORTED;
+  if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
+  if ((st = check_cache(p, k, n)) != SKV_OK || (st = check_cache(p, v, n)) != SKV_OK) return st;
+  const ChunkPlan cp = verify_plan(p, n);
+  if ((int64_t)cp.cph * gamma * G > skv::verify_max_merge_slots(p->head_dim)) return SKV_ERR_UNSUPPORTED;
+  if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + verify_scratch(p, n, gamma))) != SKV_OK)
+    return st;
+  char* base = (char*)ws;
+  const size_t slots = (size_t)p->n_kv_heads * cp.cph * gamma * G;
+  skv::VerifyArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const char*)k;
+  a.v = (const char*)v;
+  a.head_stride_b = p->kv_head_stride * 2;
+  a.pos_stride_b = p->kv_pos_stride * 2;
+  a.n = n;
+  a.gamma = gamma;
+  a.n_kv_heads = p->n_kv_heads;
+  a.group = G;
+  a.chunk = cp.chunk;
+  a.chunks_per_head = cp.cph;
+  a.scale_log2 = scale_log2(p);
+  a.part_ml = (float*)(base + SKV_WS_HEADER_BYTES);
+  a.part_acc = (float*)(base + SKV_WS_HEADER_BYTES + align_up(slots * 2 * sizeof(float)));
+  a.counters = (uint32_t*)base;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(skv::launch_verify(p->head_dim, a, (hipStream_t)stream));
+}
+
+skv_status skv_budgets(const double* s, int32_t n_heads, double total_budget, int32_t window,
+                       double rho, int64_t n_cand, int32_t* k_out, double* b_out) {
+  if (!s || !k_out || n_heads < 1 || window < 0 || !(rho >= 0.0 && rho <= 1.0) || n_cand < 0 ||
+      !(total_budget == total_budget))
+    return SKV_ERR_INVALID_ARG;
+  double total = 0.0;
+  for (int32_t i = 0; i < n_heads; ++i) {
+    if (!(s[i] >= 0.0) || isinf(s[i])) return SKV_ERR_INVALID_ARG;
+    total += s[i];
+  }
+  if (!(total > 0.0)) return SKV_ERR_INVALID_ARG;
+  // Local Window Cache: w per head; Uniform-Based Cache: r per head;
+  // Score-Preferred Cache: the remainder in proportion to the head score.
+  const double lwc_total = (double)n_heads * (double)window;
+  const double ubc_total = rho * (total_budget - lwc_total);
+  const double r = ubc_total / (double)n_heads;
+  const double spc_total = total_budget - lwc_total - ubc_total;
+  for (int32_t i = 0; i < n_heads; ++i) {
+    const double share = spc_total * s[i] / total;
+    double k = floor(r + share);
+    if (k < 0.0) k = 0.0;
+    if (k > (double)n_cand) k = (double)n_cand;
+    k_out[i] = (int32_t)k;
+    if (b_out) b_out[i] = (double)window + r + share;
+  }
+  return SKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,206 @@
+// score_step.hip -- per-step score of one decode query (window of one).
+//
+// Method: the score of key j for kv head h is the attention probability of
+// j summed over the query heads of h's group ("Sparse-to-Dense ..." Sec. 3.2:
+// attention scores of a GQA group are summed; top-K attention picks keys by
+// attention score):
+//   s_h(j) = sum_{g in group(h)} exp(l_g(j) - lse_g),  l = scale q.k.
+// A softmax row needs its normaliser before any probability, so the K stream
+// runs once and stores log2-domain logits plus per-chunk (max, sum) of every
+// query head (phase 1, same lane layout as the attention kernel, no V); phase
+// 2 merges the chunk statistics into lse_g and writes the group sums.
+#include "skv_common.h"
+#include "skv_kernels.h"
+
+namespace skv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kLoadsPerIter = 4;
+constexpr float kRescaleSlack = 8.0f;
+constexpr int kFinalizeKeys = 2048;  // keys per phase-2 workgroup
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kThreads) void score_logits_kernel(const ScoreStepArgs a) {
+  using RG = RowGeom<DT, D>;
+  constexpr int LPR = RG::kLanesPerRow;
+  constexpr int RPL = RG::kRowsPerLoad;
+  constexpr int U = kLoadsPerIter;
+  constexpr int RI = U * RPL;
+  static_assert(G <= LPR, "one writer lane per query head");
+
+  __shared__ float sm_m[kWaves][G], sm_l[kWaves][G];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cph = a.chunks_per_head;
+  const int h = blockIdx.x / cph;
+  const int c = blockIdx.x - h * cph;
+  const int64_t r0 = (int64_t)c * a.chunk;
+  const int64_t rem = a.n - r0;
+  const int rows = (int)(rem < 0 ? 0 : (rem > a.chunk ? a.chunk : rem));
+  const int part = lane % LPR, rgrp = lane / LPR;
+
+  uint32_t qr[G][4];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint4 t = ld16(reinterpret_cast<const char*>(a.q) +
+                         ((int64_t)(h * G + g) * D) * RG::kElem + part * 16);
+    qr[g][0] = t.x; qr[g][1] = t.y; qr[g][2] = t.z; qr[g][3] = t.w;
+  }
+  float m[G], l[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) { m[g] = kNegInf; l[g] = 0.0f; }
+
+  const char* kb = a.k + (int64_t)h * a.head_stride_b + part * 16;
+  float* lg_out = a.logits + (int64_t)(h * G + (part < G ? part : 0)) * a.n + r0;
+  const int nit_total = (rows + RI - 1) / RI;
+  const int per = (nit_total + kWaves - 1) / kWaves;
+  const int it0 = wave * per;
+  const int it1 = (it0 + per < nit_total) ? it0 + per : nit_total;
+
+  auto issue = [&](int it, uint4 (&kr)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = it * RI + u * RPL + rgrp;
+      const int rr = r < rows ? r : rows - 1;
+      kr[u] = ld16(kb + (r0 + rr) * a.pos_stride_b);
+    }
+  };
+  auto compute = [&](int it, const uint4 (&kr)[U]) {
+    float s[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = it * RI + u * RPL + rgrp;
+      const bool valid = r < rows;
+      float mine = 0.0f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float x = group_sum<LPR>(slice_dot<DT>(qr[g], kr[u])) * a.scale_log2;
+        s[u][g] = valid ? x : kNegInf;
+        mine = part == g ? x : mine;
+      }
+      if (valid && part < G) lg_out[r] = mine;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mb = s[0][g];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mb = fmaxf(mb, s[u][g]);
+      if (mb > m[g] + kRescaleSlack) {
+        l[g] *= fast_exp2(m[g] - mb);
+        m[g] = mb;
+      }
+      const float mu = (m[g] == kNegInf) ? 0.0f : m[g];
+#pragma unroll
+      for (int u = 0; u < U; ++u) l[g] += fast_exp2(s[u][g] - mu);
+    }
+  };
+
+  if (it0 < it1) {
+    uint4 ka[U], kc[U];
+    issue(it0, ka);
+    for (int it = it0; it < it1; it += 2) {
+      if (it + 1 < it1) issue(it + 1, kc);
+      compute(it, ka);
+      if (it + 1 >= it1) break;
+      if (it + 2 < it1) issue(it + 2, ka);
+      compute(it + 1, kc);
+    }
+  }
+
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float M = m[g];
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    float x = (m[g] == kNegInf) ? 0.0f : l[g] * fast_exp2(m[g] - M);
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+    if (lane == 0) { sm_m[wave][g] = M; sm_l[wave][g] = x; }
+  }
+  __syncthreads();
+  if (tid < G) {
+    const int g = tid;
+    float M = sm_m[0][g];
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][g]);
+    float L = 0.0f;
+    for (int w = 0; w < kWaves; ++w)
+      L += (sm_m[w][g] == kNegInf) ? 0.0f : sm_l[w][g] * fast_exp2(sm_m[w][g] - M);
+    float* ml = a.part_ml + (((int64_t)h * cph + c) * G + g) * 2;
+    ml[0] = M;
+    ml[1] = L;
+  }
+}
+
+// Phase 2: lse of each query head from the chunk statistics, then the group
+// sum of probabilities for kFinalizeKeys keys.
+template <int G>
+__global__ __launch_bounds__(kThreads) void score_finalize_kernel(const ScoreStepArgs a, int nblk) {
+  __shared__ float sm_lse2[G];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x / nblk;
+  const int b = blockIdx.x - h * nblk;
+  const int cph = a.chunks_per_head;
+  const int64_t nchunks = (a.n + a.chunk - 1) / a.chunk;
+  const float* ml = a.part_ml + (int64_t)h * cph * G * 2;
+  for (int g = wave; g < G; g += kWaves) {
+    float M = kNegInf;
+    for (int64_t cc = lane; cc < nchunks; cc += 64) M = fmaxf(M, ml[(cc * G + g) * 2]);
+    M = wave_max(M);
+    float L = 0.0f;
+    for (int64_t cc = lane; cc < nchunks; cc += 64) {
+      const float mc = ml[(cc * G + g) * 2];
+      L += (mc == kNegInf) ? 0.0f : ml[(cc * G + g) * 2 + 1] * fast_exp2(mc - M);
+    }
+    L = wave_sum(L);
+    if (lane == 0) sm_lse2[g] = M + __log2f(L);
+  }
+  __syncthreads();
+  float lse2[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) lse2[g] = sm_lse2[g];
+  const int64_t j0 = (int64_t)b * kFinalizeKeys;
+  for (int64_t j = j0 + tid; j < j0 + kFinalizeKeys && j < a.n; j += kThreads) {
+    float s = 0.0f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) s += fast_exp2(a.logits[(int64_t)(h * G + g) * a.n + j] - lse2[g]);
+    a.score[(int64_t)h * a.score_stride + j] = s;
+  }
+}
+
+template <int DT, int D, int G>
+hipError_t launch_g(const ScoreStepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((score_logits_kernel<DT, D, G>), dim3((unsigned)(a.n_kv_heads * a.chunks_per_head)),
+                     dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nblk = (int)((a.n + kFinalizeKeys - 1) / kFinalizeKeys);
+  hipLaunchKernelGGL((score_finalize_kernel<G>), dim3((unsigned)(a.n_kv_heads * nblk)), dim3(kThreads),
+                     0, s, a, nblk);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_d(int g, const ScoreStepArgs& a, hipStream_t s) {
+  switch (g) {
+    case 1: return launch_g<DT, D, 1>(a, s);
+    case 2: return launch_g<DT, D, 2>(a, s);
+    case 4: return launch_g<DT, D, 4>(a, s);
+    case 7: return launch_g<DT, D, 7>(a, s);
+    case 8: return launch_g<DT, D, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score_step(int dtype, int d, int g, const ScoreStepArgs& a, hipStream_t s) {
+  if (dtype == 1 && d == 128) return launch_d<1, 128>(g, a, s);
+  if (dtype == 1 && d == 64) return launch_d<1, 64>(g, a, s);
+  if (dtype == 0 && d == 128) return launch_d<0, 128>(g, a, s);
+  if (dtype == 0 && d == 64) return launch_d<0, 64>(g, a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace skv

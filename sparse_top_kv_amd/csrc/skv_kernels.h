@@ -1,0 +1,111 @@
+// skv_kernels.h -- launch descriptors shared by the C-ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skv {
+
+// Split-K decode attention over a per-kv-head row list.
+//   dense : rows of head h are positions [0, n)
+//   sparse: rows of head h are idx[h][0..count[h]) followed by [tail_start, n)
+struct AttendArgs {
+  const void* q;            // [Hq][d]
+  const char* k;            // byte pointer to element (0,0,0)
+  const char* v;
+  int64_t head_stride_b;    // bytes between kv heads
+  int64_t pos_stride_b;     // bytes between positions
+  int64_t n;
+  const int32_t* idx;       // sparse only
+  int64_t idx_stride;
+  const int32_t* count;     // sparse only
+  int64_t count_max;        // sparse only: counts are clamped to [0, count_max]
+  int64_t tail_start;       // sparse only
+  int32_t n_kv_heads;
+  int32_t chunk;            // rows per workgroup
+  int32_t chunks_per_head;  // grid = n_kv_heads * chunks_per_head
+  float scale_log2;         // scale * log2(e)
+  float* part_ml;           // [Hkv][chunks_per_head][G][2]  (max in log2 units, sum)
+  float* part_acc;          // [Hkv][chunks_per_head][G][d]
+  uint32_t* counters;       // [Hkv], zero between calls
+  float* out;               // [Hq][d]
+  float* lse;               // [Hq] or null
+};
+
+hipError_t launch_attend(int dtype, int d, int g, bool sparse, const AttendArgs& a,
+                         hipStream_t stream);
+// Rows per wave iteration of the attend kernel (the chunk must be a multiple
+// of 4x this).
+int attend_rows_per_iter(int dtype, int d);
+
+// Per-step score (one decode query): phase 1 writes log2-domain logits and
+// per-chunk (max, sum) per query head; phase 2 normalises and group-sums.
+struct ScoreStepArgs {
+  const void* q;            // [Hq][d]
+  const char* k;
+  int64_t head_stride_b, pos_stride_b;
+  int64_t n;
+  int32_t n_kv_heads;
+  int32_t chunk, chunks_per_head;
+  float scale_log2;
+  float* logits;            // [Hq][n] (log2 domain)
+  float* part_ml;           // [Hkv][chunks_per_head][G][2]
+  float* score;             // [Hkv][score_stride]
+  int64_t score_stride;
+};
+hipError_t launch_score_step(int dtype, int d, int g, const ScoreStepArgs& a, hipStream_t stream);
+
+// Observation-window score on MFMA (bf16 only): W queries x G heads per kv head.
+struct ScoreObsArgs {
+  const uint16_t* q;        // [W][Hq][d] bf16
+  const char* k;
+  int64_t head_stride_b, pos_stride_b;
+  int64_t n;
+  int32_t n_obs;            // W
+  int32_t n_kv_heads, group;
+  int32_t n_kblocks;        // key blocks of 256 per head
+  float scale_log2;
+  float* part_ml;           // [Hkv][n_kblocks][R][2], R = W * G
+  float* row_lse2;          // [Hkv][R]
+  float* score;
+  int64_t score_stride;
+};
+hipError_t launch_score_obs(int d, const ScoreObsArgs& a, hipStream_t stream);
+
+// Sinks + top-K selection by radix select on order-preserving score keys.
+struct SelectArgs {
+  const float* score;
+  int64_t score_stride;
+  int64_t n;
+  int32_t n_sink, n_recent;
+  const int32_t* k_per_head;  // device, may be null
+  int32_t k_uniform;
+  int32_t k_max;              // bound on every K_h (idx row capacity minus sinks)
+  int32_t* idx;
+  int64_t idx_stride;
+  int32_t* count;
+  int32_t n_kv_heads;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
+// Causal verify of gamma queries on MFMA (bf16).
+struct VerifyArgs {
+  const uint16_t* q;        // [gamma][Hq][d]
+  const char* k;
+  const char* v;
+  int64_t head_stride_b, pos_stride_b;
+  int64_t n;
+  int32_t gamma;
+  int32_t n_kv_heads, group;
+  int32_t chunk, chunks_per_head;
+  float scale_log2;
+  float* part_ml;           // [Hkv][chunks_per_head][R][2]
+  float* part_acc;          // [Hkv][chunks_per_head][R][d]
+  uint32_t* counters;       // [Hkv]
+  float* out;               // [gamma][Hq][d]
+  float* lse;               // [gamma][Hq] or null
+};
+hipError_t launch_verify(int d, const VerifyArgs& a, hipStream_t stream);
+
+hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t stream);
+
+}  // namespace skv

@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI: every declared entry point is exported, and
+argument validation rejects bad calls before anything reaches the GPU (all
+calls here fail validation, so they run on a CPU-only host)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import sparse_top_kv_amd as skv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "sparsekv.h")
+FAKE = 0x7F0000000000  # aligned, never dereferenced: validation fails first
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(skv_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_five_calls_and_library_exports_all():
+    names = _declared()
+    for f in ("skv_score", "skv_select", "skv_attend_sparse", "skv_attend_dense", "skv_verify"):
+        assert f in names
+    lib = ctypes.CDLL(skv.library_path())
+    for f in names:
+        assert hasattr(lib, f), f
+
+
+def _p(hq=32, hkv=8, d=128, dtype=skv.SKV_BF16, n_cap=4096):
+    return skv.problem(hq, hkv, d, dtype, n_cap * d, d)
+
+
+def _vp(x):
+    return ctypes.c_void_p(x)
+
+
+def _dense(p, n=1000, q=FAKE, ws_bytes=1 << 30, ws=FAKE):
+    lib = skv._load()
+    return lib.skv_attend_dense(ctypes.byref(p), _vp(q), _vp(FAKE), _vp(FAKE), n, _vp(FAKE), _vp(0),
+                                _vp(ws), ws_bytes, _vp(0))
+
+
+def test_problem_validation():
+    assert _dense(_p(hq=30, hkv=8)) == skv.SKV_ERR_INVALID_ARG      # Hq % Hkv
+    assert _dense(_p(hq=24, hkv=8)) == skv.SKV_ERR_UNSUPPORTED      # G = 3
+    assert _dense(_p(d=96)) == skv.SKV_ERR_UNSUPPORTED
+    assert _dense(_p(dtype=7)) == skv.SKV_ERR_INVALID_ARG
+    assert _dense(_p(), q=0) == skv.SKV_ERR_INVALID_ARG             # null
+    assert _dense(_p(), q=FAKE + 8) == skv.SKV_ERR_INVALID_ARG      # misaligned
+    assert _dense(_p(), n=0) == skv.SKV_ERR_INVALID_ARG
+    assert _dense(_p(n_cap=512), n=1000) == skv.SKV_ERR_INVALID_ARG  # heads overlap
+    assert _dense(_p(), ws_bytes=1024) == skv.SKV_ERR_WORKSPACE
+    assert _dense(_p(), ws=FAKE + 64) == skv.SKV_ERR_INVALID_ARG    # ws alignment
+    p = _p()
+    p.reserved = 1
+    assert _dense(p) == skv.SKV_ERR_INVALID_ARG
+
+
+def test_sparse_select_score_verify_validation():
+    lib = skv._load()
+    p = _p()
+    b = ctypes.byref(p)
+    big = 1 << 30
+    # tail_start outside [0, n]
+    assert lib.skv_attend_sparse(b, _vp(FAKE), _vp(FAKE), _vp(FAKE), 100, _vp(FAKE), 10, _vp(FAKE), 101,
+                                 _vp(FAKE), _vp(0), _vp(FAKE), big, _vp(0)) == skv.SKV_ERR_INVALID_ARG
+    # idx_stride < n_sink + k_max
+    assert lib.skv_select(b, _vp(FAKE), 100, 100, 4, 8, _vp(0), 10, 10, _vp(FAKE), 13, _vp(FAKE),
+                          _vp(FAKE), big, _vp(0)) == skv.SKV_ERR_INVALID_ARG
+    # k_uniform > k_max
+    assert lib.skv_select(b, _vp(FAKE), 100, 100, 4, 8, _vp(0), 11, 10, _vp(FAKE), 14, _vp(FAKE),
+                          _vp(FAKE), big, _vp(0)) == skv.SKV_ERR_INVALID_ARG
+    # score_stride < n, n_obs > n
+    assert lib.skv_score(b, _vp(FAKE), 1, _vp(FAKE), 100, _vp(FAKE), 99, _vp(FAKE), big,
+                         _vp(0)) == skv.SKV_ERR_INVALID_ARG
+    assert lib.skv_score(b, _vp(FAKE), 101, _vp(FAKE), 100, _vp(FAKE), 100, _vp(FAKE), big,
+                         _vp(0)) == skv.SKV_ERR_INVALID_ARG
+    # window scoring and verify need bf16
+    pf = _p(dtype=skv.SKV_F32)
+    assert lib.skv_score(ctypes.byref(pf), _vp(FAKE), 4, _vp(FAKE), 100, _vp(FAKE), 100, _vp(FAKE), big,
+                         _vp(0)) == skv.SKV_ERR_UNSUPPORTED
+    assert lib.skv_verify(ctypes.byref(pf), _vp(FAKE), 4, _vp(FAKE), _vp(FAKE), 100, _vp(FAKE), _vp(0),
+                          _vp(FAKE), big, _vp(0)) == skv.SKV_ERR_UNSUPPORTED
+    # gamma > n, and more than 64 verify rows per kv head
+    assert lib.skv_verify(b, _vp(FAKE), 8, _vp(FAKE), _vp(FAKE), 5, _vp(FAKE), _vp(0), _vp(FAKE), big,
+                          _vp(0)) == skv.SKV_ERR_INVALID_ARG
+    p7 = _p(hq=56, hkv=8)
+    assert lib.skv_verify(ctypes.byref(p7), _vp(FAKE), 10, _vp(FAKE), _vp(FAKE), 100, _vp(FAKE), _vp(0),
+                          _vp(FAKE), big, _vp(0)) == skv.SKV_ERR_UNSUPPORTED
+
+
+def test_workspace_size_is_monotone_and_zero_for_bad_problems():
+    p = _p(n_cap=131072)
+    sizes = [skv.skv_workspace_size(p, n, 32) for n in (1, 100, 2048, 32768, 131072)]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:]))
+    assert sizes[0] >= skv.SKV_WS_HEADER_BYTES
+    assert skv.skv_workspace_size(_p(hq=24), 100, 1) == 0
+
+
+def test_budgets_entry_point_equals_oracle():
+    rng = np.random.default_rng(5)
+    s = rng.exponential(1.0, 1024)
+    s[rng.choice(1024, 51, replace=False)] *= 20
+    k1, b1 = skv.skv_budgets(s, 1024 * 256, 32, 0.1, 32768 - 32)
+    k2, b2 = oracle.budgets(s, 1024 * 256, 32, 0.1, 32768 - 32)
+    assert np.array_equal(k1, k2)
+    np.testing.assert_allclose(b1, b2, rtol=1e-15)
+    with pytest.raises(skv.SkvError):
+        skv.skv_budgets(np.array([1.0, -1.0]), 10, 1, 0.1, 5)

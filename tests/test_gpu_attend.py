@@ -1,0 +1,219 @@
+"""GPU parity of the split-K attention, score and select kernels against the
+fp64 oracle, through the C ABI (libsparsekv.so via its Python binding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_top_kv_amd as skv
+import synth
+from gpu_util import banner, dev, host, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-3, 1e-4)}  # (out, lse) max abs error
+
+
+def _rand(shape, seed, dtype):
+    x = np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
+    return synth.bf16_bits(x) if dtype == "bf16" else x
+
+
+def _cache(hkv, n, d, seed, dtype, cap_extra=3):
+    return _rand((hkv, n + cap_extra, d), seed, dtype)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 64), (32, 8, 128), (28, 4, 128), (16, 2, 64), (16, 2, 128)])
+@pytest.mark.parametrize("n", [1, 67, 1000, 5003])
+def test_attend_dense_matches_oracle(dtype, hq, hkv, d, n):
+    banner(f"dense {dtype} hq={hq} hkv={hkv} d={d} n={n}")
+    q = _rand((hq, d), 1, dtype)
+    k = _cache(hkv, n, d, 2, dtype)
+    v = _cache(hkv, n, d, 3, dtype)
+    ref_o, ref_l = oracle.attend_dense(q, k, v, n)
+    qt, kt, vt = dev(q), dev(k), dev(v)
+    out = torch.full((hq, d), float("nan"), device="cuda")
+    lse = torch.full((hq,), float("nan"), device="cuda")
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n)
+    skv.skv_attend_dense(qt, kt, vt, n, out, lse, ws)
+    torch.cuda.synchronize()
+    to, tl = TOL[dtype]
+    assert np.abs(host(out) - ref_o).max() <= to
+    assert np.abs(host(lse) - ref_l).max() <= tl
+    # second call on the same workspace (counters must have been restored)
+    out2 = torch.zeros_like(out)
+    skv.skv_attend_dense(qt, kt, vt, n, out2, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+def _random_sets(hkv, tail_start, stride, seed, max_count=None):
+    rng = np.random.default_rng(seed)
+    idx = np.full((hkv, stride), -1, np.int32)
+    cnt = np.zeros(hkv, np.int32)
+    for h in range(hkv):
+        c = int(rng.integers(0, min(stride, tail_start) + 1)) if max_count is None else max_count
+        c = min(c, tail_start, stride)
+        sel = np.sort(rng.choice(tail_start, size=c, replace=False)).astype(np.int32)
+        idx[h, :c] = sel
+        cnt[h] = c
+    return idx, cnt
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 64), (32, 8, 128), (28, 4, 128)])
+@pytest.mark.parametrize("n,tail,stride", [(3000, 2900, 700), (5000, 5000, 1500), (800, 0, 16), (100, 90, 90)])
+def test_attend_sparse_matches_oracle(dtype, hq, hkv, d, n, tail, stride):
+    banner(f"sparse {dtype} hq={hq} hkv={hkv} d={d} n={n} tail={tail} stride={stride}")
+    q = _rand((hq, d), 4, dtype)
+    k = _cache(hkv, n, d, 5, dtype)
+    v = _cache(hkv, n, d, 6, dtype)
+    idx, cnt = _random_sets(hkv, tail, stride, 7)
+    cnt[0] = 0  # an empty indexed part
+    ref_o, ref_l = oracle.attend_sparse(q, k, v, n, idx, cnt, tail)
+    qt, kt, vt = dev(q), dev(k), dev(v)
+    out = torch.full((hq, d), float("nan"), device="cuda")
+    lse = torch.full((hq,), float("nan"), device="cuda")
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n)
+    skv.skv_attend_sparse(qt, kt, vt, n, dev(idx), dev(cnt), tail, out, lse, ws)
+    torch.cuda.synchronize()
+    to, tl = TOL[dtype]
+    o, l = host(out), host(lse)
+    empty = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(l), empty)
+    assert np.abs(o - ref_o).max() <= to
+    assert np.abs(l[~empty] - ref_l[~empty]).max(initial=0) <= tl
+
+
+@pytest.mark.parametrize("hkv,n,S,R,K", [(8, 2048, 4, 32, 256), (3, 5000, 4, 64, 1000), (2, 700, 0, 32, 650),
+                                          (4, 100, 4, 8, 0), (2, 100, 4, 8, 500), (1, 32768, 4, 64, 9762)])
+def test_select_bit_exact_on_oracle_scores(hkv, n, S, R, K):
+    banner(f"select hkv={hkv} n={n} S={S} R={R} K={K}")
+    rng = np.random.default_rng(n + K)
+    s = rng.exponential(1.0, (hkv, n)).astype(np.float32) / n
+    s[:, ::5] = s[:, 1:2]  # exact ties
+    s[0, 7] = -0.0
+    s[0, 8] = 0.0
+    ref_idx, ref_cnt = oracle.select(s, S, R, K)
+    stride = ref_idx.shape[1]
+    idx = torch.full((hkv, stride), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(hkv, dtype=torch.int32, device="cuda")
+    ws = skv.Workspace(skv.SKV_WS_HEADER_BYTES)
+    skv.skv_select(dev(s), n, S, R, K, idx, cnt, ws)
+    torch.cuda.synchronize()
+    gi, gc = host(idx), host(cnt)
+    assert np.array_equal(gc, ref_cnt)
+    for h in range(hkv):
+        assert np.array_equal(gi[h, :gc[h]], ref_idx[h, :ref_cnt[h]])
+
+
+def test_select_ragged_budgets_and_uniform_scores():
+    banner("select ragged")
+    hkv, n, S, R = 16, 3000, 0, 32
+    ks = np.array([0, 1, 5, 22, 100, 2968, 3000, 7, 1000, 2000, 3, 2, 1, 0, 500, 64], np.int32)
+    s = np.full((hkv, n), 1e-3, np.float32)  # all equal: lowest indices win
+    s[8:] = np.random.default_rng(3).random((8, n)).astype(np.float32)
+    ref_idx, ref_cnt = oracle.select(s, S, R, ks, idx_stride=3000)
+    idx = torch.full((hkv, 3000), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(hkv, dtype=torch.int32, device="cuda")
+    ws = skv.Workspace(skv.SKV_WS_HEADER_BYTES)
+    skv.skv_select(dev(s), n, S, R, 0, idx, cnt, ws, k_per_head=dev(ks), k_max=3000)
+    torch.cuda.synchronize()
+    gi, gc = host(idx), host(cnt)
+    assert np.array_equal(gc, ref_cnt)
+    for h in range(hkv):
+        assert np.array_equal(gi[h, :gc[h]], ref_idx[h, :ref_cnt[h]])
+    for h in range(8):
+        assert np.array_equal(gi[h, :gc[h]], np.arange(gc[h]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("hq,hkv,d,n", [(8, 8, 64, 2048), (32, 8, 128, 5000), (28, 4, 128, 777), (8, 8, 64, 1)])
+def test_score_step_matches_oracle(dtype, hq, hkv, d, n):
+    banner(f"score step {dtype} hq={hq} hkv={hkv} d={d} n={n}")
+    q = _rand((hq, d), 8, dtype)
+    k = _cache(hkv, n, d, 9, dtype)
+    s64, _ = oracle.score(q[None], k, n)
+    qt, kt = dev(q), dev(k)
+    score = torch.full((hkv, n + 5), float("nan"), device="cuda")
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n)
+    skv.skv_score(qt, kt, n, score, ws)
+    torch.cuda.synchronize()
+    g = host(score)[:, :n]
+    assert np.all(np.isfinite(g))
+    rel = np.abs(g - s64) / np.maximum(s64, 1e-30)
+    assert rel.max() <= 1e-4
+
+
+@pytest.mark.parametrize("trial", [0, 1, 2])
+def test_tiny_mha_pipeline(trial):
+    """Per-step path on the tiny fp32 MHA workload: score -> select -> sparse
+    attention, plus the dense step, against the oracle."""
+    banner(f"tiny mha pipeline trial={trial}")
+    w = synth.tiny_mha(trial=trial)
+    n, H, d = w.n, w.n_q_heads, w.head_dim
+    s64, s32 = oracle.score(w.q[None], w.k, n)
+    ora_idx, ora_cnt = oracle.select(s32, w.n_sink, w.n_recent, w.k_top)
+    qt, kt, vt = dev(w.q), dev(w.k), dev(w.v)
+    p = skv.problem_for(qt, kt)
+    ws = skv.Workspace.for_problem(p, n)
+    score = torch.empty((H, n), device="cuda")
+    skv.skv_score(qt, kt, n, score, ws)
+    stride = w.n_sink + w.k_top
+    idx = torch.empty((H, stride), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(H, dtype=torch.int32, device="cuda")
+    skv.skv_select(score, n, w.n_sink, w.n_recent, w.k_top, idx, cnt, ws)
+    tail = n - w.n_recent
+    out = torch.empty((H, d), device="cuda")
+    lse = torch.empty(H, device="cuda")
+    skv.skv_attend_sparse(qt, kt, vt, n, idx, cnt, tail, out, lse, ws)
+    outd = torch.empty((H, d), device="cuda")
+    lsed = torch.empty(H, device="cuda")
+    skv.skv_attend_dense(qt, kt, vt, n, outd, lsed, ws)
+    torch.cuda.synchronize()
+    gi, gc = host(idx), host(cnt)
+    assert np.array_equal(gc, ora_cnt)
+    for h in range(H):
+        gset, oset = set(gi[h, :gc[h]]), set(ora_idx[h, :ora_cnt[h]])
+        diff = gset ^ oset
+        if diff:  # only near-tied swaps at the threshold are allowed
+            cand = np.sort(s64[h, w.n_sink:tail])[::-1]
+            tau = cand[w.k_top - 1]
+            for j in diff:
+                assert abs(s64[h, j] - tau) <= 1e-5 * tau + np.finfo(np.float32).tiny
+        assert set(w.extra["heavy"].tolist()) <= gset
+    # attention error against the oracle on the GPU's own kept set
+    ref_o, ref_l = oracle.attend_sparse(w.q, w.k, w.v, n, gi, gc, tail)
+    assert np.abs(host(out) - ref_o).max() <= 1e-5
+    assert np.abs(host(lse) - ref_l).max() <= 1e-5
+    ref_d, ref_dl = oracle.attend_dense(w.q, w.k, w.v, n)
+    assert np.abs(host(outd) - ref_d).max() <= 1e-5
+    assert np.abs(host(lsed) - ref_dl).max() <= 1e-5
+
+
+def test_sparse_with_full_set_equals_dense_and_is_deterministic():
+    banner("sparse == dense with every candidate")
+    hq, hkv, d, n = 32, 8, 128, 4096
+    q = _rand((hq, d), 11, "bf16")
+    k = _cache(hkv, n, d, 12, "bf16")
+    v = _cache(hkv, n, d, 13, "bf16")
+    qt, kt, vt = dev(q), dev(k), dev(v)
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n)
+    tail = n - 64
+    idx = torch.arange(tail, dtype=torch.int32, device="cuda").repeat(hkv, 1).contiguous()
+    cnt = torch.full((hkv,), tail, dtype=torch.int32, device="cuda")
+    o1 = torch.empty((hq, d), device="cuda"); l1 = torch.empty(hq, device="cuda")
+    o2 = torch.empty((hq, d), device="cuda"); l2 = torch.empty(hq, device="cuda")
+    o3 = torch.empty((hq, d), device="cuda"); l3 = torch.empty(hq, device="cuda")
+    skv.skv_attend_sparse(qt, kt, vt, n, idx, cnt, tail, o1, l1, ws)
+    skv.skv_attend_dense(qt, kt, vt, n, o2, l2, ws)
+    skv.skv_attend_sparse(qt, kt, vt, n, idx, cnt, tail, o3, l3, ws)
+    torch.cuda.synchronize()
+    assert (o1 - o2).abs().max().item() <= 2e-3
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)

@@ -1,0 +1,94 @@
+"""GPU parity of the MFMA kernels (causal verify, observation-window score)
+against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_top_kv_amd as skv
+import synth
+from gpu_util import banner, dev, host, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _rand(shape, seed):
+    return synth.bf16_bits(np.random.default_rng(seed).standard_normal(shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(28, 4, 128), (32, 8, 128), (8, 8, 64), (16, 2, 64)])
+@pytest.mark.parametrize("gamma,n", [(5, 5), (5, 300), (1, 77), (5, 3001), (8, 1000)])
+def test_verify_matches_oracle(hq, hkv, d, gamma, n):
+    G = hq // hkv
+    if gamma * G > 64:
+        pytest.skip("more than 64 query rows per kv head")
+    banner(f"verify hq={hq} hkv={hkv} d={d} gamma={gamma} n={n}")
+    q = _rand((gamma, hq, d), 1)
+    k = _rand((hkv, n + 2, d), 2)
+    v = _rand((hkv, n + 2, d), 3)
+    ref_o, ref_l = oracle.verify(q, k, v, n)
+    qt, kt, vt = dev(q), dev(k), dev(v)
+    out = torch.full((gamma, hq, d), float("nan"), device="cuda")
+    lse = torch.full((gamma, hq), float("nan"), device="cuda")
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n, gamma)
+    skv.skv_verify(qt, kt, vt, n, out, lse, ws)
+    torch.cuda.synchronize()
+    assert np.abs(host(out) - ref_o).max() <= 2e-3
+    assert np.abs(host(lse) - ref_l).max() <= 1e-4
+    # each verify row equals the dense step at its own prefix
+    for t in range(gamma):
+        od = torch.empty((hq, d), device="cuda")
+        ld = torch.empty(hq, device="cuda")
+        skv.skv_attend_dense(qt[t].contiguous(), kt, vt, n - gamma + t + 1, od, ld, ws)
+        torch.cuda.synchronize()
+        assert (od - out[t]).abs().max().item() <= 2e-3
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (28, 4, 128), (4, 4, 64), (8, 1, 128)])
+@pytest.mark.parametrize("W,n", [(32, 32), (32, 1000), (2, 300), (32, 4097), (20, 257)])
+def test_obs_score_matches_oracle(hq, hkv, d, W, n):
+    banner(f"obs score hq={hq} hkv={hkv} d={d} W={W} n={n}")
+    q = _rand((W, hq, d), 4)
+    k = _rand((hkv, n, d), 5)
+    s64, s32 = oracle.score(q, k, n)
+    qt, kt = dev(q), dev(k)
+    score = torch.full((hkv, n + 3), float("nan"), device="cuda")
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n, W)
+    skv.skv_score(qt, kt, n, score, ws)
+    torch.cuda.synchronize()
+    g = host(score)[:, :n]
+    assert np.all(np.isfinite(g))
+    assert np.all(np.abs(g - s64) <= 1e-4 * s64 + 1e-12)
+    np.testing.assert_allclose(g.sum(1), hq // hkv, rtol=1e-4)
+
+
+def test_window_select_end_to_end_near_ties():
+    """Window score on the GPU -> select on the GPU; the kept set may differ from
+    the oracle's only by swaps of near-tied entries at the threshold."""
+    banner("obs score -> select end to end")
+    w = synth.llama_obs(n=4096)
+    n, S, R = w.n, w.n_sink, w.n_recent
+    K = int(0.3 * n) - S - R
+    s64, s32 = oracle.score(w.q_obs, w.k, n)
+    o_idx, o_cnt = oracle.select(s32, S, R, K)
+    qt, kt = dev(w.q_obs), dev(w.k)
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n, w.q_obs.shape[0])
+    score = torch.empty((w.n_kv_heads, n), device="cuda")
+    skv.skv_score(qt, kt, n, score, ws)
+    idx = torch.empty((w.n_kv_heads, S + K), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(w.n_kv_heads, dtype=torch.int32, device="cuda")
+    skv.skv_select(score, n, S, R, K, idx, cnt, ws)
+    torch.cuda.synchronize()
+    gi, gc = host(idx), host(cnt)
+    assert np.array_equal(gc, o_cnt)
+    for h in range(w.n_kv_heads):
+        gs, os_ = set(gi[h, :gc[h]]), set(o_idx[h, :o_cnt[h]])
+        tau = np.sort(s64[h, S:n - R])[::-1][K - 1]
+        for j in gs ^ os_:
+            assert abs(s64[h, j] - tau) <= 1e-5 * tau + np.finfo(np.float32).tiny
+        assert set(w.extra["heavy"][h].tolist()) <= gs
