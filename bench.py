@@ -7,12 +7,16 @@ head dim 128, bf16), 30 % of the cache kept (4 sinks + 64 recent + 9762
 entries per kv head chosen once by the 32-query observation-window score).
 The same step over the whole cache (dense split-K) runs beside it.
 
-Timing: W untimed warm-up steps, then K steps back to back on one stream
-between two HIP events, with a device synchronise on both sides; each step
-reads a different one of L "layers" (distinct caches, about 1 GB at 32K) so
-the 256 MB Infinity Cache cannot serve the working set.  Inputs are resident
-in HBM before the timed region.  The headline step is a single kernel launch,
-so its events also time the dominant kernel.
+Timing: W untimed warm-up steps, then K steps captured once into a HIP graph
+and replayed between two HIP events on the launch stream, with a device
+synchronise on both sides (median of several blocks); each step reads a
+different one of L "layers" (distinct caches, about 1 GB at 32K) so the 256 MB
+Infinity Cache cannot serve the working set.  Inputs are resident in HBM
+before the timed region.  A decode-attention step is two kernels: the split-K
+partial kernel (the dominant one) and the small log-sum-exp merge; the
+roofline figure divides the algorithmic bytes by the whole step time, so the
+merge counts against it.  Eager (one host launch per call) times are reported
+beside the graph times.
 
 Also reported in `details` (default sections): dense steps at 2K-128K, the
 per-step top-K pipeline at 128K (score -> select -> gathered attention), the
@@ -53,6 +57,8 @@ def parse():
     ap.add_argument("--blocks", type=int, default=5, help="timed blocks (median reported)")
     ap.add_argument("--sections", default="default", help="headline | default | all")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one 512 MiB device copy (counter calibration under a profiler)")
     return ap.parse_args()
 
 
@@ -78,20 +84,33 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
-    def time_steps(step, nsteps, warmup, blocks):
-        """Median over blocks of (elapsed / nsteps) in microseconds, HIP events on
-        the launch stream; step(i) enqueues step i."""
+    def time_steps(step, nsteps, warmup, blocks, graph=True):
+        """Median over blocks of (elapsed / nsteps) in microseconds, timed with HIP
+        events on the launch stream.  step(i) enqueues step i.  With graph=True the
+        nsteps launches are captured once into a HIP graph and each block replays
+        it, so host-side launch cost does not leak into the GPU time."""
         for i in range(warmup):
             step(i)
         torch.cuda.synchronize()
+        g = None
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(nsteps):
+                    step(i)
+            g.replay()
+            torch.cuda.synchronize()
         per = []
         for b in range(blocks):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             e0.record(stream)
-            for i in range(nsteps):
-                step(i)
+            if g is not None:
+                g.replay()
+            else:
+                for i in range(nsteps):
+                    step(i)
             e1.record(stream)
             torch.cuda.synchronize()
             per.append(e0.elapsed_time(e1) * 1000.0 / nsteps)
@@ -123,7 +142,7 @@ def main():
         skv.skv_score(lay["qo"], lay["k"], n, lay["score"], ws)
         skv.skv_select(lay["score"], n, S, R, K, lay["idx"], lay["cnt"], ws)
 
-    sel_us, _ = time_steps(select_once, L, 1, 1)
+    sel_us, _ = time_steps(select_once, L, 1, 1, graph=False)
     details["llama32k_window_score_plus_select_once_us"] = round(sel_us, 2)
     tail = n - R
 
@@ -139,6 +158,10 @@ def main():
     log("timing the 32K sparse and dense steps")
     sp_us, sp_blocks = time_steps(sparse_step, args.steps, args.warmup, args.blocks)
     de_us, de_blocks = time_steps(dense_step, args.steps, args.warmup, args.blocks)
+    sp_eager, _ = time_steps(sparse_step, args.steps, 2, 1, graph=False)
+    de_eager, _ = time_steps(dense_step, args.steps, 2, 1, graph=False)
+    details["llama32k_sparse_us_eager_launches"] = round(sp_eager, 3)
+    details["llama32k_dense_us_eager_launches"] = round(de_eager, 3)
     rows = S + K + R
     sp_bytes = rf.sparse_step_bytes(hq, hkv, d, rows, S + K, "bf16")
     de_bytes = rf.dense_step_bytes(hq, hkv, d, n, "bf16")
@@ -151,6 +174,15 @@ def main():
     details["llama32k_speedup_measured"] = round(de_us / sp_us, 3)
     details["llama32k_speedup_byte_bound"] = round(de_bytes / sp_bytes, 3)
     details["llama32k_bytes"] = {"sparse": sp_bytes, "dense": de_bytes}
+
+    if args.calib_copy:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        details["calib_copy_bytes"] = {"read": src.numel(), "written": dst.numel()}
+        del src, dst
 
     if args.sections != "headline":
         del layers
@@ -224,7 +256,7 @@ def main():
             skv.skv_score(qo4, k4, m, sc4, ws4)
             skv.skv_select(sc4, m, 0, m_t, wq.k_top, idx4, cnt4, ws4)
 
-        sel4_us, _ = time_steps(sel4, 4, 1, 1)
+        sel4_us, _ = time_steps(sel4, 4, 1, 1, graph=False)
         o4 = torch.empty((hq4, d), device="cuda")
         l4 = torch.empty(hq4, device="cuda")
         ov = torch.empty((gamma, hq4, d), device="cuda")
@@ -283,7 +315,7 @@ def main():
             skv.skv_score(qo5, k5, n5, sc5, ws5)
             skv.skv_select(sc5, n5, 0, R5, 0, idx5, cnt5, ws5, k_per_head=kdev, k_max=int(kb.max()))
 
-        s5_us, _ = time_steps(sel5, 2, 1, 1)
+        s5_us, _ = time_steps(sel5, 2, 1, 1, graph=False)
         o5 = torch.empty((H5, d), device="cuda")
         l5 = torch.empty(H5, device="cuda")
 

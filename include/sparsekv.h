@@ -30,11 +30,11 @@
  *   - Query rows are contiguous [rows][Hq][d]; query head g reads kv head
  *     g / G with G = Hq / Hkv.
  *   - Scratch: a caller-provided device workspace of at least
- *     skv_workspace_size() bytes, 256-byte aligned.  Its first
- *     SKV_WS_HEADER_BYTES hold completion counters that must be zero before
- *     the first call (skv_workspace_init does that) and that every call
- *     returns to zero; two calls that share one workspace must not overlap
- *     in time (same stream, or ordered by events).
+ *     skv_workspace_size() bytes, 256-byte aligned, holding split-K partials
+ *     and other per-call intermediates (its first SKV_WS_HEADER_BYTES are
+ *     reserved; skv_workspace_init zero-fills them).  Two calls that share
+ *     one workspace must not overlap in time (same stream, or ordered by
+ *     events); nothing in it needs to survive between calls.
  *   - Streams: every call only enqueues work on `stream` (a hipStream_t; NULL
  *     is the null stream) and returns without synchronising.
  *   - Errors: arguments are validated on the host before anything is
@@ -81,8 +81,8 @@ typedef struct {
  * skv_verify, 1 otherwise).  Returns 0 for an invalid problem. */
 size_t skv_workspace_size(const skv_problem* p, int64_t n_max, int32_t rows_max);
 
-/* Zero the workspace's completion counters (enqueued on `stream`).  Needed
- * once after the workspace is allocated. */
+/* Zero-fill the workspace's reserved header (enqueued on `stream`, with a
+ * fill kernel so it may sit inside a captured graph). */
 skv_status skv_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Score ([StD] Sec. 3.2 equation and GQA rule; [SMM] observation window;

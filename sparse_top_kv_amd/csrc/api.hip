@@ -9,10 +9,9 @@
 
 namespace skv {
 int attend_max_chunk();
-int attend_max_merge_slots();
+int attend_waves();
 int verify_max_rows();
 int verify_chunk_granule();
-int verify_max_merge_slots(int d);
 int score_obs_block_keys();
 }
 
@@ -33,9 +32,10 @@ int env_int(const char* name, int dflt) {
   return v && *v ? atoi(v) : dflt;
 }
 
-// Workgroup count the split-K attention aims for (4 per CU on 256 CUs).
+// Workgroup count the split-K attention aims for: one per CU on 256 CUs
+// (measured best on MI355X for 32K-128K; more chunks only add merge work).
 int target_wgs() {
-  static const int t = env_int("SKV_TARGET_WGS", 1024);
+  static const int t = env_int("SKV_TARGET_WGS", 256);
   return t;
 }
 
@@ -88,6 +88,8 @@ skv_status check_cache(const skv_problem* p, const void* kv, int64_t n) {
   if ((p->kv_head_stride * elem_size(p)) % 16 != 0) return SKV_ERR_INVALID_ARG;
   if (p->n_kv_heads > 1 && p->kv_head_stride < n * p->kv_pos_stride) return SKV_ERR_INVALID_ARG;
   if (p->kv_head_stride < 0) return SKV_ERR_INVALID_ARG;
+  // rows of one head are addressed with 32-bit byte offsets
+  if ((double)n * (double)p->kv_pos_stride * elem_size(p) >= 4294967296.0) return SKV_ERR_UNSUPPORTED;
   return SKV_OK;
 }
 
@@ -99,10 +101,11 @@ skv_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 
 skv_status hip_status(hipError_t e) { return e == hipSuccess ? SKV_OK : SKV_ERR_HIP; }
 
-// ---- per-call workspace requirements (header of counters + scratch) --------
+// ---- per-call workspace requirements (reserved header + scratch) -----------
 
+// chunk granule: one iteration of rows for every wave of a workgroup
 int attend_granule(const skv_problem* p) {
-  return 4 * skv::attend_rows_per_iter(p->dtype, p->head_dim);
+  return skv::attend_waves() * skv::attend_rows_per_iter(p->dtype, p->head_dim);
 }
 
 ChunkPlan attend_plan(const skv_problem* p, int64_t rows_bound, bool sparse) {
@@ -110,19 +113,46 @@ ChunkPlan attend_plan(const skv_problem* p, int64_t rows_bound, bool sparse) {
   return plan_chunks(rows_bound, p->n_kv_heads, attend_granule(p), max_chunk);
 }
 
-size_t attend_scratch(const skv_problem* p, const ChunkPlan& cp) {
-  const int G = p->n_q_heads / p->n_kv_heads;
-  const size_t slots = (size_t)p->n_kv_heads * cp.cph * G;
-  return align_up(slots * 2 * sizeof(float)) + align_up(slots * p->head_dim * sizeof(float));
+// Split-K scratch: partial (max, sum) and acc[d] per (kv head, chunk, row),
+// then the chunk count of every kv head.
+struct PartLayout {
+  size_t ml, acc, nch, end;
+};
+
+PartLayout part_layout(const skv_problem* p, int cph, int rows_per_head) {
+  const size_t slots = (size_t)p->n_kv_heads * cph * rows_per_head;
+  PartLayout L;
+  L.ml = SKV_WS_HEADER_BYTES;
+  L.acc = L.ml + align_up(slots * 2 * sizeof(float));
+  L.nch = L.acc + align_up(slots * p->head_dim * sizeof(float));
+  L.end = L.nch + align_up((size_t)p->n_kv_heads * sizeof(int32_t));
+  return L;
 }
 
-bool attend_plan_ok(const skv_problem* p, const ChunkPlan& cp) {
+size_t attend_scratch(const skv_problem* p, const ChunkPlan& cp) {
   const int G = p->n_q_heads / p->n_kv_heads;
-  return (int64_t)cp.cph * G <= skv::attend_max_merge_slots();
+  return part_layout(p, cp.cph, G).end - SKV_WS_HEADER_BYTES;
+}
+
+skv_status launch_partials_merge(const skv_problem* p, char* base, const PartLayout& L, int cph,
+                                 int rows_per_head, bool ragged, float* out, float* lse,
+                                 hipStream_t s) {
+  skv::MergeArgs m{};
+  m.part_ml = (const float*)(base + L.ml);
+  m.part_acc = (const float*)(base + L.acc);
+  m.nch = ragged ? (const int32_t*)(base + L.nch) : nullptr;
+  m.n_kv_heads = p->n_kv_heads;
+  m.cph = cph;
+  m.rows_per_head = rows_per_head;
+  m.group = p->n_q_heads / p->n_kv_heads;
+  m.out = out;
+  m.lse = lse;
+  return hip_status(skv::launch_merge(p->head_dim, m, s));
 }
 
 ChunkPlan score_step_plan(const skv_problem* p, int64_t n) {
-  return plan_chunks(n, p->n_kv_heads, attend_granule(p), skv::attend_max_chunk());
+  return plan_chunks(n, p->n_kv_heads, 4 * skv::attend_rows_per_iter(p->dtype, p->head_dim),
+                     skv::attend_max_chunk());
 }
 
 size_t score_step_scratch(const skv_problem* p, int64_t n) {
@@ -147,8 +177,7 @@ ChunkPlan verify_plan(const skv_problem* p, int64_t n) {
 size_t verify_scratch(const skv_problem* p, int64_t n, int32_t gamma) {
   const ChunkPlan cp = verify_plan(p, n);
   const int G = p->n_q_heads / p->n_kv_heads;
-  const size_t slots = (size_t)p->n_kv_heads * cp.cph * gamma * G;
-  return align_up(slots * 2 * sizeof(float)) + align_up(slots * p->head_dim * sizeof(float));
+  return part_layout(p, cp.cph, gamma * G).end - SKV_WS_HEADER_BYTES;
 }
 
 }  // namespace
@@ -200,12 +229,11 @@ skv_status skv_attend_dense(const skv_problem* p, const void* q, const void* k, 
   if (n < 1 || !q || !out || !aligned16(q) || !aligned16(out)) return SKV_ERR_INVALID_ARG;
   if ((st = check_cache(p, k, n)) != SKV_OK || (st = check_cache(p, v, n)) != SKV_OK) return st;
   const ChunkPlan cp = attend_plan(p, n, false);
-  if (!attend_plan_ok(p, cp)) return SKV_ERR_UNSUPPORTED;
   if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + attend_scratch(p, cp))) != SKV_OK)
     return st;
   const int G = p->n_q_heads / p->n_kv_heads;
   char* base = (char*)ws;
-  const size_t slots = (size_t)p->n_kv_heads * cp.cph * G;
+  const PartLayout L = part_layout(p, cp.cph, G);
   AttendArgs a{};
   a.q = q;
   a.k = (const char*)k;
@@ -217,12 +245,12 @@ skv_status skv_attend_dense(const skv_problem* p, const void* q, const void* k, 
   a.chunk = cp.chunk;
   a.chunks_per_head = cp.cph;
   a.scale_log2 = scale_log2(p);
-  a.part_ml = (float*)(base + SKV_WS_HEADER_BYTES);
-  a.part_acc = (float*)(base + SKV_WS_HEADER_BYTES + align_up(slots * 2 * sizeof(float)));
-  a.counters = (uint32_t*)base;
-  a.out = out;
-  a.lse = lse;
-  return hip_status(skv::launch_attend(p->dtype, p->head_dim, G, false, a, (hipStream_t)stream));
+  a.part_ml = (float*)(base + L.ml);
+  a.part_acc = (float*)(base + L.acc);
+  a.nch = (int32_t*)(base + L.nch);
+  if ((st = hip_status(skv::launch_attend(p->dtype, p->head_dim, G, false, a, (hipStream_t)stream))) != SKV_OK)
+    return st;
+  return launch_partials_merge(p, base, L, cp.cph, G, false, out, lse, (hipStream_t)stream);
 }
 
 skv_status skv_attend_sparse(const skv_problem* p, const void* q, const void* k, const void* v,
@@ -238,12 +266,11 @@ skv_status skv_attend_sparse(const skv_problem* p, const void* q, const void* k,
   if ((st = check_cache(p, k, n)) != SKV_OK || (st = check_cache(p, v, n)) != SKV_OK) return st;
   int64_t idx_rows = idx_stride < tail_start ? idx_stride : tail_start;
   const ChunkPlan cp = attend_plan(p, idx_rows + (n - tail_start), true);
-  if (!attend_plan_ok(p, cp)) return SKV_ERR_UNSUPPORTED;
   if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + attend_scratch(p, cp))) != SKV_OK)
     return st;
   const int G = p->n_q_heads / p->n_kv_heads;
   char* base = (char*)ws;
-  const size_t slots = (size_t)p->n_kv_heads * cp.cph * G;
+  const PartLayout L = part_layout(p, cp.cph, G);
   AttendArgs a{};
   a.q = q;
   a.k = (const char*)k;
@@ -260,12 +287,12 @@ skv_status skv_attend_sparse(const skv_problem* p, const void* q, const void* k,
   a.chunk = cp.chunk;
   a.chunks_per_head = cp.cph;
   a.scale_log2 = scale_log2(p);
-  a.part_ml = (float*)(base + SKV_WS_HEADER_BYTES);
-  a.part_acc = (float*)(base + SKV_WS_HEADER_BYTES + align_up(slots * 2 * sizeof(float)));
-  a.counters = (uint32_t*)base;
-  a.out = out;
-  a.lse = lse;
-  return hip_status(skv::launch_attend(p->dtype, p->head_dim, G, true, a, (hipStream_t)stream));
+  a.part_ml = (float*)(base + L.ml);
+  a.part_acc = (float*)(base + L.acc);
+  a.nch = (int32_t*)(base + L.nch);
+  if ((st = hip_status(skv::launch_attend(p->dtype, p->head_dim, G, true, a, (hipStream_t)stream))) != SKV_OK)
+    return st;
+  return launch_partials_merge(p, base, L, cp.cph, G, true, out, lse, (hipStream_t)stream);
 }
 
 skv_status skv_score(const skv_problem* p, const void* q, int32_t n_obs, const void* k, int64_t n,
@@ -280,7 +307,6 @@ skv_status skv_score(const skv_problem* p, const void* q, int32_t n_obs, const v
   char* base = (char*)ws;
   if (n_obs == 1) {
     const ChunkPlan cp = score_step_plan(p, n);
-    if (!attend_plan_ok(p, cp)) return SKV_ERR_UNSUPPORTED;
     if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + score_step_scratch(p, n))) != SKV_OK)
       return st;
     skv::ScoreStepArgs a{};
@@ -368,11 +394,10 @@ skv_status skv_verify(const skv_problem* p, const void* q, int32_t gamma, const 
   if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
   if ((st = check_cache(p, k, n)) != SKV_OK || (st = check_cache(p, v, n)) != SKV_OK) return st;
   const ChunkPlan cp = verify_plan(p, n);
-  if ((int64_t)cp.cph * gamma * G > skv::verify_max_merge_slots(p->head_dim)) return SKV_ERR_UNSUPPORTED;
   if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + verify_scratch(p, n, gamma))) != SKV_OK)
     return st;
   char* base = (char*)ws;
-  const size_t slots = (size_t)p->n_kv_heads * cp.cph * gamma * G;
+  const PartLayout L = part_layout(p, cp.cph, gamma * G);
   skv::VerifyArgs a{};
   a.q = (const uint16_t*)q;
   a.k = (const char*)k;
@@ -386,12 +411,11 @@ skv_status skv_verify(const skv_problem* p, const void* q, int32_t gamma, const 
   a.chunk = cp.chunk;
   a.chunks_per_head = cp.cph;
   a.scale_log2 = scale_log2(p);
-  a.part_ml = (float*)(base + SKV_WS_HEADER_BYTES);
-  a.part_acc = (float*)(base + SKV_WS_HEADER_BYTES + align_up(slots * 2 * sizeof(float)));
-  a.counters = (uint32_t*)base;
-  a.out = out;
-  a.lse = lse;
-  return hip_status(skv::launch_verify(p->head_dim, a, (hipStream_t)stream));
+  a.part_ml = (float*)(base + L.ml);
+  a.part_acc = (float*)(base + L.acc);
+  a.nch = (int32_t*)(base + L.nch);
+  if ((st = hip_status(skv::launch_verify(p->head_dim, a, (hipStream_t)stream))) != SKV_OK) return st;
+  return launch_partials_merge(p, base, L, cp.cph, gamma * G, false, out, lse, (hipStream_t)stream);
 }
 
 skv_status skv_budgets(const double* s, int32_t n_heads, double total_budget, int32_t window,

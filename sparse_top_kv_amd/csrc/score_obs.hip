@@ -153,20 +153,39 @@ __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs 
   }
 }
 
+// lse of every window row from its per-block statistics: one wave per row,
+// lanes over the key blocks.
 __global__ __launch_bounds__(kThreads) void obs_lse_kernel(const ScoreObsArgs a, int rblocks) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = blockIdx.x / rblocks;
-  const int row = (blockIdx.x - h * rblocks) * kThreads + threadIdx.x;
+  const int row = (blockIdx.x - h * rblocks) * kWaves + wave;
   const int R = a.n_obs * a.group;
   if (row >= R) return;
   const float* ml = a.part_ml + (int64_t)h * a.n_kblocks * R * 2;
+  // statistics of the row's key blocks, loaded once (blocks lane, lane+64, ...)
+  constexpr int kPer = 8;  // up to 512 key blocks (131072 keys) in one round
+  float bm[kPer], bl[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int kb = lane + 64 * i;
+    const int kc = kb < a.n_kblocks ? kb : a.n_kblocks - 1;
+    bm[i] = kb < a.n_kblocks ? ml[((int64_t)kc * R + row) * 2] : kNegInf;
+    bl[i] = ml[((int64_t)kc * R + row) * 2 + 1];
+  }
   float M = kNegInf;
-  for (int kb = 0; kb < a.n_kblocks; ++kb) M = fmaxf(M, ml[((int64_t)kb * R + row) * 2]);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) M = fmaxf(M, bm[i]);
+  for (int kb = lane + 64 * kPer; kb < a.n_kblocks; kb += 64) M = fmaxf(M, ml[((int64_t)kb * R + row) * 2]);
+  M = wave_max(M);
   float L = 0.0f;
-  for (int kb = 0; kb < a.n_kblocks; ++kb) {
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) L += bm[i] == kNegInf ? 0.0f : bl[i] * fast_exp2(bm[i] - M);
+  for (int kb = lane + 64 * kPer; kb < a.n_kblocks; kb += 64) {
     const float m = ml[((int64_t)kb * R + row) * 2];
     L += m == kNegInf ? 0.0f : ml[((int64_t)kb * R + row) * 2 + 1] * fast_exp2(m - M);
   }
-  a.row_lse2[(int64_t)h * R + row] = M + __log2f(L);
+  L = wave_sum(L);
+  if (lane == 0) a.row_lse2[(int64_t)h * R + row] = M + __log2f(L);
 }
 
 template <int D>
@@ -235,7 +254,7 @@ hipError_t launch_d(const ScoreObsArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int R = a.n_obs * a.group;
-  const int rblocks = (R + kThreads - 1) / kThreads;
+  const int rblocks = (R + kWaves - 1) / kWaves;
   hipLaunchKernelGGL(obs_lse_kernel, dim3((unsigned)(a.n_kv_heads * rblocks)), dim3(kThreads), 0, s, a,
                      rblocks);
   e = hipGetLastError();

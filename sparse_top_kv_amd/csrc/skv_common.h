@@ -68,6 +68,21 @@ __device__ __forceinline__ float wave_max(float x) { return group_max<64>(x); }
 // 16-byte global load.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Raw buffer descriptor over `bytes` bytes at `base` (gfx9 word 3: 32-bit data
+// format); loads past `bytes` return zeros instead of faulting.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16-byte buffer load at byte offset voff (per lane) + soff (uniform).
+__device__ __forceinline__ uint4 buf_load16(BufRsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+// Same with the non-temporal hint (cache policy bit 1): for data read once.
+__device__ __forceinline__ uint4 buf_load16_stream(BufRsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
+}
+
 // Dot product of this lane's 16-byte slice of a row with the matching query
 // slice.  bf16: q holds 4 packed pairs; fp32: q holds 4 floats (as bits).
 template <int DT>

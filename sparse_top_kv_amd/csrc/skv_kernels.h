@@ -26,13 +26,25 @@ struct AttendArgs {
   float scale_log2;         // scale * log2(e)
   float* part_ml;           // [Hkv][chunks_per_head][G][2]  (max in log2 units, sum)
   float* part_acc;          // [Hkv][chunks_per_head][G][d]
-  uint32_t* counters;       // [Hkv], zero between calls
-  float* out;               // [Hq][d]
-  float* lse;               // [Hq] or null
+  int32_t* nch;             // [Hkv] chunks actually used per kv head
 };
 
 hipError_t launch_attend(int dtype, int d, int g, bool sparse, const AttendArgs& a,
                          hipStream_t stream);
+
+// Log-sum-exp merge of split-K partials: for output row r of kv head h,
+//   M = max_c m_c, L = sum_c l_c 2^(m_c - M), out = sum_c acc_c 2^(m_c - M) / L,
+//   lse = (M + log2 L) ln 2  (-inf and out = 0 when L = 0).
+// Row r of head h goes to query row (r / G) * Hq + h * G + r % G.
+struct MergeArgs {
+  const float* part_ml;     // [Hkv][cph][rows_per_head][2]
+  const float* part_acc;    // [Hkv][cph][rows_per_head][d]
+  const int32_t* nch;       // [Hkv], or null when every kv head uses cph chunks
+  int32_t n_kv_heads, cph, rows_per_head, group;
+  float* out;
+  float* lse;               // may be null
+};
+hipError_t launch_merge(int d, const MergeArgs& a, hipStream_t stream);
 // Rows per wave iteration of the attend kernel (the chunk must be a multiple
 // of 4x this).
 int attend_rows_per_iter(int dtype, int d);
@@ -100,9 +112,7 @@ struct VerifyArgs {
   float scale_log2;
   float* part_ml;           // [Hkv][chunks_per_head][R][2]
   float* part_acc;          // [Hkv][chunks_per_head][R][d]
-  uint32_t* counters;       // [Hkv]
-  float* out;               // [gamma][Hq][d]
-  float* lse;               // [gamma][Hq] or null
+  int32_t* nch;             // [Hkv] chunks used per kv head
 };
 hipError_t launch_verify(int d, const VerifyArgs& a, hipStream_t stream);
 

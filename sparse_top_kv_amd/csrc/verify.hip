@@ -13,8 +13,8 @@
 //                              probabilities keep ~16 bits; A = V^T from LDS)
 // The P^T operand is used with a permuted key order (keys 4q..4q+3 of two
 // 16-key tiles) that matches the C layout of the S MFMA, so P never leaves the
-// lane; V^T is read from LDS in the same order.  Chunk partials are merged by
-// the last workgroup of the kv head exactly as in the attention kernel.
+// lane; V^T is read from LDS in the same order.  Chunk partials go through the
+// same log-sum-exp merge kernel as the decode attention.
 #include "skv_kernels.h"
 #include "skv_mfma.h"
 
@@ -34,10 +34,9 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs a) {
   constexpr int PIECES = kSub * D / 8;         // 16-byte pieces per tensor sub-block
   constexpr int PPT = PIECES / kThreads;       // pieces per thread
   static_assert(PPT * kThreads == PIECES, "sub-block must tile the workgroup");
-  constexpr int kStageBytes = 2 * kSub * PITCH;  // also holds chunks_per_head * R merge weights
+  constexpr int kStageBytes = 2 * kSub * PITCH;
 
   __shared__ __align__(16) unsigned char sm_stage[kStageBytes];
-  __shared__ int sm_last;
   unsigned char* sK = sm_stage;
   unsigned char* sV = sm_stage + kSub * PITCH;
 
@@ -193,62 +192,13 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs a) {
     }
   }
 
-  __threadfence();
-  __syncthreads();
-  const int nch = (int)((n + a.chunk - 1) / a.chunk);
-  if (tid == 0) {
-    const unsigned t = atomicAdd(&a.counters[h], 1u);
-    sm_last = (t == (unsigned)(nch - 1));
-  }
-  __syncthreads();
-  if (!sm_last) return;
-  __threadfence();
-  if (tid == 0) a.counters[h] = 0u;
-
-  float* sm_w = reinterpret_cast<float*>(sm_stage);
-  const float* ml = a.part_ml + (int64_t)h * cph * R * 2;
-  for (int rr = wave; rr < R; rr += kWaves) {
-    float M = kNegInf;
-    for (int cc = lane; cc < nch; cc += 64) M = fmaxf(M, ml[(cc * R + rr) * 2]);
-    M = wave_max(M);
-    float L = 0.0f;
-    for (int cc = lane; cc < nch; cc += 64) {
-      const float mc = ml[(cc * R + rr) * 2];
-      L += (mc == kNegInf) ? 0.0f : ml[(cc * R + rr) * 2 + 1] * fast_exp2(mc - M);
-    }
-    L = wave_sum(L);
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    for (int cc = lane; cc < nch; cc += 64) {
-      const float mc = ml[(cc * R + rr) * 2];
-      sm_w[cc * R + rr] = (mc == kNegInf) ? 0.0f : fast_exp2(mc - M) * inv;
-    }
-    if (lane == 0 && a.lse) {
-      const int t = rr / G, gi = rr - t * G;
-      a.lse[(int64_t)t * Hq + h * G + gi] = L > 0.0f ? (M + log2f(L)) * kLn2 : kNegInf;
-    }
-  }
-  __syncthreads();
-  const float* pa = a.part_acc + (int64_t)h * cph * R * D;
-  for (int o4 = tid; o4 < R * D / 4; o4 += kThreads) {
-    const int rr = (o4 * 4) / D, d0 = o4 * 4 - rr * D;
-    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-    for (int cc = 0; cc < nch; ++cc) {
-      const float w = sm_w[cc * R + rr];
-      const float4 x = *reinterpret_cast<const float4*>(pa + ((int64_t)cc * R + rr) * D + d0);
-      A.x = fmaf(w, x.x, A.x); A.y = fmaf(w, x.y, A.y);
-      A.z = fmaf(w, x.z, A.z); A.w = fmaf(w, x.w, A.w);
-    }
-    const int t = rr / G, gi = rr - t * G;
-    *reinterpret_cast<float4*>(a.out + ((int64_t)t * Hq + h * G + gi) * D + d0) = A;
-  }
+  if (c == 0 && tid == 0) a.nch[h] = (int32_t)((n + a.chunk - 1) / a.chunk);
 }
 
 }  // namespace
 
 int verify_max_rows() { return kMaxRows; }
 int verify_chunk_granule() { return kSub; }
-int verify_max_merge_slots(int d) { return 2 * kSub * (d * 2 + 16) / 4; }
 
 hipError_t launch_verify(int d, const VerifyArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_kv_heads * a.chunks_per_head));
