@@ -204,6 +204,8 @@ size_t skv_workspace_size(const skv_problem* p, int64_t n_max, int32_t rows_max)
   s = s > t ? s : t;
   t = score_step_scratch(p, n_max);
   s = s > t ? s : t;
+  t = skv::select_ws_bytes(p->n_kv_heads, n_max);
+  s = s > t ? s : t;
   if (p->dtype == SKV_BF16) {
     const int32_t w = rows_max < n_max ? rows_max : (int32_t)n_max;
     t = score_obs_scratch(p, n_max, w);
@@ -356,15 +358,16 @@ skv_status skv_select(const skv_problem* p, const float* score, int64_t score_st
                       int32_t* count, void* ws, size_t ws_bytes, void* stream) {
   skv_status st = check_problem(p);
   if (st != SKV_OK) return st;
-  (void)ws;
-  (void)ws_bytes;
   if (n < 1 || !score || score_stride < n || n_sink < 0 || n_recent < 0 || !count)
     return SKV_ERR_INVALID_ARG;
   if (k_max < 0 || (!k_per_head && (k_uniform < 0 || k_uniform > k_max)))
     return SKV_ERR_INVALID_ARG;
   if (idx_stride < (int64_t)n_sink + k_max || (idx_stride > 0 && !idx)) return SKV_ERR_INVALID_ARG;
   if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
+  const size_t sel_ws = skv::select_ws_bytes(p->n_kv_heads, n);
+  if (sel_ws > 0 && (st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + sel_ws)) != SKV_OK) return st;
   skv::SelectArgs a{};
+  a.ws = sel_ws > 0 ? (char*)ws + SKV_WS_HEADER_BYTES : nullptr;
   a.score = score;
   a.score_stride = score_stride;
   a.n = n;

@@ -1,4 +1,5 @@
 // select.hip -- sinks + per-head top-K of the candidate range by radix select.
+#include <limits.h>
 //
 // Method: keep the attention sinks, the run of recent entries and the
 // highest-scoring history entries of each kv head ("Where Activation Sparsity
@@ -158,10 +159,328 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Block-parallel path for long caches with few kv heads (a one-workgroup-per-
+// head select would leave most CUs idle).  Candidates are cut into blocks of
+// kBlk; five short kernels, no global atomics, so the result is identical run
+// to run:
+//   1 per block: histogram of key bits [31:21]
+//   2 per head : the bin d1 holding the K-th key, how many to take from it,
+//                where each block's bin members go; sinks and count
+//   3 per block: copy bin members (key, index) in index order; count keys
+//                above the bin
+//   4 per head : finish the radix select on the bin members (bits [20:10],
+//                [9:0]) -> threshold key T, tie cutoff index jT; output
+//                offset of every block
+//   5 per block: write kept indices (key > T, or key == T and index <= jT)
+// ---------------------------------------------------------------------------
+constexpr int kBlk = 4096;                 // candidates per block
+constexpr int kBlkPer = kBlk / kSelThreads;
+
+struct SelGeom {  // per-head geometry shared by the five kernels
+  int64_t c_lo, c_hi, ncand, nsink, K;
+  int nb;         // blocks of this head
+};
+
+__device__ __forceinline__ SelGeom sel_geom(const SelectArgs& a, int h) {
+  SelGeom g;
+  const int64_t tail = a.n - a.n_recent > 0 ? a.n - a.n_recent : 0;
+  g.nsink = a.n_sink < tail ? a.n_sink : tail;
+  g.c_lo = a.n_sink;
+  g.c_hi = a.n - a.n_recent;
+  g.ncand = g.c_lo < g.c_hi ? g.c_hi - g.c_lo : 0;
+  int64_t K = a.k_per_head ? a.k_per_head[h] : a.k_uniform;
+  K = K < 0 ? 0 : K;
+  K = K > g.ncand ? g.ncand : K;
+  K = K > a.k_max ? a.k_max : K;
+  g.K = K;
+  g.nb = (int)((g.ncand + kBlk - 1) / kBlk);
+  return g;
+}
+
+// Scratch layout (per kv head, nbm = blocks for the longest head).
+struct SelWs {
+  uint32_t* hist;    // [Hkv][nbm][2048]
+  uint32_t* above;   // [Hkv][nbm]
+  uint32_t* binoff;  // [Hkv][nbm]
+  uint32_t* outoff;  // [Hkv][nbm]
+  uint32_t* head;    // [Hkv][8]: mode, d1, krem, cbin, T, jT
+  uint32_t* ckey;    // [Hkv][n]
+  int32_t* cidx;     // [Hkv][n]
+  int nbm;
+};
+
+__host__ __device__ inline int sel_blocks_max(int64_t n) { return (int)((n + kBlk - 1) / kBlk); }
+
+__host__ __device__ inline SelWs sel_ws(void* ws, int hkv, int64_t n) {
+  SelWs w;
+  w.nbm = sel_blocks_max(n);
+  char* p = (char*)ws;
+  auto take = [&](size_t bytes) {
+    char* q = p;
+    p += (bytes + 255) / 256 * 256;
+    return q;
+  };
+  w.hist = (uint32_t*)take((size_t)hkv * w.nbm * 2048 * 4);
+  w.above = (uint32_t*)take((size_t)hkv * w.nbm * 4);
+  w.binoff = (uint32_t*)take((size_t)hkv * w.nbm * 4);
+  w.outoff = (uint32_t*)take((size_t)hkv * w.nbm * 4);
+  w.head = (uint32_t*)take((size_t)hkv * 8 * 4);
+  w.ckey = (uint32_t*)take((size_t)hkv * n * 4);
+  w.cidx = (int32_t*)take((size_t)hkv * n * 4);
+  return w;
+}
+
+enum { kModeRadix = 0, kModeAll = 1, kModeNone = 2 };
+
+__global__ __launch_bounds__(kSelThreads) void sel_hist1_kernel(const SelectArgs a) {
+  __shared__ uint32_t hist[kBins];
+  const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
+  const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
+  const SelGeom g = sel_geom(a, h);
+  if (b >= g.nb) return;
+  const float* s = a.score + (int64_t)h * a.score_stride;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0u;
+  __syncthreads();
+  const int64_t j0 = g.c_lo + (int64_t)b * kBlk;
+  const int64_t j1 = j0 + kBlk < g.c_hi ? j0 + kBlk : g.c_hi;
+  for (int64_t j = j0 + tid; j < j1; j += kSelThreads) atomicAdd(&hist[score_key(s[j]) >> 21], 1u);
+  __syncthreads();
+  uint32_t* out = w.hist + ((int64_t)h * w.nbm + b) * kBins;
+  for (int i = tid; i < kBins; i += kSelThreads) out[i] = hist[i];
+}
+
+__global__ __launch_bounds__(kSelThreads) void sel_pick1_kernel(const SelectArgs a) {
+  __shared__ uint32_t sm_w[kSelWaves + 1];
+  __shared__ uint32_t sm_digit, sm_krem;
+  const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const SelGeom g = sel_geom(a, h);
+  int32_t* out = a.idx + (int64_t)h * a.idx_stride;
+  for (int64_t i = tid; i < g.nsink; i += kSelThreads) out[i] = (int32_t)i;
+  if (tid == 0) a.count[h] = (int32_t)(g.nsink + g.K);
+  uint32_t* hd = w.head + (int64_t)h * 8;
+  uint32_t* outoff = w.outoff + (int64_t)h * w.nbm;
+  if (g.K == 0 || g.K == g.ncand) {  // nothing or everything: no radix passes
+    if (tid == 0) {
+      hd[0] = g.K == 0 ? kModeNone : kModeAll;
+      hd[4] = g.K == 0 ? 0xFFFFFFFFu : 0u;
+      hd[5] = g.K == 0 ? 0xFFFFFFFFu : 0x7FFFFFFFu;
+    }
+    for (int b = tid; b < g.nb; b += kSelThreads) outoff[b] = (uint32_t)(g.nsink + (int64_t)b * kBlk);
+    return;
+  }
+  const uint32_t* hist = w.hist + (int64_t)h * w.nbm * kBins;
+  const int top = kBins - 1 - tid * 2;  // this thread's bins: top, top-1 (visited from the top)
+  uint32_t c0 = 0, c1 = 0;
+  for (int b = 0; b < g.nb; ++b) {
+    c0 += hist[(int64_t)b * kBins + top];
+    c1 += hist[(int64_t)b * kBins + top - 1];
+  }
+  uint32_t total;
+  const uint32_t krem = (uint32_t)g.K;
+  const uint32_t above = block_excl_scan(c0 + c1, sm_w, &total);
+  if (above < krem && krem <= above + c0 + c1) {
+    if (krem <= above + c0) {
+      sm_digit = (uint32_t)top;
+      sm_krem = krem - above;
+    } else {
+      sm_digit = (uint32_t)(top - 1);
+      sm_krem = krem - above - c0;
+    }
+  }
+  __syncthreads();
+  const uint32_t d1 = sm_digit;
+  // members of bin d1 per block, and where each block's members start
+  uint32_t mine = 0;
+  if (tid < g.nb) mine = hist[(int64_t)tid * kBins + d1];
+  uint32_t cbin;
+  const uint32_t off = block_excl_scan(mine, sm_w, &cbin);
+  if (tid < g.nb) w.binoff[(int64_t)h * w.nbm + tid] = off;
+  if (tid == 0) {
+    hd[0] = kModeRadix;
+    hd[1] = d1;
+    hd[2] = sm_krem;
+    hd[3] = cbin;
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void sel_collect_kernel(const SelectArgs a) {
+  __shared__ uint32_t sm_w[kSelWaves + 1];
+  const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
+  const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
+  const SelGeom g = sel_geom(a, h);
+  if (b >= g.nb) return;
+  const uint32_t* hd = w.head + (int64_t)h * 8;
+  if (hd[0] != kModeRadix) return;
+  const uint32_t d1 = hd[1];
+  const float* s = a.score + (int64_t)h * a.score_stride;
+  const int tid = threadIdx.x;
+  const int64_t j0 = g.c_lo + (int64_t)b * kBlk;
+  uint32_t base = w.binoff[(int64_t)h * w.nbm + b], n_above = 0;
+  uint32_t* ck = w.ckey + (int64_t)h * a.n;
+  int32_t* ci = w.cidx + (int64_t)h * a.n;
+#pragma unroll 1
+  for (int t = 0; t < kBlkPer; ++t) {
+    const int64_t j = j0 + t * kSelThreads + tid;
+    const bool valid = j < g.c_hi;
+    const uint32_t key = valid ? score_key(s[j]) : 0u;
+    const bool inbin = valid && (key >> 21) == d1;
+    const bool above = valid && (key >> 21) > d1;
+    uint32_t n_in, n_ab;
+    const uint32_t r = block_flag_rank(inbin, sm_w, &n_in);
+    block_flag_rank(above, sm_w, &n_ab);
+    if (inbin) {
+      ck[base + r] = key;
+      ci[base + r] = (int32_t)j;
+    }
+    base += n_in;
+    n_above += n_ab;
+  }
+  if (tid == 0) w.above[(int64_t)h * w.nbm + b] = n_above;
+}
+
+__global__ __launch_bounds__(kSelThreads) void sel_pick2_kernel(const SelectArgs a) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t sm_w[kSelWaves + 1];
+  __shared__ uint32_t sm_digit, sm_krem, sm_jt;
+  __shared__ uint32_t sm_kept[1024];
+  const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const SelGeom g = sel_geom(a, h);
+  uint32_t* hd = w.head + (int64_t)h * 8;
+  if (hd[0] != kModeRadix) return;
+  const uint32_t C = hd[3];
+  const uint32_t* ck = w.ckey + (int64_t)h * a.n;
+  const int32_t* ci = w.cidx + (int64_t)h * a.n;
+  uint32_t prefix = hd[1] << 21, mask = 0xFFE00000u;
+  uint32_t krem = hd[2];
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    const int nb = pass == 0 ? 2048 : 1024;
+    for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < C; i += kSelThreads) {
+      const uint32_t key = ck[i];
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    const int per = nb / kSelThreads;
+    const int top = nb - 1 - tid * per;
+    uint32_t mine = 0;
+    for (int i = 0; i < per; ++i) mine += hist[top - i];
+    uint32_t total;
+    uint32_t above = block_excl_scan(mine, sm_w, &total);
+    if (above < krem && krem <= above + mine) {
+      for (int i = 0; i < per; ++i) {
+        const uint32_t cb = hist[top - i];
+        if (krem <= above + cb) {
+          sm_digit = (uint32_t)(top - i);
+          sm_krem = krem - above;
+          break;
+        }
+        above += cb;
+      }
+    }
+    __syncthreads();
+    prefix |= sm_digit << shift;
+    mask |= (uint32_t)(nb - 1) << shift;
+    krem = sm_krem;
+    __syncthreads();
+  }
+  const uint32_t T = prefix, take = krem;
+  // bin members in index order: the first `take` equal to T are kept
+  for (int b = tid; b < 1024; b += kSelThreads) sm_kept[b] = 0u;
+  if (tid == 0) sm_jt = 0xFFFFFFFFu;
+  __syncthreads();
+  uint32_t eq_seen = 0;
+#pragma unroll 1
+  for (uint32_t t0 = 0; t0 < C; t0 += kSelThreads) {
+    const uint32_t i = t0 + tid;
+    const bool valid = i < C;
+    const uint32_t key = valid ? ck[i] : 0u;
+    const bool eq = valid && key == T;
+    uint32_t n_eq;
+    const uint32_t eq_rank = eq_seen + block_flag_rank(eq, sm_w, &n_eq);
+    const bool keep = valid && (key > T || (eq && eq_rank < take));
+    if (keep) {
+      const int32_t j = ci[i];
+      atomicAdd(&sm_kept[(j - g.c_lo) / kBlk], 1u);
+      if (eq && eq_rank == take - 1) sm_jt = (uint32_t)j;
+    }
+    eq_seen += n_eq;
+  }
+  __syncthreads();
+  // output offset of each block: sinks, then blocks in order
+  uint32_t mine = 0;
+  if (tid < g.nb) mine = w.above[(int64_t)h * w.nbm + tid] + sm_kept[tid];
+  uint32_t total;
+  const uint32_t off = block_excl_scan(mine, sm_w, &total);
+  if (tid < g.nb) w.outoff[(int64_t)h * w.nbm + tid] = (uint32_t)g.nsink + off;
+  if (tid == 0) {
+    hd[4] = T;
+    hd[5] = take == 0 ? 0xFFFFFFFFu : sm_jt;  // 0xFFFFFFFF: no equal key kept
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void sel_write_kernel(const SelectArgs a) {
+  __shared__ uint32_t sm_w[kSelWaves + 1];
+  const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
+  const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
+  const SelGeom g = sel_geom(a, h);
+  if (b >= g.nb) return;
+  const uint32_t* hd = w.head + (int64_t)h * 8;
+  if (hd[0] == kModeNone) return;
+  const uint32_t T = hd[4];
+  const int64_t jt = hd[5] == 0xFFFFFFFFu ? -1 : (hd[0] == kModeAll ? INT64_MAX : (int64_t)hd[5]);
+  const float* s = a.score + (int64_t)h * a.score_stride;
+  int32_t* out = a.idx + (int64_t)h * a.idx_stride;
+  const int tid = threadIdx.x;
+  const int64_t j0 = g.c_lo + (int64_t)b * kBlk;
+  const uint32_t limit = (uint32_t)(g.nsink + g.K);
+  uint32_t base = w.outoff[(int64_t)h * w.nbm + b];
+#pragma unroll 1
+  for (int t = 0; t < kBlkPer; ++t) {
+    const int64_t j = j0 + t * kSelThreads + tid;
+    const bool valid = j < g.c_hi;
+    const uint32_t key = valid ? score_key(s[j]) : 0u;
+    const bool keep = valid && (key > T || (key == T && j <= jt));
+    uint32_t n_keep;
+    const uint32_t pos = base + block_flag_rank(keep, sm_w, &n_keep);
+    if (keep && pos < limit) out[pos] = (int32_t)j;  // never past the row
+    base += n_keep;
+  }
+}
+
+// Block path for long rows and few heads; its per-head scans over blocks hold
+// at most one block per thread (n <= kSelThreads * kBlk).
+bool use_block_path(int32_t hkv, int64_t n) {
+  return n > 16384 && n <= (int64_t)kSelThreads * kBlk && hkv < 64;
+}
+
 }  // namespace
 
+size_t select_ws_bytes(int32_t n_kv_heads, int64_t n) {
+  if (!use_block_path(n_kv_heads, n)) return 0;
+  const SelWs w = sel_ws(nullptr, n_kv_heads, n);
+  return (size_t)((char*)(w.cidx + (int64_t)n_kv_heads * n) - (char*)nullptr) + 256;
+}
+
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.n_kv_heads), dim3(kSelThreads), 0, stream, a);
+  if (!use_block_path(a.n_kv_heads, a.n)) {
+    hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.n_kv_heads), dim3(kSelThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  const unsigned grid_b = (unsigned)(a.n_kv_heads * sel_blocks_max(a.n));
+  const unsigned grid_h = (unsigned)a.n_kv_heads;
+  hipLaunchKernelGGL(sel_hist1_kernel, dim3(grid_b), dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_pick1_kernel, dim3(grid_h), dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_collect_kernel, dim3(grid_b), dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_pick2_kernel, dim3(grid_h), dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_write_kernel, dim3(grid_b), dim3(kSelThreads), 0, stream, a);
   return hipGetLastError();
 }
 

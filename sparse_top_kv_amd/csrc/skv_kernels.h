@@ -96,8 +96,12 @@ struct SelectArgs {
   int64_t idx_stride;
   int32_t* count;
   int32_t n_kv_heads;
+  void* ws;                   // scratch of the block-parallel path (select_ws_bytes)
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+// Scratch the block-parallel select needs (0 when the one-workgroup-per-head
+// path is used for this shape).
+size_t select_ws_bytes(int32_t n_kv_heads, int64_t n);
 
 // Causal verify of gamma queries on MFMA (bf16).
 struct VerifyArgs {

@@ -91,6 +91,58 @@ def test_attend_sparse_matches_oracle(dtype, hq, hkv, d, n, tail, stride):
     assert np.abs(l[~empty] - ref_l[~empty]).max(initial=0) <= tl
 
 
+def select_ws(hkv, n):
+    return skv.Workspace.for_problem(skv.problem(hkv, hkv, 128, skv.SKV_BF16, 128, 128), n)
+
+
+def check_select(s, S, R, K, k_per_head=None, k_max=None):
+    """Run skv_select on host scores s [Hkv][n] and compare with the oracle bit for bit."""
+    hkv, n = s.shape
+    ref_idx, ref_cnt = oracle.select(s, S, R, K if k_per_head is None else k_per_head,
+                                     idx_stride=None if k_max is None else S + k_max)
+    stride = ref_idx.shape[1]
+    idx = torch.full((hkv, stride), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(hkv, dtype=torch.int32, device="cuda")
+    kph = None if k_per_head is None else dev(np.asarray(k_per_head, np.int32))
+    skv.skv_select(dev(s), n, S, R, 0 if k_per_head is not None else K, idx, cnt, select_ws(hkv, n),
+                   k_per_head=kph, k_max=k_max)
+    torch.cuda.synchronize()
+    gi, gc = host(idx), host(cnt)
+    assert np.array_equal(gc, ref_cnt)
+    for h in range(hkv):
+        assert np.array_equal(gi[h, :gc[h]], ref_idx[h, :ref_cnt[h]]), h
+        assert np.all(gi[h, gc[h]:] == -7)  # nothing written past count
+
+
+@pytest.mark.parametrize("n", [16385, 40000, 131072 + 37])
+def test_select_block_path_ties_and_budget_edges(n):
+    """Long rows with few kv heads take the multi-workgroup select: per-head K at
+    0, 1, all but one, all candidates and in between, on scores with heavy exact
+    ties (quantised), all-equal rows, +-0 and a tie run across block borders."""
+    banner(f"select block path n={n}")
+    hkv, S, R = 8, 4, 64
+    ncand = n - S - R
+    rng = np.random.default_rng(n)
+    s = rng.exponential(1.0, (hkv, n)).astype(np.float32)
+    s[1] = np.round(s[1] * 4) / 4              # few distinct values: long tie runs
+    s[2] = 0.5                                 # all equal: lowest indices win
+    s[3, ::2] = -0.0
+    s[3, 1::2] = 0.0
+    s[4, 4000:4200] = 1e6                      # a tie run across a block border
+    s[5] = -s[5]
+    ks = [0, 1, ncand - 1, ncand, 2 * n // 10, 4200, n // 3, 777]
+    check_select(s, S, R, 0, k_per_head=ks, k_max=ncand)
+
+
+@pytest.mark.parametrize("hkv,n,K", [(1, 20000, 5000), (2, 65536, 1), (8, 32768, 9762), (63, 17000, 3000)])
+def test_select_block_path_uniform_k(hkv, n, K):
+    banner(f"select block path hkv={hkv} n={n} K={K}")
+    rng = np.random.default_rng(hkv * n)
+    s = (rng.random((hkv, n)) ** 3).astype(np.float32) / n
+    s[:, ::7] = s[:, 3:4]
+    check_select(s, 4, 64, K)
+
+
 @pytest.mark.parametrize("hkv,n,S,R,K", [(8, 2048, 4, 32, 256), (3, 5000, 4, 64, 1000), (2, 700, 0, 32, 650),
                                           (4, 100, 4, 8, 0), (2, 100, 4, 8, 500), (1, 32768, 4, 64, 9762)])
 def test_select_bit_exact_on_oracle_scores(hkv, n, S, R, K):
@@ -104,7 +156,7 @@ def test_select_bit_exact_on_oracle_scores(hkv, n, S, R, K):
     stride = ref_idx.shape[1]
     idx = torch.full((hkv, stride), -7, dtype=torch.int32, device="cuda")
     cnt = torch.zeros(hkv, dtype=torch.int32, device="cuda")
-    ws = skv.Workspace(skv.SKV_WS_HEADER_BYTES)
+    ws = select_ws(hkv, n)
     skv.skv_select(dev(s), n, S, R, K, idx, cnt, ws)
     torch.cuda.synchronize()
     gi, gc = host(idx), host(cnt)
@@ -122,7 +174,7 @@ def test_select_ragged_budgets_and_uniform_scores():
     ref_idx, ref_cnt = oracle.select(s, S, R, ks, idx_stride=3000)
     idx = torch.full((hkv, 3000), -7, dtype=torch.int32, device="cuda")
     cnt = torch.zeros(hkv, dtype=torch.int32, device="cuda")
-    ws = skv.Workspace(skv.SKV_WS_HEADER_BYTES)
+    ws = select_ws(hkv, n)
     skv.skv_select(dev(s), n, S, R, 0, idx, cnt, ws, k_per_head=dev(ks), k_max=3000)
     torch.cuda.synchronize()
     gi, gc = host(idx), host(cnt)
