@@ -42,6 +42,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn µs/step and % HBM roofline at 32K/128K ctx, dense vs top-K"
+# FETCH_SIZE / WRITE_SIZE of the headline step, taken with rocprofv3 --pmc
+COUNTERS = os.path.join(ROOT, "profiles", "attend_sparse_llama32k_hbm_counters.md")
 
 
 def log(msg):
@@ -374,8 +376,8 @@ def main():
             "peak": 8000.0,
             "unit": "GB/s",
             "frac": round(rf.roofline_fraction(sp_bytes, sp_us * 1e-6), 4),
-            "traffic": None,
-            "kernel": "attend_kernel<bf16, d=128, G=4, sparse>",
+            "traffic": rf.counter_traffic(COUNTERS),
+            "kernel": "skv_attend_sparse step = attend_kernel<bf16, d=128, G=4, sparse> + merge_kernel",
             "algorithmic_bytes_per_launch": sp_bytes,
         },
         "cpu_baseline": {

@@ -95,3 +95,45 @@ def verify_bytes(hq: int, hkv: int, d: int, n: int, gamma: int, dtype: str) -> i
 
 def roofline_fraction(nbytes: float, seconds: float, peak: float = HBM_PEAK_BYTES_PER_S) -> float:
     return nbytes / seconds / peak
+
+
+# ---------------------------------------------------------------------------
+# measured HBM traffic (hardware counters), valid only for unchanged kernels
+# ---------------------------------------------------------------------------
+# Sources whose change alters what one sparse decode step moves: the split-K
+# partial and merge kernels, their shared helpers and the host-side planner.
+STEP_SOURCES = ("api.hip", "attend.hip", "merge.hip", "skv_common.h", "skv_kernels.h")
+
+
+def step_source_digest() -> str:
+    """sha256 (first 16 hex digits) over the step's sources, in STEP_SOURCES order."""
+    import hashlib
+    import os
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    h = hashlib.sha256()
+    for name in STEP_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(summary_path: str):
+    """HBM bytes per step recorded in a counter summary, or None if the summary is
+    missing or was taken on other step sources than the ones in the tree.  The
+    summary holds the lines `source_sha256: <digest>` and
+    `traffic_bytes_per_step: <int>`."""
+    import os
+    if not os.path.exists(summary_path):
+        return None
+    fields = {}
+    with open(summary_path) as f:
+        for line in f:
+            key, sep, val = line.strip().strip("`").partition(":")
+            if sep:
+                fields[key.strip()] = val.strip().strip("`")
+    if fields.get("source_sha256") != step_source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_step"])
+    except (KeyError, ValueError):
+        return None

@@ -55,3 +55,17 @@ def test_step_byte_counts_for_the_llama_shape():
     s = rf.sparse_step_bytes(32, 8, 128, 9830, 9766, "bf16")
     assert s == 2 * 8 * 9830 * 256 + 4 * 8 * 9766 + 32 + 32 * 256 + 32 * 129 * 4
     assert rf.speedup_bound(b, b - s) == pytest.approx(b / s)
+
+
+def test_counter_traffic_only_for_unchanged_step_sources(tmp_path):
+    """Measured traffic is reported only while the step's kernel sources match the
+    digest the counters were taken on."""
+    from sparse_top_kv_amd import roofline as rf
+    good = tmp_path / "good.md"
+    good.write_text(f"# counters\nsource_sha256: `{rf.step_source_digest()}`\n"
+                    "traffic_bytes_per_step: `41234567`\n")
+    assert rf.counter_traffic(str(good)) == 41234567
+    stale = tmp_path / "stale.md"
+    stale.write_text("source_sha256: 0123456789abcdef\ntraffic_bytes_per_step: 5\n")
+    assert rf.counter_traffic(str(stale)) is None
+    assert rf.counter_traffic(str(tmp_path / "missing.md")) is None
