@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparsekv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "attend.hip", "score_step.hip", "score_obs.hip", "select.hip",
+SOURCES = ["api.hip", "attend.hip", "attend_mfma.hip", "score_step.hip", "score_obs.hip", "select.hip",
            "verify.hip", "merge.hip", "util.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -88,8 +88,10 @@ skv_status check_cache(const skv_problem* p, const void* kv, int64_t n) {
   if ((p->kv_head_stride * elem_size(p)) % 16 != 0) return SKV_ERR_INVALID_ARG;
   if (p->n_kv_heads > 1 && p->kv_head_stride < n * p->kv_pos_stride) return SKV_ERR_INVALID_ARG;
   if (p->kv_head_stride < 0) return SKV_ERR_INVALID_ARG;
-  // rows of one head are addressed with 32-bit byte offsets
-  if ((double)n * (double)p->kv_pos_stride * elem_size(p) >= 4294967296.0) return SKV_ERR_UNSUPPORTED;
+  // rows of one head (plus one 16-row tile read past the end and masked) are
+  // addressed with 32-bit byte offsets
+  if ((double)(n + 16) * (double)p->kv_pos_stride * elem_size(p) >= 4294967296.0)
+    return SKV_ERR_UNSUPPORTED;
   return SKV_OK;
 }
 
@@ -104,13 +106,28 @@ skv_status hip_status(hipError_t e) { return e == hipSuccess ? SKV_OK : SKV_ERR_
 // ---- per-call workspace requirements (reserved header + scratch) -----------
 
 // chunk granule: one iteration of rows for every wave of a workgroup
+// bf16 caches run the matrix-core partial kernel, fp32 caches the vector one.
+bool attend_uses_mfma(const skv_problem* p) { return p->dtype == SKV_BF16; }
+
 int attend_granule(const skv_problem* p) {
+  if (attend_uses_mfma(p)) return skv::attend_mfma_granule();
   return skv::attend_waves() * skv::attend_rows_per_iter(p->dtype, p->head_dim);
 }
 
 ChunkPlan attend_plan(const skv_problem* p, int64_t rows_bound, bool sparse) {
-  const int max_chunk = sparse ? 512 : skv::attend_max_chunk();
+  int max_chunk;
+  if (attend_uses_mfma(p))  // dense chunks need no per-row LDS, so they may grow
+    max_chunk = sparse ? skv::attend_mfma_sparse_max_chunk() : (1 << 20);
+  else
+    max_chunk = sparse ? 512 : skv::attend_max_chunk();
   return plan_chunks(rows_bound, p->n_kv_heads, attend_granule(p), max_chunk);
+}
+
+hipError_t launch_attend_any(const skv_problem* p, bool sparse, const skv::AttendArgs& a,
+                             hipStream_t s) {
+  const int G = p->n_q_heads / p->n_kv_heads;
+  if (attend_uses_mfma(p)) return skv::launch_attend_mfma(p->head_dim, G, sparse, a, s);
+  return skv::launch_attend(p->dtype, p->head_dim, G, sparse, a, s);
 }
 
 // Split-K scratch: partial (max, sum) and acc[d] per (kv head, chunk, row),
@@ -250,7 +267,7 @@ skv_status skv_attend_dense(const skv_problem* p, const void* q, const void* k, 
   a.part_ml = (float*)(base + L.ml);
   a.part_acc = (float*)(base + L.acc);
   a.nch = (int32_t*)(base + L.nch);
-  if ((st = hip_status(skv::launch_attend(p->dtype, p->head_dim, G, false, a, (hipStream_t)stream))) != SKV_OK)
+  if ((st = hip_status(launch_attend_any(p, false, a, (hipStream_t)stream))) != SKV_OK)
     return st;
   return launch_partials_merge(p, base, L, cp.cph, G, false, out, lse, (hipStream_t)stream);
 }
@@ -292,7 +309,7 @@ skv_status skv_attend_sparse(const skv_problem* p, const void* q, const void* k,
   a.part_ml = (float*)(base + L.ml);
   a.part_acc = (float*)(base + L.acc);
   a.nch = (int32_t*)(base + L.nch);
-  if ((st = hip_status(skv::launch_attend(p->dtype, p->head_dim, G, true, a, (hipStream_t)stream))) != SKV_OK)
+  if ((st = hip_status(launch_attend_any(p, true, a, (hipStream_t)stream))) != SKV_OK)
     return st;
   return launch_partials_merge(p, base, L, cp.cph, G, true, out, lse, (hipStream_t)stream);
 }

@@ -49,6 +49,13 @@ hipError_t launch_merge(int d, const MergeArgs& a, hipStream_t stream);
 // of 4x this).
 int attend_rows_per_iter(int dtype, int d);
 
+// bf16 caches: the matrix-core variant of the split-K partial kernel (same
+// arguments and partial format).  Chunks are multiples of the granule; the
+// sparse variant stages at most attend_mfma_sparse_max_chunk() row offsets.
+hipError_t launch_attend_mfma(int d, int g, bool sparse, const AttendArgs& a, hipStream_t stream);
+int attend_mfma_granule();
+int attend_mfma_sparse_max_chunk();
+
 // Per-step score (one decode query): phase 1 writes log2-domain logits and
 // per-chunk (max, sum) per query head; phase 2 normalises and group-sums.
 struct ScoreStepArgs {
