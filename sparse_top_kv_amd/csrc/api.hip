@@ -10,8 +10,6 @@
 namespace skv {
 int attend_max_chunk();
 int attend_waves();
-int verify_max_rows();
-int verify_chunk_granule();
 int score_obs_block_keys();
 }
 
@@ -110,7 +108,7 @@ skv_status hip_status(hipError_t e) { return e == hipSuccess ? SKV_OK : SKV_ERR_
 bool attend_uses_mfma(const skv_problem* p) { return p->dtype == SKV_BF16; }
 
 int attend_granule(const skv_problem* p) {
-  if (attend_uses_mfma(p)) return skv::attend_mfma_granule();
+  if (attend_uses_mfma(p)) return skv::attend_mfma_granule(p->n_q_heads / p->n_kv_heads, p->head_dim);
   return skv::attend_waves() * skv::attend_rows_per_iter(p->dtype, p->head_dim);
 }
 
@@ -126,7 +124,7 @@ ChunkPlan attend_plan(const skv_problem* p, int64_t rows_bound, bool sparse) {
 hipError_t launch_attend_any(const skv_problem* p, bool sparse, const skv::AttendArgs& a,
                              hipStream_t s) {
   const int G = p->n_q_heads / p->n_kv_heads;
-  if (attend_uses_mfma(p)) return skv::launch_attend_mfma(p->head_dim, G, sparse, a, s);
+  if (attend_uses_mfma(p)) return skv::launch_attend_mfma(p->head_dim, sparse, false, a, s);
   return skv::launch_attend(p->dtype, p->head_dim, G, sparse, a, s);
 }
 
@@ -187,12 +185,14 @@ size_t score_obs_scratch(const skv_problem* p, int64_t n, int32_t n_obs) {
          align_up((size_t)p->n_kv_heads * R * sizeof(float));
 }
 
-ChunkPlan verify_plan(const skv_problem* p, int64_t n) {
-  return plan_chunks(n, p->n_kv_heads, skv::verify_chunk_granule(), 2048);
+// The verify pass: dense, causal, gamma * G query rows per kv head.
+ChunkPlan verify_plan(const skv_problem* p, int64_t n, int32_t gamma) {
+  const int rows = gamma * (p->n_q_heads / p->n_kv_heads);
+  return plan_chunks(n, p->n_kv_heads, skv::attend_mfma_granule(rows, p->head_dim), 1 << 20);
 }
 
 size_t verify_scratch(const skv_problem* p, int64_t n, int32_t gamma) {
-  const ChunkPlan cp = verify_plan(p, n);
+  const ChunkPlan cp = verify_plan(p, n, gamma);
   const int G = p->n_q_heads / p->n_kv_heads;
   return part_layout(p, cp.cph, gamma * G).end - SKV_WS_HEADER_BYTES;
 }
@@ -267,6 +267,8 @@ skv_status skv_attend_dense(const skv_problem* p, const void* q, const void* k, 
   a.part_ml = (float*)(base + L.ml);
   a.part_acc = (float*)(base + L.acc);
   a.nch = (int32_t*)(base + L.nch);
+  a.group = G;
+  a.n_pos = 1;
   if ((st = hip_status(launch_attend_any(p, false, a, (hipStream_t)stream))) != SKV_OK)
     return st;
   return launch_partials_merge(p, base, L, cp.cph, G, false, out, lse, (hipStream_t)stream);
@@ -309,6 +311,8 @@ skv_status skv_attend_sparse(const skv_problem* p, const void* q, const void* k,
   a.part_ml = (float*)(base + L.ml);
   a.part_acc = (float*)(base + L.acc);
   a.nch = (int32_t*)(base + L.nch);
+  a.group = G;
+  a.n_pos = 1;
   if ((st = hip_status(launch_attend_any(p, true, a, (hipStream_t)stream))) != SKV_OK)
     return st;
   return launch_partials_merge(p, base, L, cp.cph, G, true, out, lse, (hipStream_t)stream);
@@ -410,31 +414,32 @@ skv_status skv_verify(const skv_problem* p, const void* q, int32_t gamma, const 
       !aligned16(out))
     return SKV_ERR_INVALID_ARG;
   const int G = p->n_q_heads / p->n_kv_heads;
-  if (gamma * G > skv::verify_max_rows()) return SKV_ERR_UNSUPPORTED;
+  if (gamma * G > skv::attend_mfma_max_rows()) return SKV_ERR_UNSUPPORTED;
   if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
   if ((st = check_cache(p, k, n)) != SKV_OK || (st = check_cache(p, v, n)) != SKV_OK) return st;
-  const ChunkPlan cp = verify_plan(p, n);
+  const ChunkPlan cp = verify_plan(p, n, gamma);
   if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + verify_scratch(p, n, gamma))) != SKV_OK)
     return st;
   char* base = (char*)ws;
   const PartLayout L = part_layout(p, cp.cph, gamma * G);
-  skv::VerifyArgs a{};
-  a.q = (const uint16_t*)q;
+  skv::AttendArgs a{};
+  a.q = q;
   a.k = (const char*)k;
   a.v = (const char*)v;
   a.head_stride_b = p->kv_head_stride * 2;
   a.pos_stride_b = p->kv_pos_stride * 2;
   a.n = n;
-  a.gamma = gamma;
   a.n_kv_heads = p->n_kv_heads;
-  a.group = G;
   a.chunk = cp.chunk;
   a.chunks_per_head = cp.cph;
   a.scale_log2 = scale_log2(p);
   a.part_ml = (float*)(base + L.ml);
   a.part_acc = (float*)(base + L.acc);
   a.nch = (int32_t*)(base + L.nch);
-  if ((st = hip_status(skv::launch_verify(p->head_dim, a, (hipStream_t)stream))) != SKV_OK) return st;
+  a.group = G;
+  a.n_pos = gamma;
+  if ((st = hip_status(skv::launch_attend_mfma(p->head_dim, false, true, a, (hipStream_t)stream))) != SKV_OK)
+    return st;
   return launch_partials_merge(p, base, L, cp.cph, gamma * G, false, out, lse, (hipStream_t)stream);
 }
 

@@ -14,9 +14,11 @@
 // contractions (q.K^T over d, P.V over keys) that the vector ALUs only do at
 // ~30 instructions per key; here they run as MFMAs with the query heads padded
 // to the 16-wide tile, and the vector ALUs keep only the softmax.
-//   - Each wave owns a private ring of kStages tiles of 16 keys (K and V,
-//     4 KB each at d=128) in LDS, filled by buffer_load ... lds, so up to
-//     (kStages-1) tiles per wave are in flight without holding registers.
+//   - Each of the eight waves owns a private ring of kStages tiles of 16 keys
+//     (K and V, 4 KB each at d=128) in LDS, filled by buffer_load ... lds, so
+//     (kStages-1) tiles per wave are in flight without holding registers:
+//     64 KB per CU with two stages, one 128 KB workgroup per CU.  (Four waves
+//     with three or four stages, or two workgroups per CU, measured slower.)
 //     Waits are explicit vmcnt counts; the stages are distinct LDS objects so
 //     the compiler can tell which outstanding copies a read depends on.
 //   - q.K^T: v_mfma_f32_16x16x32_bf16 with A = 16 keys (one 16-byte LDS read
@@ -30,9 +32,10 @@
 //     reads are free of bank conflicts; the direct-to-LDS copy writes whole
 //     1 KB runs, and each lane fetches the 16-byte piece that belongs at its
 //     slot, so the swizzle costs nothing on the copy side.
-//   - Softmax in the log2 domain against a per-head reference fixed from the
+//   - Softmax in the log2 domain against a per-row reference fixed from the
 //     wave's first tile; a tile whose logits pass the reference by kSlack
-//     rescales the accumulators (rare, wave-uniform branch).
+//     rescales the accumulators first (rare, wave-uniform branch, inside the
+//     pipelined loop).
 #include "skv_common.h"
 #include "skv_kernels.h"
 #include "skv_mfma.h"
@@ -40,10 +43,7 @@
 namespace skv {
 namespace {
 
-constexpr int kW = 4;                     // waves per workgroup
-constexpr int kT = 64 * kW;
 constexpr int kStep = 16;                 // keys per wave step (one tile)
-constexpr int kStages = 4;                // tiles per wave ring
 constexpr int kSparseMaxChunk = 512;      // rows per workgroup (LDS offset list)
 constexpr float kSlack = 30.0f;
 
@@ -73,6 +73,12 @@ template <int D>
 __device__ __forceinline__ int swz_v(int t) {
   return D == 128 ? 2 * (t & 7) : 2 * ((t & 1) | (((t >> 2) & 1) << 1));
 }
+// Staged query rows (row-major, D / 8 pieces per row): the 16 rows one MFMA
+// operand read touches land on distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_q(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
 // LDS byte of piece slot `pos` of tile row t: copy u = t % NI writes 1 KB
 // holding rows u, u + NI, u + 2 NI, ...
 template <int D>
@@ -88,6 +94,16 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Wait until at most min(newer, N) groups of PER copies are outstanding.
+template <int N, int PER>
+__device__ __forceinline__ void wait_newer(int newer) {
+  if constexpr (N == 0) {
+    wait_vm<0>();
+  } else {
+    if (newer >= N) wait_vm<N * PER>();
+    else wait_newer<N - 1, PER>(newer);
+  }
+}
 
 __device__ __forceinline__ floatx4_t mfma16(const short4_t& a, const short4_t& b, const floatx4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -104,24 +120,32 @@ __device__ __forceinline__ short4_t lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((SKV_LDS short4_t*)p);
 }
 
-// Two floats to packed bf16 (round to nearest even).
+// Two floats to packed bf16, round to nearest even (one v_cvt_pk_bf16_f32).
+typedef float float2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
-  return f32_to_bf16_bits(x) | (f32_to_bf16_bits(y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{x, y}, bf16x2_t));
 }
 
-template <int D, int G, bool SPARSE>
-__global__ __launch_bounds__(kT) void attend_mfma_kernel(const AttendArgs a) {
+// W waves of 64 lanes, S-tile ring per wave, NG groups of 16 query rows.
+// Query rows of kv head h: r = t * G + g for position t < a.n_pos and group
+// member g < G (decode: one position).  CAUSAL: row r sees keys
+// j <= n - n_pos + t (the verify pass); otherwise every key of the set.
+template <int D, int NG, bool SPARSE, bool CAUSAL, int W, int S>
+__global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a) {
   using TG = TileGeom<D>;
   constexpr int NI = TG::kNI, TB = TG::kTB, PPR = TG::kPPR, KS = TG::kKS, NT = TG::kNT;
+  constexpr int kT = 64 * W;
 
   // per wave: [K tile | V tile]; one LDS object per stage
-  __shared__ __attribute__((aligned(1024))) char st0[kW][2 * TB];
-  __shared__ __attribute__((aligned(1024))) char st1[kW][2 * TB];
-  __shared__ __attribute__((aligned(1024))) char st2[kW][2 * TB];
-  __shared__ __attribute__((aligned(1024))) char st3[kW][2 * TB];
+  __shared__ __attribute__((aligned(1024))) char st0[W][2 * TB];
+  __shared__ __attribute__((aligned(1024))) char st1[W][2 * TB];
+  __shared__ __attribute__((aligned(1024))) char st2[W][2 * TB];
+  __shared__ __attribute__((aligned(1024))) char st3[W][2 * TB];
   __shared__ __attribute__((aligned(16))) uint32_t sm_off[SPARSE ? kSparseMaxChunk : 1];
-  __shared__ float sm_m[kW][G], sm_l[kW][G];
-  __shared__ float sm_acc[kW][G][D];
+  __shared__ float sm_m[W][16], sm_l[W][16];
+  static_assert(S >= 2 && S <= 4, "ring of two to four stages");
+  static_assert(16 * D * 4 <= 2 * TB, "a wave's 16-row partial fits its first stage");
+  static_assert(!(SPARSE && CAUSAL), "the causal pass is dense");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -130,6 +154,9 @@ __global__ __launch_bounds__(kT) void attend_mfma_kernel(const AttendArgs a) {
   const int cph = a.chunks_per_head;
   const int h = blockIdx.x / cph;
   const int c = blockIdx.x - h * cph;
+  const int G = a.group;
+  const int R = G * a.n_pos;  // query rows of this kv head
+  const int Hq = a.n_kv_heads * G;
 
   int32_t cnt = 0;
   int64_t rows_h;
@@ -153,15 +180,44 @@ __global__ __launch_bounds__(kT) void attend_mfma_kernel(const AttendArgs a) {
   } else {
     rows_h = a.n;
   }
-  // q as the B operand of q.K^T: lane (q4, li) holds head li's channels
-  // [32 s + 8 q4, +8); heads past G are zero
-  bf16x8_t qb[KS];
+  // q as the B operand of q.K^T: in group gi, lane (q4, li) takes row
+  // 16 gi + li, channels [32 s + 8 q4, +8); rows past R are zero.  One row
+  // group lives in registers; more are staged in LDS (XOR-swizzled by row)
+  // and read per step, which keeps the accumulators of all groups in VGPRs.
+  // lim: the last key position the lane's row may see (causal pass only).
+  constexpr bool kQInLds = NG > 1;
+  __shared__ __attribute__((aligned(16))) char sm_q[kQInLds ? NG * 16 * D * 2 : 16];
+  bf16x8_t qb[kQInLds ? 1 : KS];
+  bool row_ok[NG];
+  int lim[NG];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    uint4 t = make_uint4(0u, 0u, 0u, 0u);
-    if (li < G)
-      t = ld16(reinterpret_cast<const char*>(a.q) + ((int64_t)(h * G + li) * D + 32 * s + 8 * q4) * 2);
-    qb[s] = as_bf16x8(t);
+  for (int gi = 0; gi < NG; ++gi) {
+    const int r = 16 * gi + li;
+    row_ok[gi] = r < R;
+    const int t = row_ok[gi] ? r / G : 0;
+    lim[gi] = (int)(a.n - a.n_pos) + t;
+  }
+  if constexpr (kQInLds) {
+    for (int e = tid; e < NG * 16 * (D / 8); e += kT) {
+      const int r = e / (D / 8), pc = e - r * (D / 8);
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < R) {
+        const int t = r / G, g = r - t * G;
+        v = ld16(reinterpret_cast<const char*>(a.q) + (((int64_t)t * Hq + h * G + g) * D + pc * 8) * 2);
+      }
+      *reinterpret_cast<uint4*>(sm_q + r * D * 2 + ((pc ^ swz_q<D>(r)) * 16)) = v;
+    }
+  } else {
+    const int r = li;
+    const int t = row_ok[0] ? r / G : 0;
+    const int g = row_ok[0] ? r - t * G : 0;
+    const char* qrow = reinterpret_cast<const char*>(a.q) + ((int64_t)t * Hq + h * G + g) * D * 2;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (row_ok[0]) v = ld16(qrow + (32 * s + 8 * q4) * 2);
+      qb[s] = as_bf16x8(v);
+    }
   }
   int nch = (int)((rows_h + a.chunk - 1) / a.chunk);
   nch = nch < 1 ? 1 : (nch > cph ? cph : nch);
@@ -184,8 +240,8 @@ __global__ __launch_bounds__(kT) void attend_mfma_kernel(const AttendArgs a) {
         sm_off[i] = (uint32_t)p * stride;
       }
     }
-    __syncthreads();
   }
+  if constexpr (SPARSE || kQInLds) __syncthreads();
 
   const uint32_t span = (uint32_t)(a.n * a.pos_stride_b);
   const BufRsrc rk = make_rsrc(a.k + (int64_t)h * a.head_stride_b, span);
@@ -218,12 +274,12 @@ __global__ __launch_bounds__(kT) void attend_mfma_kernel(const AttendArgs a) {
   }
 
   const int nsteps = (rows + kStep - 1) / kStep;
-  const int nst = wave < nsteps ? (nsteps - 1 - wave) / kW + 1 : 0;  // this wave's steps
+  const int nst = wave < nsteps ? (nsteps - 1 - wave) / W + 1 : 0;  // this wave's steps
   const float c2 = a.scale_log2;
 
-  // copies of local step k (global step wave + kW k) into a stage
+  // copies of local step k (global step wave + W k) into a stage
   auto issue = [&](char (*stg)[2 * TB], int k) {
-    const int j = wave + kW * k;
+    const int j = wave + W * k;
     char* dst = &stg[wave][0];
     if constexpr (SPARSE) {
       uint32_t ro[NI];
@@ -235,223 +291,275 @@ __global__ __launch_bounds__(kT) void attend_mfma_kernel(const AttendArgs a) {
         ro[0] = o2.x; ro[1] = o2.y;
       }
 #pragma unroll
-      for (int u = 0; u < NI; ++u)
-        copy_to_lds(rk, dst + u * 1024, ro[u] + pk[u], 0);
+      for (int u = 0; u < NI; ++u) copy_to_lds(rk, dst + u * 1024, ro[u] + pk[u], 0);
 #pragma unroll
-      for (int u = 0; u < NI; ++u)
-        copy_to_lds(rv, dst + TB + u * 1024, ro[u] + pv[u], 0);
+      for (int u = 0; u < NI; ++u) copy_to_lds(rv, dst + TB + u * 1024, ro[u] + pv[u], 0);
     } else {
       const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(r0 + (int64_t)j * kStep) * stride);
 #pragma unroll
-      for (int u = 0; u < NI; ++u)
-        copy_to_lds(rk, dst + u * 1024, pk[u], soff);
+      for (int u = 0; u < NI; ++u) copy_to_lds(rk, dst + u * 1024, pk[u], soff);
 #pragma unroll
-      for (int u = 0; u < NI; ++u)
-        copy_to_lds(rv, dst + TB + u * 1024, pv[u], soff);
+      for (int u = 0; u < NI; ++u) copy_to_lds(rv, dst + TB + u * 1024, pv[u], soff);
     }
   };
 
-  float m = kNegInf;   // reference of head li (log2 units)
-  float l = 0.0f;      // this lane's share of head li's sum
-  floatx4_t o[NT];
+  float m[NG];   // reference of row 16 gi + li (log2 units)
+  float l[NG];   // this lane's share of that row's sum
+  floatx4_t o[NG][NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) o[n] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int gi = 0; gi < NG; ++gi) {
+    m[gi] = kNegInf;
+    l[gi] = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[gi][n] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
   // log2-domain logits of the tile of local step k (already in LDS): key
-  // 4 q4 + r of head li; -inf past the chunk
-  auto logits = [&](const char* base, int k, float (&sv)[4]) {
-    floatx4_t cs = {0.0f, 0.0f, 0.0f, 0.0f};
+  // 4 q4 + r of row 16 gi + li; -inf past the chunk (and past the row's
+  // causal limit)
+  auto logits = [&](const char* base, int k, float (&sv)[NG][4]) {
+    floatx4_t cs[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) cs[gi] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const uint4 kv = *reinterpret_cast<const uint4*>(base + koff[s]);
-      cs = mfma_bf16(as_bf16x8(kv), qb[s], cs);
-    }
-    const int rb = (wave + kW * k) * kStep + 4 * q4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = rb + r < rows ? cs[r] * c2 : kNegInf;
+      for (int gi = 0; gi < NG; ++gi) {
+        bf16x8_t qv;
+        if constexpr (kQInLds)
+          qv = as_bf16x8(*reinterpret_cast<const uint4*>(
+              sm_q + (16 * gi + li) * D * 2 + (((4 * s + q4) ^ swz_q<D>(16 * gi + li)) * 16)));
+        else
+          qv = qb[s];
+        cs[gi] = mfma_bf16(as_bf16x8(kv), qv, cs[gi]);
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[gi][r] = cs[gi][r] * c2;
+    // masks only on a tile that reaches past the chunk or, in the causal
+    // pass, past the first row's last key (wave-uniform test)
+    const int j = wave + W * k;
+    bool edge = (j + 1) * kStep > rows;
+    if constexpr (CAUSAL) edge = edge || r0 + (int64_t)(j + 1) * kStep - 1 > a.n - a.n_pos;
+    if (edge) {
+      const int rb = j * kStep + 4 * q4;  // chunk row of key r = 0
+      const int pb = (int)r0 + rb;        // its position (dense)
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bool ok = rb + r < rows;
+          if constexpr (CAUSAL) ok = ok & (pb + r <= lim[gi]);
+          sv[gi][r] = ok ? sv[gi][r] : kNegInf;
+        }
+    }
   };
-  // max over the tile's keys of head li (all four q4 lanes agree)
-  auto head_max = [&](const float (&sv)[4]) {
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  // max over the tile's keys of the lane's row (all four q4 lanes agree)
+  auto row_max = [&](const float (&x)[4]) {
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     return fmaxf(mx, __shfl_xor(mx, 32, 64));
   };
-  // probabilities against the reference, into the sum and the P.V MFMAs
-  auto accumulate = [&](const char* base, const float (&sv)[4]) {
-    float p[4];
+  // probabilities against the reference, into the sums and the P.V MFMAs
+  auto accumulate = [&](const char* base, const float (&sv)[NG][4]) {
+    short4_t ahi[NG], alo[NG];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = fast_exp2(sv[r] - m);
-      l += p[r];
+    for (int gi = 0; gi < NG; ++gi) {
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = fast_exp2(sv[gi][r] - m[gi]);
+        l[gi] += p[r];
+      }
+      const uint32_t h01 = pack_bf16(p[0], p[1]), h23 = pack_bf16(p[2], p[3]);
+      const uint32_t l01 = pack_bf16(p[0] - bf16lo(h01), p[1] - bf16hi(h01));
+      const uint32_t l23 = pack_bf16(p[2] - bf16lo(h23), p[3] - bf16hi(h23));
+      ahi[gi] = __builtin_bit_cast(short4_t, make_uint2(h01, h23));
+      alo[gi] = __builtin_bit_cast(short4_t, make_uint2(l01, l23));
     }
-    const uint32_t h01 = pack_bf16(p[0], p[1]), h23 = pack_bf16(p[2], p[3]);
-    const uint32_t l01 = pack_bf16(p[0] - bf16lo(h01), p[1] - bf16hi(h01));
-    const uint32_t l23 = pack_bf16(p[2] - bf16lo(h23), p[3] - bf16hi(h23));
-    const short4_t ahi = __builtin_bit_cast(short4_t, make_uint2(h01, h23));
-    const short4_t alo = __builtin_bit_cast(short4_t, make_uint2(l01, l23));
     short4_t vb[NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      vb[n] = lds_read_tr16(base + voff[n]);
+    for (int n = 0; n < NT; ++n) vb[n] = lds_read_tr16(base + voff[n]);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) o[n] = mfma16(ahi, vb[n], o[n]);
+    for (int gi = 0; gi < NG; ++gi) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) o[n] = mfma16(alo, vb[n], o[n]);
-  };
-
-  // wait until the copies of local step k have landed (newer = steps issued after k)
-  auto wait_step = [&](int newer) {
-    if (newer >= kStages - 1) wait_vm<(kStages - 1) * 2 * NI>();
-    else if (newer == 2) wait_vm<2 * 2 * NI>();
-    else if (newer == 1) wait_vm<2 * NI>();
-    else wait_vm<0>();
-  };
-  auto newer_than = [&](int k) { return (nst - 1 - k) < (kStages - 1) ? (nst - 1 - k) : (kStages - 1); };
-
-  // steady state: refill the stage freed by the previous step, wait for step
-  // k, and accumulate it against the fixed reference.  Returns false, with
-  // nothing accumulated, if a logit passes the reference by kSlack.
-  auto fast_step = [&](char (*cur)[2 * TB], char (*nxt)[2 * TB], int k) {
-    if (k + kStages - 1 < nst) {
-      wait_lgkm0();  // reads of the stage being refilled are done
-      issue(nxt, k + kStages - 1);
+      for (int n = 0; n < NT; ++n) o[gi][n] = mfma16(ahi[gi], vb[n], o[gi][n]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[gi][n] = mfma16(alo[gi], vb[n], o[gi][n]);
     }
-    wait_step(newer_than(k));
-    float sv[4];
-    logits(&cur[0][0], k, sv);
-    const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    if (__builtin_amdgcn_ballot_w64(li < G && mx > m + kSlack) != 0) return false;
-    accumulate(&cur[0][0], sv);
-    return true;
   };
 
-  static_assert(kStages == 4, "the ring below is written for four stages");
-  if (nst > 0) issue(st0, 0);
-  if (nst > 1) issue(st1, 1);
-  if (nst > 2) issue(st2, 2);
-  int k = 0;
-  bool slow = false;
-  if (nst > 0) {
-    // reference: the first tile's max per head (0 for a head with no valid key)
-    wait_step(newer_than(0));
-    float sv[4];
-    logits(&st0[0][0], 0, sv);
-    const float mx = head_max(sv);
-    m = mx == kNegInf ? 0.0f : mx;
-    while (k < nst) {
-      if (!fast_step(st0, st3, k)) { slow = true; break; }
-      if (++k >= nst) break;
-      if (!fast_step(st1, st0, k)) { slow = true; break; }
-      if (++k >= nst) break;
-      if (!fast_step(st2, st1, k)) { slow = true; break; }
-      if (++k >= nst) break;
-      if (!fast_step(st3, st2, k)) { slow = true; break; }
-      ++k;
-    }
-  }
-  if (slow) {
-    // rare: online rescaling from step k on; steps up to `issued` are in
-    // flight in their stages, later ones are copied one at a time
-    int issued = k + kStages - 1 < nst ? k + kStages - 1 : nst - 1;
-    for (; k < nst; ++k) {
-      const int sel = k & 3;
-      char (*cur)[2 * TB] = sel == 0 ? st0 : (sel == 1 ? st1 : (sel == 2 ? st2 : st3));
-      if (k > issued) {
-        wait_lgkm0();
-        issue(cur, k);
-        issued = k;
-      }
-      wait_vm<0>();
-      float sv[4];
-      logits(&cur[0][0], k, sv);
-      const float mn = fmaxf(m, head_max(sv));
-      const float alpha = fast_exp2(m - mn);
-      l *= alpha;
-      m = mn;
+  // steps issued after local step k (their copies may still be in flight)
+  auto newer_than = [&](int k) { return (nst - 1 - k) < (S - 1) ? (nst - 1 - k) : (S - 1); };
+
+  // move the references up to cover this tile and rescale what is accumulated
+  auto rescale = [&](const float (&sv)[NG][4]) {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const float mn = fmaxf(m[gi], row_max(sv[gi]));
+      const float alpha = fast_exp2(m[gi] - mn);
+      l[gi] *= alpha;
+      m[gi] = mn;
       float ar[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * q4 + r, 64);  // head 4 q4 + r
+      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * q4 + r, 64);  // row 4 q4 + r
 #pragma unroll
       for (int n = 0; n < NT; ++n)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[n][r] *= ar[r];
-      accumulate(&cur[0][0], sv);
+        for (int r = 0; r < 4; ++r) o[gi][n][r] *= ar[r];
+    }
+  };
+
+  // one step: refill the stage freed by the previous step, wait for step k,
+  // and accumulate it against the reference; a tile with a logit past the
+  // reference by kSlack first rescales (rare, wave-uniform branch)
+  auto step = [&](char (*cur)[2 * TB], char (*nxt)[2 * TB], int k) {
+    if (k + S - 1 < nst) {
+      wait_lgkm0();  // reads of the stage being refilled are done
+      issue(nxt, k + S - 1);
+    }
+    wait_newer<S - 1, 2 * NI>(newer_than(k));
+    float sv[NG][4];
+    logits(&cur[0][0], k, sv);
+    bool over = false;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const float mx = fmaxf(fmaxf(sv[gi][0], sv[gi][1]), fmaxf(sv[gi][2], sv[gi][3]));
+      over = over || (row_ok[gi] && mx > m[gi] + kSlack);
+    }
+    if (__builtin_amdgcn_ballot_w64(over) != 0) rescale(sv);
+    accumulate(&cur[0][0], sv);
+  };
+
+  // stage u of the ring
+  auto ring = [&](int u) -> char (*)[2 * TB] {
+    if (S > 3 && u == 3) return st3;  // stages past S are never referenced
+    if (S > 2 && u == 2) return st2;
+    return u == 1 ? st1 : st0;
+  };
+#pragma unroll
+  for (int u = 0; u < S - 1; ++u)
+    if (u < nst) issue(ring(u), u);
+  if (nst > 0) {
+    // reference: the first tile's max per row (0 for a row with no visible
+    // key there).  Only the prologue's copies are in flight here: steps 1 ..
+    // min(nst, S - 1) - 1 are newer than step 0.
+    wait_newer<S - 2, 2 * NI>(nst - 1 < S - 2 ? nst - 1 : S - 2);
+    float sv[NG][4];
+    logits(&st0[0][0], 0, sv);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const float mx = row_max(sv[gi]);
+      m[gi] = mx == kNegInf ? 0.0f : mx;
+    }
+    for (int k = 0; k < nst;) {
+#pragma unroll
+      for (int u = 0; u < S; ++u) {
+        if (k < nst) step(ring(u), ring((u + S - 1) % S), k);
+        ++k;
+      }
     }
   }
 
-  // fold the four lanes of each head (q4 groups) and park the wave's partial
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (nst == 0) {
-    m = kNegInf;
-    l = 0.0f;
-  }
-  if (lane < G) {
-    sm_m[wave][lane] = m;
-    sm_l[wave][lane] = l;
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int g = 4 * q4 + r;
-    if (g < G) {
-#pragma unroll
-      for (int n = 0; n < NT; ++n) sm_acc[wave][g][16 * n + li] = o[n][r];
-    }
-  }
-  __syncthreads();
-
+  // Per row group: each wave parks its partial in its own first stage (its
+  // copies are done); 16 threads turn the waves' (max, sum) into the row's
+  // max, sum and one weight per wave; then the workgroup folds the waves'
+  // accumulators into the chunk's partial of those rows.
   const int64_t slot = (int64_t)h * cph + c;
-  for (int e = tid; e < G * D; e += kT) {
-    const int g = e / D, dd = e - g * D;
-    float M = sm_m[0][g];
+  float (*acc_w)[D] = reinterpret_cast<float (*)[D]>(&st0[wave][0]);
 #pragma unroll
-    for (int w = 1; w < kW; ++w) M = fmaxf(M, sm_m[w][g]);
-    float L = 0.0f, A = 0.0f;
+  for (int gi = 0; gi < NG; ++gi) {
+    if (16 * gi >= R) break;  // uniform
+    float lg = l[gi];
+    lg += __shfl_xor(lg, 16, 64);
+    lg += __shfl_xor(lg, 32, 64);
+    if (lane < 16) {
+      sm_m[wave][lane] = nst == 0 ? kNegInf : m[gi];
+      sm_l[wave][lane] = nst == 0 ? 0.0f : lg;
+    }
 #pragma unroll
-    for (int w = 0; w < kW; ++w) {
-      const float sc = (sm_m[w][g] == kNegInf) ? 0.0f : fast_exp2(sm_m[w][g] - M);
-      L += sm_l[w][g] * sc;
-      A += sm_acc[w][g][dd] * sc;
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc_w[4 * q4 + r][16 * n + li] = o[gi][n][r];
+    __syncthreads();
+    if (tid < 16) {
+      const int row = 16 * gi + tid;
+      float M = sm_m[0][tid];
+#pragma unroll
+      for (int w = 1; w < W; ++w) M = fmaxf(M, sm_m[w][tid]);
+      float L = 0.0f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float sc = (sm_m[w][tid] == kNegInf) ? 0.0f : fast_exp2(sm_m[w][tid] - M);
+        L += sm_l[w][tid] * sc;
+        sm_l[w][tid] = sc;  // now the wave's weight
+      }
+      if (row < R) {
+        a.part_ml[(slot * R + row) * 2 + 0] = M;
+        a.part_ml[(slot * R + row) * 2 + 1] = L;
+      }
     }
-    a.part_acc[(slot * G + g) * D + dd] = A;
-    if (dd == 0) {
-      a.part_ml[(slot * G + g) * 2 + 0] = M;
-      a.part_ml[(slot * G + g) * 2 + 1] = L;
+    __syncthreads();
+    for (int e = tid; e < 16 * D; e += kT) {
+      const int rr = e / D, dd = e - rr * D;
+      const int row = 16 * gi + rr;
+      if (row < R) {
+        float A = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+          A += reinterpret_cast<const float (*)[D]>(&st0[w][0])[rr][dd] * sm_l[w][rr];
+        a.part_acc[(slot * R + row) * D + dd] = A;
+      }
     }
+    __syncthreads();
   }
   if (c == 0 && tid == 0) a.nch[h] = nch;
 }
 
-template <int D, int G>
-hipError_t launch_g(bool sparse, const AttendArgs& a, hipStream_t s) {
+// Eight waves with a two-tile ring (one 128 KB workgroup per CU), the
+// accumulators kept in VGPRs (built with -amdgpu-mfma-vgpr-form): up to three
+// row groups fit two waves per SIMD.  Four groups at d = 128 need more than
+// 256 registers per wave, so they run four waves with a four-tile ring.
+template <int D, int NG>
+constexpr int mfma_waves() { return (NG >= 4 && D == 128) ? 4 : 8; }
+
+template <int D, int NG, bool SPARSE, bool CAUSAL>
+hipError_t launch_k(const AttendArgs& a, hipStream_t s) {
+  constexpr int W = mfma_waves<D, NG>();
+  constexpr int S = W == 8 ? 2 : 4;
   const dim3 grid((unsigned)(a.n_kv_heads * a.chunks_per_head));
-  if (sparse)
-    hipLaunchKernelGGL((attend_mfma_kernel<D, G, true>), grid, dim3(kT), 0, s, a);
-  else
-    hipLaunchKernelGGL((attend_mfma_kernel<D, G, false>), grid, dim3(kT), 0, s, a);
+  hipLaunchKernelGGL((attend_mfma_kernel<D, NG, SPARSE, CAUSAL, W, S>), grid, dim3(64 * W), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(int g, bool sparse, const AttendArgs& a, hipStream_t s) {
-  switch (g) {
-    case 1: return launch_g<D, 1>(sparse, a, s);
-    case 2: return launch_g<D, 2>(sparse, a, s);
-    case 4: return launch_g<D, 4>(sparse, a, s);
-    case 7: return launch_g<D, 7>(sparse, a, s);
-    case 8: return launch_g<D, 8>(sparse, a, s);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_d(int rows, bool sparse, bool causal, const AttendArgs& a, hipStream_t s) {
+  if (sparse) return rows <= 16 ? launch_k<D, 1, true, false>(a, s) : hipErrorInvalidValue;
+  if (!causal) return rows <= 16 ? launch_k<D, 1, false, false>(a, s) : hipErrorInvalidValue;
+  if (rows <= 16) return launch_k<D, 1, false, true>(a, s);
+  if (rows <= 32) return launch_k<D, 2, false, true>(a, s);
+  if (rows <= 48) return launch_k<D, 3, false, true>(a, s);
+  if (rows <= 64) return launch_k<D, 4, false, true>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int attend_mfma_granule() { return kW * kStep; }
+int attend_mfma_granule(int rows, int d) {
+  const int w = rows > 48 ? (d == 128 ? mfma_waves<128, 4>() : mfma_waves<64, 4>()) : 8;
+  return w * kStep;
+}
 int attend_mfma_sparse_max_chunk() { return kSparseMaxChunk; }
+int attend_mfma_max_rows() { return 64; }
 
-hipError_t launch_attend_mfma(int d, int g, bool sparse, const AttendArgs& a, hipStream_t s) {
-  if (d == 128) return launch_d<128>(g, sparse, a, s);
-  if (d == 64) return launch_d<64>(g, sparse, a, s);
+hipError_t launch_attend_mfma(int d, bool sparse, bool causal, const AttendArgs& a, hipStream_t s) {
+  const int rows = a.group * a.n_pos;
+  if (rows < 1) return hipErrorInvalidValue;
+  if (d == 128) return launch_d<128>(rows, sparse, causal, a, s);
+  if (d == 64) return launch_d<64>(rows, sparse, causal, a, s);
   return hipErrorInvalidValue;
 }
 

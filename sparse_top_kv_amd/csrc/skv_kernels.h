@@ -9,7 +9,7 @@ namespace skv {
 //   dense : rows of head h are positions [0, n)
 //   sparse: rows of head h are idx[h][0..count[h]) followed by [tail_start, n)
 struct AttendArgs {
-  const void* q;            // [Hq][d]
+  const void* q;            // [n_pos][Hq][d]
   const char* k;            // byte pointer to element (0,0,0)
   const char* v;
   int64_t head_stride_b;    // bytes between kv heads
@@ -24,9 +24,11 @@ struct AttendArgs {
   int32_t chunk;            // rows per workgroup
   int32_t chunks_per_head;  // grid = n_kv_heads * chunks_per_head
   float scale_log2;         // scale * log2(e)
-  float* part_ml;           // [Hkv][chunks_per_head][G][2]  (max in log2 units, sum)
-  float* part_acc;          // [Hkv][chunks_per_head][G][d]
+  float* part_ml;           // [Hkv][chunks_per_head][R][2]  (max in log2 units, sum)
+  float* part_acc;          // [Hkv][chunks_per_head][R][d]
   int32_t* nch;             // [Hkv] chunks actually used per kv head
+  int32_t group;            // G = Hq / Hkv
+  int32_t n_pos;            // query positions (1 for a decode step); R = n_pos * G rows
 };
 
 hipError_t launch_attend(int dtype, int d, int g, bool sparse, const AttendArgs& a,
@@ -50,11 +52,15 @@ hipError_t launch_merge(int d, const MergeArgs& a, hipStream_t stream);
 int attend_rows_per_iter(int dtype, int d);
 
 // bf16 caches: the matrix-core variant of the split-K partial kernel (same
-// arguments and partial format).  Chunks are multiples of the granule; the
-// sparse variant stages at most attend_mfma_sparse_max_chunk() row offsets.
-hipError_t launch_attend_mfma(int d, int g, bool sparse, const AttendArgs& a, hipStream_t stream);
-int attend_mfma_granule();
+// partial format).  R = n_pos * G <= attend_mfma_max_rows() query rows per kv
+// head; causal: row (t, g) sees keys j <= n - n_pos + t (dense only).  Chunks
+// are multiples of attend_mfma_granule(R, d); the sparse variant stages at most
+// attend_mfma_sparse_max_chunk() row offsets.
+hipError_t launch_attend_mfma(int d, bool sparse, bool causal, const AttendArgs& a,
+                              hipStream_t stream);
+int attend_mfma_granule(int rows, int d);
 int attend_mfma_sparse_max_chunk();
+int attend_mfma_max_rows();
 
 // Per-step score (one decode query): phase 1 writes log2-domain logits and
 // per-chunk (max, sum) per query head; phase 2 normalises and group-sums.
@@ -111,22 +117,6 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 size_t select_ws_bytes(int32_t n_kv_heads, int64_t n);
 
 // Causal verify of gamma queries on MFMA (bf16).
-struct VerifyArgs {
-  const uint16_t* q;        // [gamma][Hq][d]
-  const char* k;
-  const char* v;
-  int64_t head_stride_b, pos_stride_b;
-  int64_t n;
-  int32_t gamma;
-  int32_t n_kv_heads, group;
-  int32_t chunk, chunks_per_head;
-  float scale_log2;
-  float* part_ml;           // [Hkv][chunks_per_head][R][2]
-  float* part_acc;          // [Hkv][chunks_per_head][R][d]
-  int32_t* nch;             // [Hkv] chunks used per kv head
-};
-hipError_t launch_verify(int d, const VerifyArgs& a, hipStream_t stream);
-
 hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t stream);
 
 }  // namespace skv

@@ -53,6 +53,46 @@ def test_attend_dense_matches_oracle(dtype, hq, hkv, d, n):
     assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("sparse", [False, True])
+def test_softmax_reference_comes_from_this_calls_keys(sparse):
+    """Regression: each wave fixes its softmax reference from its first tile.
+    Run a call whose logits are ~100x larger first, so stale LDS tiles hold
+    huge keys; the next ordinary call must still match the oracle (a reference
+    read before the tile landed would underflow every probability)."""
+    banner(f"reference after a large-logit call sparse={sparse}")
+    hq, hkv, d, n = 32, 8, 128, 8192
+    q = _rand((hq, d), 11, "bf16")
+    k = _cache(hkv, n, d, 12, "bf16")
+    v = _cache(hkv, n, d, 13, "bf16")
+    big = synth.bf16_bits(synth.bf16_to_f32(k) * 100.0)
+    qt, kt, kb, vt = dev(q), dev(k), dev(big), dev(v)
+    out = torch.full((hq, d), float("nan"), device="cuda")
+    lse = torch.full((hq,), float("nan"), device="cuda")
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n)
+    if sparse:
+        idx, cnt = _random_sets(hkv, n - 64, n - 64, 14)
+        ref_o, ref_l = oracle.attend_sparse(q, k, v, n, idx, cnt, n - 64)
+        big_o, big_l = oracle.attend_sparse(q, big, v, n, idx, cnt, n - 64)
+        it, ct = dev(idx), dev(cnt)
+        call = lambda kk, o, l: skv.skv_attend_sparse(qt, kk, vt, n, it, ct, n - 64, o, l, ws)
+    else:
+        ref_o, ref_l = oracle.attend_dense(q, k, v, n)
+        big_o, big_l = oracle.attend_dense(q, big, v, n)
+        call = lambda kk, o, l: skv.skv_attend_dense(qt, kk, vt, n, o, l, ws)
+    ob, lb = torch.empty_like(out), torch.empty_like(lse)
+    for _ in range(3):
+        call(kb, ob, lb)
+        call(kt, out, lse)
+    torch.cuda.synchronize()
+    to, tl = TOL["bf16"]
+    assert np.abs(host(out) - ref_o).max() <= to
+    assert np.abs(host(lse) - ref_l).max() <= tl
+    # the large-logit call itself runs the rescaling path (logits spread over
+    # hundreds of units pass any first-tile reference)
+    assert np.abs(host(ob) - big_o).max() <= to
+    assert np.abs(host(lb) - big_l).max() <= 100 * tl
+
+
 def _random_sets(hkv, tail_start, stride, seed, max_count=None):
     rng = np.random.default_rng(seed)
     idx = np.full((hkv, stride), -1, np.int32)
