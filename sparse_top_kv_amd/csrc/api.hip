@@ -166,14 +166,18 @@ skv_status launch_partials_merge(const skv_problem* p, char* base, const PartLay
 }
 
 ChunkPlan score_step_plan(const skv_problem* p, int64_t n) {
+  if (p->dtype == SKV_BF16) return plan_chunks(n, p->n_kv_heads, skv::score_step_mfma_granule(), 1 << 20);
   return plan_chunks(n, p->n_kv_heads, 4 * skv::attend_rows_per_iter(p->dtype, p->head_dim),
                      skv::attend_max_chunk());
 }
 
+// Logits rows are padded to a multiple of 4 keys (16-byte stores).
+int64_t logits_stride(int64_t n) { return (n + 3) / 4 * 4; }
+
 size_t score_step_scratch(const skv_problem* p, int64_t n) {
   const ChunkPlan cp = score_step_plan(p, n);
   const int G = p->n_q_heads / p->n_kv_heads;
-  return align_up((size_t)p->n_q_heads * n * sizeof(float)) +
+  return align_up((size_t)p->n_q_heads * logits_stride(n) * sizeof(float)) +
          align_up((size_t)p->n_kv_heads * cp.cph * G * 2 * sizeof(float));
 }
 
@@ -343,8 +347,9 @@ skv_status skv_score(const skv_problem* p, const void* q, int32_t n_obs, const v
     a.chunks_per_head = cp.cph;
     a.scale_log2 = scale_log2(p);
     a.logits = (float*)(base + SKV_WS_HEADER_BYTES);
+    a.logits_stride = logits_stride(n);
     a.part_ml = (float*)(base + SKV_WS_HEADER_BYTES +
-                         align_up((size_t)p->n_q_heads * n * sizeof(float)));
+                         align_up((size_t)p->n_q_heads * a.logits_stride * sizeof(float)));
     a.score = score;
     a.score_stride = score_stride;
     return hip_status(skv::launch_score_step(p->dtype, p->head_dim, G, a, (hipStream_t)stream));

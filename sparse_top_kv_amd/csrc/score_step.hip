@@ -11,6 +11,7 @@
 // 2 merges the chunk statistics into lse_g and writes the group sums.
 #include "skv_common.h"
 #include "skv_kernels.h"
+#include "skv_tile.h"
 
 namespace skv {
 namespace {
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void score_logits_kernel(const ScoreStepA
   for (int g = 0; g < G; ++g) { m[g] = kNegInf; l[g] = 0.0f; }
 
   const char* kb = a.k + (int64_t)h * a.head_stride_b + part * 16;
-  float* lg_out = a.logits + (int64_t)(h * G + (part < G ? part : 0)) * a.n + r0;
+  float* lg_out = a.logits + (int64_t)(h * G + (part < G ? part : 0)) * a.logits_stride + r0;
   const int nit_total = (rows + RI - 1) / RI;
   const int per = (nit_total + kWaves - 1) / kWaves;
   const int it0 = wave * per;
@@ -164,9 +165,183 @@ __global__ __launch_bounds__(kThreads) void score_finalize_kernel(const ScoreSte
   for (int64_t j = j0 + tid; j < j0 + kFinalizeKeys && j < a.n; j += kThreads) {
     float s = 0.0f;
 #pragma unroll
-    for (int g = 0; g < G; ++g) s += fast_exp2(a.logits[(int64_t)(h * G + g) * a.n + j] - lse2[g]);
+    for (int g = 0; g < G; ++g) s += fast_exp2(a.logits[(int64_t)(h * G + g) * a.logits_stride + j] - lse2[g]);
     a.score[(int64_t)h * a.score_stride + j] = s;
   }
+}
+
+// bf16 caches: phase 1 on the matrix cores.  K streams through a per-wave
+// ring of 16-key LDS tiles (direct-to-LDS copies, as in the attention kernel;
+// no V, so each wave keeps S = 4 tiles); q.K^T is one 16x16x32 MFMA per 32
+// channels with the G query heads padded to 16.  Lane (q4, li) holds the
+// logits of keys 4 q4 .. 4 q4 + 3 for head li: it stores them as one 16-byte
+// write and keeps a running (max, sum) of its head.
+template <int D, int W, int S>
+__global__ __launch_bounds__(64 * W) void score_mfma_kernel(const ScoreStepArgs a, int G) {
+  using TG = TileGeom<D>;
+  constexpr int NI = TG::kNI, TB = TG::kTB, PPR = TG::kPPR, KS = TG::kKS;
+  __shared__ __attribute__((aligned(1024))) char st0[W][TB];
+  __shared__ __attribute__((aligned(1024))) char st1[W][TB];
+  __shared__ __attribute__((aligned(1024))) char st2[W][TB];
+  __shared__ __attribute__((aligned(1024))) char st3[W][TB];
+  __shared__ float sm_m[W][16], sm_l[W][16];
+  static_assert(S >= 2 && S <= 4, "ring of two to four stages");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q4 = lane >> 4, li = lane & 15;
+  const int cph = a.chunks_per_head;
+  const int h = blockIdx.x / cph;
+  const int c = blockIdx.x - h * cph;
+  const int64_t r0 = (int64_t)c * a.chunk;
+  const int64_t rem = a.n - r0;
+  const int rows = (int)(rem < 0 ? 0 : (rem > a.chunk ? a.chunk : rem));
+  const uint32_t stride = (uint32_t)a.pos_stride_b;
+
+  bf16x8_t qb[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (li < G)
+      v = ld16(reinterpret_cast<const char*>(a.q) + ((int64_t)(h * G + li) * D + 32 * s + 8 * q4) * 2);
+    qb[s] = as_bf16x8(v);
+  }
+  const uint32_t span = (uint32_t)(a.n * a.pos_stride_b);
+  const BufRsrc rk = make_rsrc(a.k + (int64_t)h * a.head_stride_b, span);
+  const int grp = lane / PPR, pos = lane % PPR;
+  uint32_t pk[NI];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int t = grp * NI + u;
+    pk[u] = (uint32_t)((pos ^ swz_k<D>(t)) * 16) + (uint32_t)t * stride;
+  }
+  const int wbase = wave * TB;
+  int koff[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) koff[s] = wbase + tile_byte<D>(li, (4 * s + q4) ^ swz_k<D>(li));
+
+  const int nsteps = (rows + kStep - 1) / kStep;
+  const int nst = wave < nsteps ? (nsteps - 1 - wave) / W + 1 : 0;
+  const float c2 = a.scale_log2;
+  float* lrow = a.logits + (int64_t)(h * G + (li < G ? li : 0)) * a.logits_stride;
+
+  auto issue = [&](char (*stg)[TB], int k) {
+    const int j = wave + W * k;
+    char* dst = &stg[wave][0];
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(r0 + (int64_t)j * kStep) * stride);
+#pragma unroll
+    for (int u = 0; u < NI; ++u) copy_to_lds(rk, dst + u * 1024, pk[u], soff);
+  };
+  auto ring = [&](int u) -> char (*)[TB] {
+    if (S > 3 && u == 3) return st3;
+    if (S > 2 && u == 2) return st2;
+    return u == 1 ? st1 : st0;
+  };
+  auto newer_than = [&](int k) { return (nst - 1 - k) < (S - 1) ? (nst - 1 - k) : (S - 1); };
+
+  float m = kNegInf, l = 0.0f;  // running max and sum of head li over this lane's keys
+  auto step = [&](char (*cur)[TB], char (*nxt)[TB], int k) {
+    if (k + S - 1 < nst) {
+      wait_lgkm0();
+      issue(nxt, k + S - 1);
+    }
+    wait_newer<S - 1, NI>(newer_than(k));
+    const char* base = &cur[0][0];
+    floatx4_t cs = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      cs = mfma_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(base + koff[s])), qb[s], cs);
+    const int j = wave + W * k;
+    const int rb = j * kStep + 4 * q4;  // chunk row of key r = 0
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = cs[r] * c2;
+    const bool full = (j + 1) * kStep <= rows;  // wave-uniform
+    if (full) {
+      if (li < G) *reinterpret_cast<float4*>(lrow + r0 + rb) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = rb + r < rows;
+        if (ok && li < G) lrow[r0 + rb + r] = sv[r];
+        sv[r] = ok ? sv[r] : kNegInf;
+      }
+    }
+    const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    const float mn = fmaxf(m, mx);
+    if (mn != kNegInf) {
+      l = l * fast_exp2(m - mn) + fast_exp2(sv[0] - mn) + fast_exp2(sv[1] - mn) +
+          fast_exp2(sv[2] - mn) + fast_exp2(sv[3] - mn);
+      m = mn;
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < S - 1; ++u)
+    if (u < nst) issue(ring(u), u);
+  for (int k = 0; k < nst;) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      if (k < nst) step(ring(u), ring((u + S - 1) % S), k);
+      ++k;
+    }
+  }
+
+  // (max, sum) of head li: the four q4 lanes, then the waves
+  float M = fmaxf(m, __shfl_xor(m, 16, 64));
+  M = fmaxf(M, __shfl_xor(M, 32, 64));
+  float x = (m == kNegInf) ? 0.0f : l * fast_exp2(m - M);
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  if (lane < 16) {
+    sm_m[wave][lane] = M;
+    sm_l[wave][lane] = x;
+  }
+  __syncthreads();
+  if (tid < G) {
+    const int g = tid;
+    float Mw = sm_m[0][g];
+#pragma unroll
+    for (int w = 1; w < W; ++w) Mw = fmaxf(Mw, sm_m[w][g]);
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+      L += (sm_m[w][g] == kNegInf) ? 0.0f : sm_l[w][g] * fast_exp2(sm_m[w][g] - Mw);
+    float* ml = a.part_ml + (((int64_t)h * cph + c) * G + g) * 2;
+    ml[0] = Mw;
+    ml[1] = L;
+  }
+}
+
+template <int G>
+hipError_t launch_finalize(const ScoreStepArgs& a, hipStream_t s) {
+  const int nblk = (int)((a.n + kFinalizeKeys - 1) / kFinalizeKeys);
+  hipLaunchKernelGGL((score_finalize_kernel<G>), dim3((unsigned)(a.n_kv_heads * nblk)), dim3(kThreads),
+                     0, s, a, nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_g(int g, const ScoreStepArgs& a, hipStream_t s) {
+  switch (g) {
+    case 1: return launch_finalize<1>(a, s);
+    case 2: return launch_finalize<2>(a, s);
+    case 4: return launch_finalize<4>(a, s);
+    case 7: return launch_finalize<7>(a, s);
+    case 8: return launch_finalize<8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+constexpr int kScoreWaves = 8;
+constexpr int kScoreStages = 4;
+
+template <int D>
+hipError_t launch_mfma(int g, const ScoreStepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((score_mfma_kernel<D, kScoreWaves, kScoreStages>),
+                     dim3((unsigned)(a.n_kv_heads * a.chunks_per_head)), dim3(64 * kScoreWaves), 0, s,
+                     a, g);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_finalize_g(g, a, s);
 }
 
 template <int DT, int D, int G>
@@ -195,9 +370,11 @@ hipError_t launch_d(int g, const ScoreStepArgs& a, hipStream_t s) {
 
 }  // namespace
 
+int score_step_mfma_granule() { return kScoreWaves * kStep; }
+
 hipError_t launch_score_step(int dtype, int d, int g, const ScoreStepArgs& a, hipStream_t s) {
-  if (dtype == 1 && d == 128) return launch_d<1, 128>(g, a, s);
-  if (dtype == 1 && d == 64) return launch_d<1, 64>(g, a, s);
+  if (dtype == 1 && d == 128) return launch_mfma<128>(g, a, s);
+  if (dtype == 1 && d == 64) return launch_mfma<64>(g, a, s);
   if (dtype == 0 && d == 128) return launch_d<0, 128>(g, a, s);
   if (dtype == 0 && d == 64) return launch_d<0, 64>(g, a, s);
   return hipErrorInvalidValue;

@@ -72,12 +72,15 @@ struct ScoreStepArgs {
   int32_t n_kv_heads;
   int32_t chunk, chunks_per_head;
   float scale_log2;
-  float* logits;            // [Hq][n] (log2 domain)
+  float* logits;            // [Hq][logits_stride] (log2 domain)
+  int64_t logits_stride;    // >= n; a multiple of 4 for 16-byte stores
   float* part_ml;           // [Hkv][chunks_per_head][G][2]
   float* score;             // [Hkv][score_stride]
   int64_t score_stride;
 };
 hipError_t launch_score_step(int dtype, int d, int g, const ScoreStepArgs& a, hipStream_t stream);
+// bf16 runs phase 1 on the matrix cores: chunks are multiples of this.
+int score_step_mfma_granule();
 
 // Observation-window score on MFMA (bf16 only): W queries x G heads per kv head.
 struct ScoreObsArgs {
