@@ -162,6 +162,12 @@ def main():
     de_us, de_blocks = time_steps(dense_step, args.steps, args.warmup, args.blocks)
     sp_eager, _ = time_steps(sparse_step, args.steps, 2, 1, graph=False)
     de_eager, _ = time_steps(dense_step, args.steps, 2, 1, graph=False)
+    # the same steps on one layer only: its cache stays in the 256 MB Infinity
+    # Cache (labelled MALL-warm; not the headline)
+    sp_warm, _ = time_steps(lambda i: sparse_step(0), args.steps, args.warmup, 3)
+    de_warm, _ = time_steps(lambda i: dense_step(0), args.steps, args.warmup, 3)
+    details["llama32k_sparse_us_mall_warm"] = round(sp_warm, 3)
+    details["llama32k_dense_us_mall_warm"] = round(de_warm, 3)
     details["llama32k_sparse_us_eager_launches"] = round(sp_eager, 3)
     details["llama32k_dense_us_eager_launches"] = round(de_eager, 3)
     rows = S + K + R
@@ -169,6 +175,7 @@ def main():
     de_bytes = rf.dense_step_bytes(hq, hkv, d, n, "bf16")
     details["llama32k_sparse_us"] = round(sp_us, 3)
     details["llama32k_sparse_blocks_us"] = [round(x, 3) for x in sp_blocks]
+    details["llama32k_sparse_block_range_us"] = [round(sp_blocks[0], 3), round(sp_blocks[-1], 3)]
     details["llama32k_dense_us"] = round(de_us, 3)
     details["llama32k_dense_blocks_us"] = [round(x, 3) for x in de_blocks]
     details["llama32k_dense_hbm_frac"] = round(rf.roofline_fraction(de_bytes, de_us * 1e-6), 4)
@@ -185,6 +192,24 @@ def main():
         torch.cuda.synchronize()
         details["calib_copy_bytes"] = {"read": src.numel(), "written": dst.numel()}
         del src, dst
+
+    # streaming ceiling of this machine: a 1 GiB device-to-device copy (read + write)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ceil_gbps = 2 * src.numel() * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    details["copy_ceiling_GBps"] = round(ceil_gbps, 1)
+    details["llama32k_sparse_frac_of_copy_ceiling"] = round(sp_bytes / (sp_us * 1e-6) / 1e9 / ceil_gbps, 4)
+    details["llama32k_dense_frac_of_copy_ceiling"] = round(de_bytes / (de_us * 1e-6) / 1e9 / ceil_gbps, 4)
+    del src, dst
+    torch.cuda.empty_cache()
 
     if args.sections != "headline":
         del layers
@@ -293,6 +318,9 @@ def main():
             "dense_5_steps_us": round(rd_us, 2),
             "verify_us": round(v_us, 3),
             "verify_hbm_frac": round(rf.roofline_fraction(v_bytes, v_us * 1e-6), 4),
+            "verify_tflops": round(rf.verify_flops(hq4, m + gamma, d, gamma) / (v_us * 1e-6) / 1e12, 2),
+            "verify_mfma_frac_of_bf16_peak": round(
+                rf.verify_flops(hq4, m + gamma, d, gamma) / (v_us * 1e-6) / 2.5e15, 5),
             "round_speedup_measured_alpha1": round(rd_us / r_us, 3),
             "round_speedup_byte_bound_alpha1": round(dense_round_bytes / (draft_bytes + v_bytes), 3),
         }
@@ -350,6 +378,36 @@ def main():
         if time.perf_counter() - t0 >= args.cpu_seconds:
             break
     cpu_us = (time.perf_counter() - t0) / reps * 1e6
+    # single thread, same step (a few runs)
+    t0 = time.perf_counter()
+    reps1 = 0
+    while True:
+        oracle.attend_sparse(w0.q, w0.k, w0.v, n, oi, oc, tail, nthreads=1)
+        reps1 += 1
+        if time.perf_counter() - t0 >= max(1.0, args.cpu_seconds / 5):
+            break
+    cpu1_us = (time.perf_counter() - t0) / reps1 * 1e6
+    t0 = time.perf_counter()
+    oracle.attend_dense(w0.q, w0.k, w0.v, n, nthreads=threads)
+    cpu_dense_us = (time.perf_counter() - t0) * 1e6
+    cpu_score_select_us = None
+    if args.sections != "headline":
+        # per-step score + select of the 128K workload (one run)
+        w3c = synth.llama_needle(layer=0)
+        t0 = time.perf_counter()
+        _, s3 = oracle.score(w3c.q[None], w3c.k, w3c.n, nthreads=threads)
+        oracle.select(s3, w3c.n_sink, w3c.n_recent, w3c.k_top)
+        cpu_score_select_us = round((time.perf_counter() - t0) * 1e6, 1)
+        del w3c, s3
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
 
     line = {
         "metric": METRIC,
@@ -377,7 +435,7 @@ def main():
             "unit": "GB/s",
             "frac": round(rf.roofline_fraction(sp_bytes, sp_us * 1e-6), 4),
             "traffic": rf.counter_traffic(COUNTERS),
-            "kernel": "skv_attend_sparse step = attend_kernel<bf16, d=128, G=4, sparse> + merge_kernel",
+            "kernel": "skv_attend_sparse step = attend_mfma_kernel<d=128, one 16-row group, sparse> + merge_kernel",
             "algorithmic_bytes_per_launch": sp_bytes,
         },
         "cpu_baseline": {
@@ -387,6 +445,10 @@ def main():
             "kind": "oracle",
             "sample": f"{reps} fp64 oracle runs of the headline sparse step (32 heads x {rows} kept rows) "
                       f"on one layer, {args.cpu_seconds:.0f} s budget",
+            "single_thread_value": round(cpu1_us, 1),
+            "dense_step_us": round(cpu_dense_us, 1),
+            "score_select_128k_us": cpu_score_select_us,
+            "cpu_model": cpu_model,
         },
         "details": details,
     }

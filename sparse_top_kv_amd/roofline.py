@@ -93,6 +93,12 @@ def verify_bytes(hq: int, hkv: int, d: int, n: int, gamma: int, dtype: str) -> i
     return 2 * hkv * n * d * e + gamma * hq * d * e + gamma * hq * (d + 1) * 4
 
 
+def verify_flops(hq: int, n: int, d: int, gamma: int) -> int:
+    """q.k and p.v multiply-adds of the causal verify pass (2 flops each)."""
+    keys = sum(n - gamma + t + 1 for t in range(gamma))  # keys seen per query head
+    return 2 * 2 * hq * d * keys
+
+
 def roofline_fraction(nbytes: float, seconds: float, peak: float = HBM_PEAK_BYTES_PER_S) -> float:
     return nbytes / seconds / peak
 
@@ -101,8 +107,10 @@ def roofline_fraction(nbytes: float, seconds: float, peak: float = HBM_PEAK_BYTE
 # measured HBM traffic (hardware counters), valid only for unchanged kernels
 # ---------------------------------------------------------------------------
 # Sources whose change alters what one sparse decode step moves: the split-K
-# partial and merge kernels, their shared helpers and the host-side planner.
-STEP_SOURCES = ("api.hip", "attend.hip", "merge.hip", "skv_common.h", "skv_kernels.h")
+# partial kernels (matrix-core for bf16, vector for fp32), the merge kernel,
+# their shared helpers and the host-side planner.
+STEP_SOURCES = ("api.hip", "attend.hip", "attend_mfma.hip", "merge.hip", "skv_common.h",
+                "skv_kernels.h", "skv_mfma.h", "skv_tile.h")
 
 
 def step_source_digest() -> str:
