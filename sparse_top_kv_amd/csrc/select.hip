@@ -176,6 +176,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
 //   5 per block: write kept indices (key > T, or key == T and index <= jT)
 // ---------------------------------------------------------------------------
 constexpr int kBlk = 4096;                 // candidates per block
+constexpr int kStageCand = 8192;           // threshold-bin members staged in LDS
 constexpr int kBlkPer = kBlk / kSelThreads;
 
 struct SelGeom {  // per-head geometry shared by the five kernels
@@ -242,11 +243,15 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist1_kernel(const SelectArgs
   if (b >= g.nb) return;
   const float* s = a.score + (int64_t)h * a.score_stride;
   const int tid = threadIdx.x;
+  const int64_t j0 = g.c_lo + (int64_t)b * kBlk + kBlkPer * tid;  // this thread's candidates
+  float sv[kBlkPer];
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u) sv[u] = j0 + u < g.c_hi ? s[j0 + u] : 0.0f;
   for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0u;
   __syncthreads();
-  const int64_t j0 = g.c_lo + (int64_t)b * kBlk;
-  const int64_t j1 = j0 + kBlk < g.c_hi ? j0 + kBlk : g.c_hi;
-  for (int64_t j = j0 + tid; j < j1; j += kSelThreads) atomicAdd(&hist[score_key(s[j]) >> 21], 1u);
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u)
+    if (j0 + u < g.c_hi) atomicAdd(&hist[score_key(sv[u]) >> 21], 1u);
   __syncthreads();
   uint32_t* out = w.hist + ((int64_t)h * w.nbm + b) * kBins;
   for (int i = tid; i < kBins; i += kSelThreads) out[i] = hist[i];
@@ -275,9 +280,24 @@ __global__ __launch_bounds__(kSelThreads) void sel_pick1_kernel(const SelectArgs
   const uint32_t* hist = w.hist + (int64_t)h * w.nbm * kBins;
   const int top = kBins - 1 - tid * 2;  // this thread's bins: top, top-1 (visited from the top)
   uint32_t c0 = 0, c1 = 0;
-  for (int b = 0; b < g.nb; ++b) {
-    c0 += hist[(int64_t)b * kBins + top];
-    c1 += hist[(int64_t)b * kBins + top - 1];
+  // bins top - 1 and top are adjacent: one 8-byte load per block, eight
+  // blocks in flight per round
+  const uint2* hp = reinterpret_cast<const uint2*>(hist + top - 1);
+  int b = 0;
+  for (; b + 8 <= g.nb; b += 8) {
+    uint2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = hp[(int64_t)(b + u) * (kBins / 2)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      c0 += v[u].y;
+      c1 += v[u].x;
+    }
+  }
+  for (; b < g.nb; ++b) {
+    const uint2 v = hp[(int64_t)b * (kBins / 2)];
+    c0 += v.y;
+    c1 += v.x;
   }
   uint32_t total;
   const uint32_t krem = (uint32_t)g.K;
@@ -313,33 +333,40 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect_kernel(const SelectAr
   const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
   const SelGeom g = sel_geom(a, h);
   if (b >= g.nb) return;
-  const uint32_t* hd = w.head + (int64_t)h * 8;
-  if (hd[0] != kModeRadix) return;
-  const uint32_t d1 = hd[1];
   const float* s = a.score + (int64_t)h * a.score_stride;
   const int tid = threadIdx.x;
-  const int64_t j0 = g.c_lo + (int64_t)b * kBlk;
-  uint32_t base = w.binoff[(int64_t)h * w.nbm + b], n_above = 0;
+  // every load of the kernel in one round: scores, head state, block offset
+  const int64_t j0 = g.c_lo + (int64_t)b * kBlk + kBlkPer * tid;
+  float sv[kBlkPer];
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u) sv[u] = j0 + u < g.c_hi ? s[j0 + u] : 0.0f;
+  const uint32_t* hd = w.head + (int64_t)h * 8;
+  const uint32_t mode = hd[0], d1 = hd[1];
+  const uint32_t base = w.binoff[(int64_t)h * w.nbm + b];
+  if (mode != kModeRadix) return;  // uniform
+  // candidates in the threshold bin (kept in index order) and above it
+  uint32_t key[kBlkPer], n_in = 0, n_ab = 0;
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u) {
+    const bool valid = j0 + u < g.c_hi;
+    key[u] = score_key(sv[u]);
+    n_in += (valid && (key[u] >> 21) == d1) ? 1u : 0u;
+    n_ab += (valid && (key[u] >> 21) > d1) ? 1u : 0u;
+  }
+  uint32_t tot;  // counts <= kBlk < 2^16: both in one scan
+  const uint32_t ex = block_excl_scan((n_in << 16) | n_ab, sm_w, &tot);
+  uint32_t r = base + (ex >> 16);
   uint32_t* ck = w.ckey + (int64_t)h * a.n;
   int32_t* ci = w.cidx + (int64_t)h * a.n;
-#pragma unroll 1
-  for (int t = 0; t < kBlkPer; ++t) {
-    const int64_t j = j0 + t * kSelThreads + tid;
-    const bool valid = j < g.c_hi;
-    const uint32_t key = valid ? score_key(s[j]) : 0u;
-    const bool inbin = valid && (key >> 21) == d1;
-    const bool above = valid && (key >> 21) > d1;
-    uint32_t n_in, n_ab;
-    const uint32_t r = block_flag_rank(inbin, sm_w, &n_in);
-    block_flag_rank(above, sm_w, &n_ab);
-    if (inbin) {
-      ck[base + r] = key;
-      ci[base + r] = (int32_t)j;
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u) {
+    if (j0 + u < g.c_hi && (key[u] >> 21) == d1) {
+      ck[r] = key[u];
+      ci[r] = (int32_t)(j0 + u);
+      ++r;
     }
-    base += n_in;
-    n_above += n_ab;
   }
-  if (tid == 0) w.above[(int64_t)h * w.nbm + b] = n_above;
+  if (tid == 0) w.above[(int64_t)h * w.nbm + b] = tot & 0xFFFFu;
 }
 
 __global__ __launch_bounds__(kSelThreads) void sel_pick2_kernel(const SelectArgs a) {
@@ -347,16 +374,42 @@ __global__ __launch_bounds__(kSelThreads) void sel_pick2_kernel(const SelectArgs
   __shared__ uint32_t sm_w[kSelWaves + 1];
   __shared__ uint32_t sm_digit, sm_krem, sm_jt;
   __shared__ uint32_t sm_kept[1024];
+  // bin members staged in LDS when they fit (the usual case): the three
+  // passes below then read LDS instead of global memory
+  __shared__ uint32_t sm_ck[kStageCand];
+  __shared__ int32_t sm_ci[kStageCand];
   const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
   const int h = blockIdx.x, tid = threadIdx.x;
   const SelGeom g = sel_geom(a, h);
   uint32_t* hd = w.head + (int64_t)h * 8;
-  if (hd[0] != kModeRadix) return;
-  const uint32_t C = hd[3];
   const uint32_t* ck = w.ckey + (int64_t)h * a.n;
   const int32_t* ci = w.cidx + (int64_t)h * a.n;
-  uint32_t prefix = hd[1] << 21, mask = 0xFFE00000u;
-  uint32_t krem = hd[2];
+  // every independent load in one round: head state, the blocks' counts
+  // above the bin, and (speculatively) the first kStageCand bin members
+  constexpr int kPre = kStageCand / kSelThreads;
+  uint32_t pk[kPre];
+  int32_t pi[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {  // rows hold n > kStageCand entries: in bounds
+    pk[u] = ck[tid * kPre + u];
+    pi[u] = ci[tid * kPre + u];
+  }
+  const uint32_t abv = tid < g.nb ? w.above[(int64_t)h * w.nbm + tid] : 0u;
+  const uint32_t mode = hd[0], d1h = hd[1], krem0 = hd[2], C = hd[3];
+  if (mode != kModeRadix) return;  // uniform
+  const bool staged = C <= (uint32_t)kStageCand;
+  if (staged) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      sm_ck[tid * kPre + u] = pk[u];
+      sm_ci[tid * kPre + u] = pi[u];
+    }
+    __syncthreads();
+    ck = sm_ck;
+    ci = sm_ci;
+  }
+  uint32_t prefix = d1h << 21, mask = 0xFFE00000u;
+  uint32_t krem = krem0;
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass == 0 ? 10 : 0;
@@ -396,27 +449,48 @@ __global__ __launch_bounds__(kSelThreads) void sel_pick2_kernel(const SelectArgs
   for (int b = tid; b < 1024; b += kSelThreads) sm_kept[b] = 0u;
   if (tid == 0) sm_jt = 0xFFFFFFFFu;
   __syncthreads();
-  uint32_t eq_seen = 0;
-#pragma unroll 1
-  for (uint32_t t0 = 0; t0 < C; t0 += kSelThreads) {
-    const uint32_t i = t0 + tid;
-    const bool valid = i < C;
-    const uint32_t key = valid ? ck[i] : 0u;
-    const bool eq = valid && key == T;
-    uint32_t n_eq;
-    const uint32_t eq_rank = eq_seen + block_flag_rank(eq, sm_w, &n_eq);
-    const bool keep = valid && (key > T || (eq && eq_rank < take));
-    if (keep) {
+  auto keep_member = [&](uint32_t i, uint32_t key, uint32_t eq_rank) {
+    const bool eq = key == T;
+    if (key > T || (eq && eq_rank < take)) {
       const int32_t j = ci[i];
       atomicAdd(&sm_kept[(j - g.c_lo) / kBlk], 1u);
       if (eq && eq_rank == take - 1) sm_jt = (uint32_t)j;
     }
-    eq_seen += n_eq;
+  };
+  if (staged) {
+    // kPre consecutive members per thread: one scan ranks the equal keys
+    const uint32_t i0 = (uint32_t)tid * kPre;
+    uint32_t n_eq = 0;
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) n_eq += (i0 + u < C && ck[i0 + u] == T) ? 1u : 0u;
+    uint32_t tot_eq;
+    uint32_t eq_rank = block_excl_scan(n_eq, sm_w, &tot_eq);
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const uint32_t i = i0 + u;
+      if (i < C) {
+        const uint32_t key = ck[i];
+        keep_member(i, key, eq_rank);
+        eq_rank += key == T ? 1u : 0u;
+      }
+    }
+  } else {
+    uint32_t eq_seen = 0;
+#pragma unroll 1
+    for (uint32_t t0 = 0; t0 < C; t0 += kSelThreads) {
+      const uint32_t i = t0 + tid;
+      const bool valid = i < C;
+      const uint32_t key = valid ? ck[i] : 0u;
+      uint32_t n_eq;
+      const uint32_t eq_rank = eq_seen + block_flag_rank(valid && key == T, sm_w, &n_eq);
+      if (valid) keep_member(i, key, eq_rank);
+      eq_seen += n_eq;
+    }
   }
   __syncthreads();
   // output offset of each block: sinks, then blocks in order
   uint32_t mine = 0;
-  if (tid < g.nb) mine = w.above[(int64_t)h * w.nbm + tid] + sm_kept[tid];
+  if (tid < g.nb) mine = abv + sm_kept[tid];
   uint32_t total;
   const uint32_t off = block_excl_scan(mine, sm_w, &total);
   if (tid < g.nb) w.outoff[(int64_t)h * w.nbm + tid] = (uint32_t)g.nsink + off;
@@ -432,26 +506,36 @@ __global__ __launch_bounds__(kSelThreads) void sel_write_kernel(const SelectArgs
   const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
   const SelGeom g = sel_geom(a, h);
   if (b >= g.nb) return;
-  const uint32_t* hd = w.head + (int64_t)h * 8;
-  if (hd[0] == kModeNone) return;
-  const uint32_t T = hd[4];
-  const int64_t jt = hd[5] == 0xFFFFFFFFu ? -1 : (hd[0] == kModeAll ? INT64_MAX : (int64_t)hd[5]);
   const float* s = a.score + (int64_t)h * a.score_stride;
-  int32_t* out = a.idx + (int64_t)h * a.idx_stride;
   const int tid = threadIdx.x;
-  const int64_t j0 = g.c_lo + (int64_t)b * kBlk;
+  const int64_t j0 = g.c_lo + (int64_t)b * kBlk + kBlkPer * tid;
+  float sv[kBlkPer];
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u) sv[u] = j0 + u < g.c_hi ? s[j0 + u] : 0.0f;
+  const uint32_t* hd = w.head + (int64_t)h * 8;
+  const uint32_t mode = hd[0], T = hd[4], jtw = hd[5];
+  const uint32_t base = w.outoff[(int64_t)h * w.nbm + b];
+  if (mode == kModeNone) return;  // uniform
+  const int64_t jt = jtw == 0xFFFFFFFFu ? -1 : (mode == kModeAll ? INT64_MAX : (int64_t)jtw);
+  bool keep[kBlkPer];
+  uint32_t n_keep = 0;
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u) {
+    const int64_t j = j0 + u;
+    const uint32_t key = score_key(sv[u]);
+    keep[u] = j < g.c_hi && (key > T || (key == T && j <= jt));
+    n_keep += keep[u] ? 1u : 0u;
+  }
+  uint32_t tot;
+  uint32_t pos = base + block_excl_scan(n_keep, sm_w, &tot);
+  int32_t* out = a.idx + (int64_t)h * a.idx_stride;
   const uint32_t limit = (uint32_t)(g.nsink + g.K);
-  uint32_t base = w.outoff[(int64_t)h * w.nbm + b];
-#pragma unroll 1
-  for (int t = 0; t < kBlkPer; ++t) {
-    const int64_t j = j0 + t * kSelThreads + tid;
-    const bool valid = j < g.c_hi;
-    const uint32_t key = valid ? score_key(s[j]) : 0u;
-    const bool keep = valid && (key > T || (key == T && j <= jt));
-    uint32_t n_keep;
-    const uint32_t pos = base + block_flag_rank(keep, sm_w, &n_keep);
-    if (keep && pos < limit) out[pos] = (int32_t)j;  // never past the row
-    base += n_keep;
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u) {
+    if (keep[u]) {
+      if (pos < limit) out[pos] = (int32_t)(j0 + u);  // never past the row
+      ++pos;
+    }
   }
 }
 
