@@ -63,7 +63,7 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
   __shared__ __attribute__((aligned(1024))) char st2[W][2 * TB];
   __shared__ __attribute__((aligned(1024))) char st3[W][2 * TB];
   __shared__ __attribute__((aligned(16))) uint32_t sm_off[SPARSE ? kSparseMaxChunk : 1];
-  __shared__ float sm_m[W][16], sm_l[W][16];
+  __shared__ float sm_m[S][W][16], sm_l[S][W][16];
   static_assert(S >= 2 && S <= 4, "ring of two to four stages");
   static_assert(16 * D * 4 <= 2 * TB, "a wave's 16-row partial fits its first stage");
   static_assert(!(SPARSE && CAUSAL), "the causal pass is dense");
@@ -385,54 +385,68 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
     }
   }
 
-  // Per row group: each wave parks its partial in its own first stage (its
-  // copies are done); 16 threads turn the waves' (max, sum) into the row's
-  // max, sum and one weight per wave; then the workgroup folds the waves'
-  // accumulators into the chunk's partial of those rows.
+  // Folding the waves, S row groups per round: each wave parks the partial
+  // of group g0 + u in its own stage u (its copies are done); 16 threads per
+  // group turn the waves' (max, sum) into the row's max, sum and one weight
+  // per wave; then the workgroup folds the waves' accumulators.
+  constexpr int GPR = S < NG ? S : NG;  // groups per round
   const int64_t slot = (int64_t)h * cph + c;
-  float (*acc_w)[D] = reinterpret_cast<float (*)[D]>(&st0[wave][0]);
 #pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    if (16 * gi >= R) break;  // uniform
-    float lg = l[gi];
-    lg += __shfl_xor(lg, 16, 64);
-    lg += __shfl_xor(lg, 32, 64);
-    if (lane < 16) {
-      sm_m[wave][lane] = nst == 0 ? kNegInf : m[gi];
-      sm_l[wave][lane] = nst == 0 ? 0.0f : lg;
+  for (int g0 = 0; g0 < NG; g0 += GPR) {
+    if (16 * g0 >= R) break;  // uniform
+#pragma unroll
+    for (int u = 0; u < GPR; ++u) {
+      const int gi = g0 + u;
+      if (gi < NG) {
+        float lg = l[gi];
+        lg += __shfl_xor(lg, 16, 64);
+        lg += __shfl_xor(lg, 32, 64);
+        if (lane < 16) {
+          sm_m[u][wave][lane] = nst == 0 ? kNegInf : m[gi];
+          sm_l[u][wave][lane] = nst == 0 ? 0.0f : lg;
+        }
+        float (*acc_w)[D] = reinterpret_cast<float (*)[D]>(&ring(u)[wave][0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc_w[4 * q4 + r][16 * n + li] = o[gi][n][r];
+      }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc_w[4 * q4 + r][16 * n + li] = o[gi][n][r];
     __syncthreads();
-    if (tid < 16) {
-      const int row = 16 * gi + tid;
-      float M = sm_m[0][tid];
+    if (tid < 16 * GPR) {
+      const int u = tid >> 4, rr = tid & 15;
+      const int row = 16 * (g0 + u) + rr;
+      float M = sm_m[u][0][rr];
 #pragma unroll
-      for (int w = 1; w < W; ++w) M = fmaxf(M, sm_m[w][tid]);
+      for (int w = 1; w < W; ++w) M = fmaxf(M, sm_m[u][w][rr]);
       float L = 0.0f;
 #pragma unroll
       for (int w = 0; w < W; ++w) {
-        const float sc = (sm_m[w][tid] == kNegInf) ? 0.0f : fast_exp2(sm_m[w][tid] - M);
-        L += sm_l[w][tid] * sc;
-        sm_l[w][tid] = sc;  // now the wave's weight
+        const float sc = (sm_m[u][w][rr] == kNegInf) ? 0.0f : fast_exp2(sm_m[u][w][rr] - M);
+        L += sm_l[u][w][rr] * sc;
+        sm_l[u][w][rr] = sc;  // now the wave's weight
       }
-      if (row < R) {
+      if (g0 + u < NG && row < R) {
         a.part_ml[(slot * R + row) * 2 + 0] = M;
         a.part_ml[(slot * R + row) * 2 + 1] = L;
       }
     }
     __syncthreads();
-    for (int e = tid; e < 16 * D; e += kT) {
-      const int rr = e / D, dd = e - rr * D;
-      const int row = 16 * gi + rr;
-      if (row < R) {
-        float A = 0.0f;
 #pragma unroll
-        for (int w = 0; w < W; ++w)
-          A += reinterpret_cast<const float (*)[D]>(&st0[w][0])[rr][dd] * sm_l[w][rr];
-        a.part_acc[(slot * R + row) * D + dd] = A;
+    for (int u = 0; u < GPR; ++u) {
+      const int gi = g0 + u;
+      if (gi < NG) {
+        for (int e = tid; e < 16 * D; e += kT) {
+          const int rr = e / D, dd = e - rr * D;
+          const int row = 16 * gi + rr;
+          if (row < R) {
+            float A = 0.0f;
+#pragma unroll
+            for (int w = 0; w < W; ++w)
+              A += reinterpret_cast<const float (*)[D]>(&ring(u)[w][0])[rr][dd] * sm_l[u][w][rr];
+            a.part_acc[(slot * R + row) * D + dd] = A;
+          }
+        }
       }
     }
     __syncthreads();
