@@ -145,6 +145,26 @@ skv_status skv_verify(const skv_problem* p, const void* q, int32_t gamma, const 
                       const void* v, int64_t n, float* out, float* lse, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* Compaction ([BX] "Speedup Across Context": the kept entries are gathered
+ * once into a contiguous buffer that every later step reads with one kernel
+ * call).  For each kv head h, copies K and V rows idx[h * idx_stride + i],
+ * i < count[h], then the tail [tail_start, n), to rows 0 .. rows_h - 1 of the
+ * output cache, rows_h = count[h] + (n - tail_start); row r of head h is at
+ * k_out / v_out + h * out_head_stride + r * out_pos_stride (elements of the
+ * problem's dtype, same alignment rules as the input cache).  The output must
+ * hold rows_max = min(idx_stride, tail_start) + (n - tail_start) rows per
+ * head; rows at or beyond rows_h are left untouched.  rows_out (device, may be
+ * NULL) receives rows_h.  On the device count[h] is clamped to
+ * [0, min(idx_stride, tail_start)] and index entries to [0, n), so every write
+ * stays inside rows_max rows; the copy is exact (bytes).  With equal
+ * counts on every head the output is an ordinary cache of rows_h positions
+ * for skv_attend_dense, which then gives the result of skv_attend_sparse on
+ * the same set.  Input and output must not overlap. */
+skv_status skv_gather(const skv_problem* p, const void* k, const void* v, int64_t n,
+                      const int32_t* idx, int64_t idx_stride, const int32_t* count,
+                      int64_t tail_start, void* k_out, void* v_out, int64_t out_head_stride,
+                      int64_t out_pos_stride, int32_t* rows_out, void* stream);
+
 /* Per-head budgets ([SMM] method section), host only.  For N heads with
  * visual scores s (host), total budget B, local window w and share rho:
  *   r = rho (B - N w) / N,  B_remain = B - N w - rho (B - N w),

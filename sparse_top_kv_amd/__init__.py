@@ -3,7 +3,8 @@
 Argument marshalling only: every step runs in the HIP kernels of
 ``libsparsekv.so`` (built from ``csrc/`` by ``sparse_top_kv_amd.build``).  The
 functions carry the C names (``skv_score``, ``skv_select``,
-``skv_attend_sparse``, ``skv_attend_dense``, ``skv_verify``, ``skv_budgets``)
+``skv_attend_sparse``, ``skv_attend_dense``, ``skv_verify``, ``skv_gather``,
+``skv_budgets``)
 and take torch tensors on a ROCm device; torch provides device memory and the
 current stream, nothing else.  A missing library raises at the first call.
 
@@ -64,9 +65,10 @@ def _load():
         lib.skv_attend_sparse.argtypes = [P, vp, vp, vp, i64, vp, i64, vp, i64, vp, vp, vp, sz, vp]
         lib.skv_attend_dense.argtypes = [P, vp, vp, vp, i64, vp, vp, vp, sz, vp]
         lib.skv_verify.argtypes = [P, vp, i32, vp, vp, i64, vp, vp, vp, sz, vp]
+        lib.skv_gather.argtypes = [P, vp, vp, i64, vp, i64, vp, i64, vp, vp, i64, i64, vp, vp]
         lib.skv_budgets.argtypes = [vp, i32, ctypes.c_double, i32, ctypes.c_double, i64, vp, vp]
         for f in ("skv_workspace_init", "skv_score", "skv_select", "skv_attend_sparse",
-                  "skv_attend_dense", "skv_verify", "skv_budgets"):
+                  "skv_attend_dense", "skv_verify", "skv_gather", "skv_budgets"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -157,6 +159,11 @@ def skv_workspace_init(ws: Workspace, stream=None):
         raise SkvError(st, "skv_workspace_init")
 
 
+def _idx_stride(idx):
+    # an empty index list [Hkv][0] has no row stride to speak of
+    return idx.stride(0) if idx.shape[-1] > 0 else 0
+
+
 def _rows(q, hq):
     return q.shape[0] if q.dim() == 3 else 1
 
@@ -201,7 +208,7 @@ def skv_attend_sparse(q, k, v, n: int, idx, count, tail_start: int, out, lse, ws
         raise ValueError("K and V must share strides")
     p = problem_for(q, k, scale)
     st = _load().skv_attend_sparse(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), n, _ptr(idx),
-                                   idx.stride(0), _ptr(count), tail_start, _ptr(out), _ptr(lse),
+                                   _idx_stride(idx), _ptr(count), tail_start, _ptr(out), _ptr(lse),
                                    ws.ptr, ws.nbytes, _stream(stream))
     if st != SKV_OK:
         raise SkvError(st, "skv_attend_sparse")
@@ -232,6 +239,28 @@ def skv_verify(q, k, v, n: int, out, lse, ws: Workspace, scale: float = 0.0, str
     if st != SKV_OK:
         raise SkvError(st, "skv_verify")
     return out, lse
+
+
+def skv_gather(k, v, n: int, idx, count, tail_start: int, k_out, v_out, rows_out=None,
+               stream=None):
+    """Copy each kv head's idx[h][:count[h]] rows and the tail [tail_start, n) of K and V
+    into k_out / v_out ([Hkv][>= rows_max][d], same dtype); rows_out[h] = rows copied."""
+    torch = _torch()
+    _check_dev(k, v, idx, count, k_out, v_out, rows_out)
+    if k.stride() != v.stride() or k_out.stride() != v_out.stride():
+        raise ValueError("K and V (and their outputs) must share strides")
+    if k_out.dtype != k.dtype or v.dtype != k.dtype or k_out.stride(2) != 1:
+        raise ValueError("outputs must match the cache dtype with contiguous channels")
+    for t in (idx, count) + ((rows_out,) if rows_out is not None else ()):
+        if t.dtype != torch.int32:
+            raise TypeError("idx, count and rows_out are int32")
+    p = problem(k.shape[0], k.shape[0], k.shape[2], _dtype_code(k), k.stride(0), k.stride(1))
+    st = _load().skv_gather(ctypes.byref(p), _ptr(k), _ptr(v), n, _ptr(idx), _idx_stride(idx),
+                            _ptr(count), tail_start, _ptr(k_out), _ptr(v_out), k_out.stride(0),
+                            k_out.stride(1), _ptr(rows_out), _stream(stream))
+    if st != SKV_OK:
+        raise SkvError(st, "skv_gather")
+    return k_out, v_out
 
 
 def skv_budgets(s, total_budget: float, window: int, rho: float, n_cand: int):

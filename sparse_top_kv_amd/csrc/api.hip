@@ -448,6 +448,47 @@ skv_status skv_verify(const skv_problem* p, const void* q, int32_t gamma, const 
   return launch_partials_merge(p, base, L, cp.cph, gamma * G, false, out, lse, (hipStream_t)stream);
 }
 
+skv_status skv_gather(const skv_problem* p, const void* k, const void* v, int64_t n,
+                      const int32_t* idx, int64_t idx_stride, const int32_t* count,
+                      int64_t tail_start, void* k_out, void* v_out, int64_t out_head_stride,
+                      int64_t out_pos_stride, int32_t* rows_out, void* stream) {
+  skv_status st = check_problem(p);
+  if (st != SKV_OK) return st;
+  if (n < 1 || !count || (!idx && idx_stride > 0) || idx_stride < 0) return SKV_ERR_INVALID_ARG;
+  if (tail_start < 0 || tail_start > n) return SKV_ERR_INVALID_ARG;
+  if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
+  if ((st = check_cache(p, k, n)) != SKV_OK || (st = check_cache(p, v, n)) != SKV_OK) return st;
+  const int64_t count_max = idx_stride < tail_start ? idx_stride : tail_start;
+  const int64_t rows_max = count_max + (n - tail_start);
+  if (rows_max < 1) return SKV_ERR_INVALID_ARG;
+  const int es = elem_size(p);
+  if (!k_out || !v_out || !aligned16(k_out) || !aligned16(v_out)) return SKV_ERR_INVALID_ARG;
+  if (out_pos_stride < p->head_dim || (out_pos_stride * es) % 16 != 0 ||
+      (out_head_stride * es) % 16 != 0 || out_head_stride < 0)
+    return SKV_ERR_INVALID_ARG;
+  if (p->n_kv_heads > 1 && out_head_stride < rows_max * out_pos_stride) return SKV_ERR_INVALID_ARG;
+  skv::GatherArgs a{};
+  a.k = (const char*)k;
+  a.v = (const char*)v;
+  a.head_stride_b = p->kv_head_stride * es;
+  a.pos_stride_b = p->kv_pos_stride * es;
+  a.n = n;
+  a.idx = idx;
+  a.idx_stride = idx_stride;
+  a.count = count;
+  a.count_max = count_max;
+  a.tail_start = tail_start;
+  a.k_out = (char*)k_out;
+  a.v_out = (char*)v_out;
+  a.out_head_stride_b = out_head_stride * es;
+  a.out_pos_stride_b = out_pos_stride * es;
+  a.rows_max = rows_max;
+  a.rows_out = rows_out;
+  a.n_kv_heads = p->n_kv_heads;
+  a.row_bytes = p->head_dim * es;
+  return hip_status(skv::launch_gather(a, (hipStream_t)stream));
+}
+
 skv_status skv_budgets(const double* s, int32_t n_heads, double total_budget, int32_t window,
                        double rho, int64_t n_cand, int32_t* k_out, double* b_out) {
   if (!s || !k_out || n_heads < 1 || window < 0 || !(rho >= 0.0 && rho <= 1.0) || n_cand < 0 ||

@@ -122,4 +122,25 @@ size_t select_ws_bytes(int32_t n_kv_heads, int64_t n);
 // Causal verify of gamma queries on MFMA (bf16).
 hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t stream);
 
+// Compaction of a kept set (skv_gather).
+struct GatherArgs {
+  const char* k;
+  const char* v;
+  int64_t head_stride_b, pos_stride_b;
+  int64_t n;
+  const int32_t* idx;
+  int64_t idx_stride;
+  const int32_t* count;
+  int64_t count_max;        // min(idx_stride, tail_start)
+  int64_t tail_start;
+  char* k_out;
+  char* v_out;
+  int64_t out_head_stride_b, out_pos_stride_b;
+  int64_t rows_max;
+  int32_t* rows_out;        // may be null
+  int32_t n_kv_heads;
+  int32_t row_bytes;        // d * element bytes
+};
+hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
+
 }  // namespace skv

@@ -110,3 +110,23 @@ def test_budgets_entry_point_equals_oracle():
     np.testing.assert_allclose(b1, b2, rtol=1e-15)
     with pytest.raises(skv.SkvError):
         skv.skv_budgets(np.array([1.0, -1.0]), 10, 1, 0.1, 5)
+
+
+def test_gather_validation():
+    lib = skv._load()
+    p = _p()
+    b = ctypes.byref(p)
+
+    def g(n=100, idx_stride=20, tail=90, out=FAKE, ohs=4096 * 128, ops=128, count=FAKE):
+        return lib.skv_gather(b, _vp(FAKE), _vp(FAKE), n, _vp(FAKE), idx_stride, _vp(count), tail,
+                              _vp(out), _vp(FAKE), ohs, ops, _vp(0), _vp(0))
+
+    assert g(tail=101) == skv.SKV_ERR_INVALID_ARG                 # tail_start > n
+    assert g(count=0) == skv.SKV_ERR_INVALID_ARG                  # null count
+    assert g(out=0) == skv.SKV_ERR_INVALID_ARG                    # null output
+    assert g(out=FAKE + 8) == skv.SKV_ERR_INVALID_ARG             # misaligned output
+    assert g(ops=64) == skv.SKV_ERR_INVALID_ARG                   # row stride < d
+    assert g(ops=132) == skv.SKV_ERR_INVALID_ARG                  # row stride not 16-byte
+    assert g(ohs=29 * 128) == skv.SKV_ERR_INVALID_ARG             # heads overlap: 20 + 10 rows
+    assert g(n=0, tail=0) == skv.SKV_ERR_INVALID_ARG
+    assert g(idx_stride=0, tail=100) == skv.SKV_ERR_INVALID_ARG   # nothing to copy
