@@ -134,6 +134,27 @@ def select(score32: np.ndarray, n_sink: int, n_recent: int, k_per_head, idx_stri
     return idx, cnt
 
 
+def select_topp(score32: np.ndarray, n_sink: int, n_recent: int, lam: float, prune: float,
+                pooled: bool = False, fill_mode: int = 0, idx_stride=None):
+    """SpecVLM two-stage selection (top-P retention, then uniform fill).
+    Returns (idx [H][stride], count [H], count_r [H] = |V_R|)."""
+    lib = _load()
+    score32 = np.ascontiguousarray(score32, dtype=np.float32)
+    h, n = score32.shape
+    if idx_stride is None:
+        idx_stride = max(1, n - n_recent if n - n_recent > 0 else 1)
+    idx = np.full((h, idx_stride), -1, np.int32)
+    cnt = np.zeros(h, np.int32)
+    cnt_r = np.zeros(h, np.int32)
+    rc = lib.ora_select_topp(_ptr(score32), ctypes.c_int64(n), ctypes.c_int32(h), ctypes.c_int64(n),
+                             ctypes.c_int32(n_sink), ctypes.c_int32(n_recent), ctypes.c_double(lam),
+                             ctypes.c_double(prune), ctypes.c_int32(int(pooled)),
+                             ctypes.c_int32(fill_mode), _ptr(idx), ctypes.c_int64(idx_stride),
+                             _ptr(cnt), _ptr(cnt_r))
+    _check(rc, "select_topp")
+    return idx, cnt, cnt_r
+
+
 def attend_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, n: int, scale=None,
                  nthreads=None):
     """Exact attention of q [Hq][d] over keys [0, n); returns (out [Hq][d], lse [Hq])."""

@@ -253,6 +253,113 @@ int ora_select(const float* score, int64_t score_stride, int32_t Hkv, int64_t n,
   return 0;
 }
 
+// Verifier-guided selection (SpecVLM blog, "The SpecVLM Method": Stage I
+// top-P retention, Stage II spatially uniform reduction).  Candidates, sinks
+// and the recent run are split as in ora_select.  One selection per score row,
+// or, with pooled != 0, one selection on the per-token sum over all rows that
+// every row then receives (the blog averages over layers and heads; the
+// constant factor does not change the selection).
+//
+// Readings, in the order the blog gives the steps:
+//   mass     a_j >= 0 is measured exactly as the integer u_j = floor(a_j 2^S)
+//            (pooled: the sum over rows of those integers), with
+//            S = 62 - E - ceil(log2 N), 2^(E-1) <= max a < 2^E and N the number
+//            of terms summed into one total (n_cand, or rows x n_cand); every
+//            total then stays below 2^62 and all sums are exact;
+//   order    u descending, index ascending;
+//   Stage I  c = the smallest c' whose first c' candidates in that order carry
+//            mass >= lambda * (total mass), compared exactly; V_R = those c;
+//   Stage II B = (1 - r) n_cand rounded to nearest in double (ties away from
+//            zero: r = 0.9 of 100 candidates gives 10); the L = n_cand - c leftover
+//            candidates, in ascending index order, are sampled at ranks
+//            floor(i L / n_U), i < n_U, where n_U = clamp(B - c, 0, L)
+//            (fill_mode 0: the interval that brings the kept set to B) or
+//            n_U = min(B, L) (fill_mode 1: the interval as printed,
+//            (|V| - |V_R|) / ((1 - r) |V|)).
+// idx[h][0..count[h]) = sinks, V_R and V_U in ascending order; count_r[h] = c.
+// Scores must be finite and >= 0 (else 2).
+int ora_select_topp(const float* score, int64_t score_stride, int32_t H, int64_t n, int32_t S,
+                    int32_t R, double lambda, double prune, int32_t pooled, int32_t fill_mode,
+                    int32_t* idx, int64_t idx_stride, int32_t* count, int32_t* count_r) {
+  if (!score || !idx || !count || H < 1 || n < 1 || S < 0 || R < 0 || score_stride < n ||
+      !(lambda >= 0.0 && lambda <= 1.0) || !(prune >= 0.0 && prune <= 1.0) ||
+      (fill_mode != 0 && fill_mode != 1))
+    return 1;
+  typedef unsigned __int128 u128;
+  const int64_t tail = std::max<int64_t>(n - R, 0);
+  const int64_t nsink = std::min<int64_t>(S, tail);
+  const int64_t c_lo = S, ncand = (S < n - R) ? (n - R) - S : 0;
+  if (idx_stride < nsink + ncand) return 1;
+  for (int h = 0; h < H; ++h)
+    for (int64_t j = c_lo; j < c_lo + ncand; ++j) {
+      const float x = score[h * score_stride + j];
+      if (!std::isfinite(x) || x < 0.0f) return 2;
+    }
+  const int64_t budget = std::llround((1.0 - prune) * (double)ncand);
+  const int n_sel = pooled ? 1 : H;
+  for (int sel = 0; sel < n_sel; ++sel) {
+    const int h0 = pooled ? 0 : sel, h1 = pooled ? H : sel + 1;
+    // fixed-point scale from the largest score and the number of summed terms
+    double amax = 0.0;
+    for (int h = h0; h < h1; ++h)
+      for (int64_t j = c_lo; j < c_lo + ncand; ++j) amax = std::max(amax, (double)score[h * score_stride + j]);
+    std::vector<uint64_t> u(ncand, 0);
+    if (amax > 0.0) {
+      int E = 0;
+      std::frexp(amax, &E);
+      const int64_t terms = (int64_t)(h1 - h0) * ncand;
+      int lg = 0;
+      while (((int64_t)1 << lg) < terms) ++lg;
+      const int Sfix = 62 - E - lg;
+      for (int64_t i = 0; i < ncand; ++i)
+        for (int h = h0; h < h1; ++h)
+          u[i] += (uint64_t)std::floor(std::ldexp((double)score[h * score_stride + c_lo + i], Sfix));
+    }
+    uint64_t total = 0;
+    for (int64_t i = 0; i < ncand; ++i) total += u[i];
+    // Stage I: sort by mass, keep the shortest prefix reaching lambda of the total
+    std::vector<int64_t> order(ncand);
+    for (int64_t i = 0; i < ncand; ++i) order[i] = i;
+    std::sort(order.begin(), order.end(), [&](int64_t a, int64_t b) {
+      if (u[a] != u[b]) return u[a] > u[b];
+      return a < b;
+    });
+    int mexp = 0;
+    const double mfrac = std::frexp(lambda, &mexp);          // lambda = mfrac 2^mexp
+    const uint64_t lam_m = (uint64_t)std::ldexp(mfrac, 53);  // exact: 53-bit mantissa
+    const int lam_sh = 53 - mexp;                            // lambda = lam_m / 2^lam_sh
+    // an integer mass m reaches lambda * total exactly when m >= ceil(lambda * total)
+    const u128 prod = (u128)lam_m * total;
+    uint64_t theta;
+    if (lam_sh >= 128) theta = prod != 0;
+    else theta = (uint64_t)((prod >> lam_sh) + ((prod & (((u128)1 << lam_sh) - 1)) != 0));
+    int64_t c = 0;
+    uint64_t acc = 0;
+    while (c < ncand && acc < theta) acc += u[order[c++]];
+    std::vector<char> in_r(ncand, 0);
+    for (int64_t i = 0; i < c; ++i) in_r[order[i]] = 1;
+    // Stage II: uniform walk through the leftovers in index order
+    const int64_t L = ncand - c;
+    int64_t n_u = fill_mode == 0 ? std::min(std::max<int64_t>(budget - c, 0), L) : std::min(budget, L);
+    std::vector<char> in_u(ncand, 0);
+    if (n_u > 0) {
+      std::vector<int64_t> left;
+      for (int64_t i = 0; i < ncand; ++i)
+        if (!in_r[i]) left.push_back(i);
+      for (int64_t t = 0; t < n_u; ++t) in_u[left[(t * L) / n_u]] = 1;
+    }
+    for (int h = h0; h < h1; ++h) {
+      int64_t w = 0;
+      for (int64_t j = 0; j < nsink; ++j) idx[h * idx_stride + w++] = (int32_t)j;
+      for (int64_t i = 0; i < ncand; ++i)
+        if (in_r[i] || in_u[i]) idx[h * idx_stride + w++] = (int32_t)(c_lo + i);
+      count[h] = (int32_t)w;
+      if (count_r) count_r[h] = (int32_t)c;
+    }
+  }
+  return 0;
+}
+
 // Dense decode attention (BX "The Attention Baseline": the dense step reads the
 // whole cache): one decode query per head at position n-1 over keys [0, n).
 // q [Hq][d]; out [Hq][d]; lse [Hq] (natural log of the softmax normaliser).
