@@ -23,7 +23,8 @@ sets into contiguous caches (gather once, then the dense step over them),
 dense steps at 2K-128K, the
 per-step top-K pipeline at 128K (score -> select -> gathered attention), the
 Sparse-to-Dense round of the Qwen2-7B video workload (5 sparse drafts + one
-gamma=5 verify), one-time selection costs, and the byte-count speedup bounds.
+gamma=5 verify), the SpecVLM selection on it (top-P 0.5 + uniform fill to
+10 % of the video tokens) and the round over that set, one-time selection costs, and the byte-count speedup bounds.
 `--sections all` adds the 1024-head SparseMM batched step (17 GB of cache).
 
 cpu_baseline: the fp64 oracle (test infrastructure) timed on this host on a
@@ -87,6 +88,9 @@ def main():
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
+
+    def host_list(t):
+        return [int(x) for x in t.cpu().tolist()]
 
     def time_steps(step, nsteps, warmup, blocks, graph=True):
         """Median over blocks of (elapsed / nsteps) in microseconds, timed with HIP
@@ -338,8 +342,34 @@ def main():
             k4, v4 = kv4[i % L4]
             skv.skv_verify(qv4, k4, v4, m + gamma, ov, lv, ws4)
 
+        # SpecVLM selection on the same text-window score: top-P retention
+        # (lambda 0.5) + uniform fill to 10 % of the video tokens (r = 90 %)
+        vidx4 = torch.empty((hkv4, m_v), dtype=torch.int32, device="cuda")
+        vcnt4 = torch.empty(hkv4, dtype=torch.int32, device="cuda")
+        vcr4 = torch.empty(hkv4, dtype=torch.int32, device="cuda")
+
+        def topp4(i):
+            skv.skv_select_topp(sc4, m, 0, m_t, 0.5, 0.9, vidx4, vcnt4, ws4, count_r=vcr4)
+
+        def topp4_pooled(i):
+            skv.skv_select_topp(sc4, m, 0, m_t, 0.5, 0.9, vidx4, vcnt4, ws4, count_r=vcr4, pooled=True)
+
+        sel4(0)
+        tp_pool_us, _ = time_steps(topp4_pooled, 8, 2, 3)
+        tp_us, _ = time_steps(topp4, 8, 2, 3)
+        torch.cuda.synchronize()
+        v_kept = host_list(vcnt4)
+        v_ret = host_list(vcr4)
+
+        def round_specvlm(i):
+            k4, v4 = kv4[i % L4]
+            for t in range(gamma):
+                skv.skv_attend_sparse(qd4[t], k4, v4, m + t + 1, vidx4, vcnt4, m_v, o4, l4, ws4)
+            skv.skv_verify(qv4, k4, v4, m + gamma, ov, lv, ws4)
+
         log("timing the Sparse-to-Dense round")
         r_us, _ = time_steps(round_std, max(20, args.steps // 4), 5, 3)
+        rv_us, _ = time_steps(round_specvlm, max(20, args.steps // 4), 5, 3)
         rd_us, _ = time_steps(round_dense, max(20, args.steps // 4), 5, 3)
         v_us, _ = time_steps(verify_only, args.steps, args.warmup, 3)
         v_bytes = rf.verify_bytes(hq4, hkv4, d, m + gamma, gamma, "bf16")
@@ -356,6 +386,11 @@ def main():
             "verify_mfma_frac_of_bf16_peak": round(
                 rf.verify_flops(hq4, m + gamma, d, gamma) / (v_us * 1e-6) / 2.5e15, 5),
             "round_speedup_measured_alpha1": round(rd_us / r_us, 3),
+            "specvlm_topp_select_us": round(tp_us, 2),
+            "specvlm_topp_select_pooled_us": round(tp_pool_us, 2),
+            "specvlm_kept_per_head": v_kept,
+            "specvlm_top_p_retained_per_head": v_ret,
+            "specvlm_round_5_drafts_plus_verify_us": round(rv_us, 2),
             "round_speedup_byte_bound_alpha1": round(dense_round_bytes / (draft_bytes + v_bytes), 3),
         }
         del kv4

@@ -13,6 +13,9 @@
  *         prompt queries, four sinks, highest-scoring entries per kv head,
  *         every step read by a split-K decoding kernel), header figure (sinks,
  *         scored history, run of recent entries), "The Attention Baseline".
+ *   [SV]  blog "Paper Breakdown: SpecVLM" (verifier-guided token pruning for
+ *         video speculative decoding): "The SpecVLM Method" (Stage I top-P
+ *         retention, Stage II spatially uniform reduction), "The Numbers".
  *   [SMM] blog on SparseMM, "Head Sparsity Emerges from Visual Concept
  *         Responses in MLLMs": method section (Local Window Cache w,
  *         Uniform-Based Cache rho, Score-Preferred Cache; observation window of
@@ -113,6 +116,32 @@ skv_status skv_select(const skv_problem* p, const float* score, int64_t score_st
                       const int32_t* k_per_head, int32_t k_uniform, int32_t k_max,
                       int32_t* idx, int64_t idx_stride, int32_t* count, void* ws,
                       size_t ws_bytes, void* stream);
+
+/* Verifier-guided selection ([SV] "The SpecVLM Method": Stage I top-P
+ * retention, Stage II spatially uniform reduction).  Sinks, recent window and
+ * candidates are split as in skv_select.  Per score row h (or, pooled = 1, once
+ * on the per-candidate sum over all n_kv_heads rows, the set then written to
+ * every row):
+ *   mass     u_j = floor(a_j 2^S), exact integers, S = 62 - E - ceil(log2 N)
+ *            with 2^(E-1) <= max a < 2^E and N the terms in one total;
+ *   Stage I  V_R = the shortest prefix of the candidates ordered by
+ *            (u descending, index ascending) whose mass is >= lambda * total
+ *            (exact comparison; c = |V_R|);
+ *   Stage II B = round((1 - prune_ratio) * #candidates) (double product,
+ *            halves away from zero); the L = #candidates - c leftovers, in
+ *            index order, are sampled at ranks floor(i L / n_U), i < n_U, with
+ *            n_U = clamp(B - c, 0, L) (fill_mode 0: the kept set is brought to
+ *            B) or n_U = min(B, L) (fill_mode 1: B uniform picks on top of V_R).
+ * Writes idx[h * idx_stride + i], i < count[h]: sinks, V_R and the uniform
+ * picks in ascending order; count_r[h] = c (device, may be NULL).  Scores are
+ * finite and >= 0 (others count as zero mass).  Requires 0 <= lambda <= 1,
+ * 0 <= prune_ratio <= 1, idx_stride >= #sinks + #candidates; pooled = 1 needs
+ * a workspace (skv_workspace_size covers it). */
+skv_status skv_select_topp(const skv_problem* p, const float* score, int64_t score_stride,
+                           int64_t n, int32_t n_sink, int32_t n_recent, double lambda,
+                           double prune_ratio, int32_t pooled, int32_t fill_mode, int32_t* idx,
+                           int64_t idx_stride, int32_t* count, int32_t* count_r, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /* Sparse decode attention ([StD] Sec. 3.2 top-K attention, Sec. 3.3 draft
  * reads K selected entries plus the text run; [BX] kept set read by one

@@ -4,7 +4,7 @@ Argument marshalling only: every step runs in the HIP kernels of
 ``libsparsekv.so`` (built from ``csrc/`` by ``sparse_top_kv_amd.build``).  The
 functions carry the C names (``skv_score``, ``skv_select``,
 ``skv_attend_sparse``, ``skv_attend_dense``, ``skv_verify``, ``skv_gather``,
-``skv_budgets``)
+``skv_select_topp``, ``skv_budgets``)
 and take torch tensors on a ROCm device; torch provides device memory and the
 current stream, nothing else.  A missing library raises at the first call.
 
@@ -65,10 +65,13 @@ def _load():
         lib.skv_attend_sparse.argtypes = [P, vp, vp, vp, i64, vp, i64, vp, i64, vp, vp, vp, sz, vp]
         lib.skv_attend_dense.argtypes = [P, vp, vp, vp, i64, vp, vp, vp, sz, vp]
         lib.skv_verify.argtypes = [P, vp, i32, vp, vp, i64, vp, vp, vp, sz, vp]
+        dbl = ctypes.c_double
+        lib.skv_select_topp.argtypes = [P, vp, i64, i64, i32, i32, dbl, dbl, i32, i32, vp, i64, vp,
+                                        vp, vp, sz, vp]
         lib.skv_gather.argtypes = [P, vp, vp, i64, vp, i64, vp, i64, vp, vp, i64, i64, vp, vp]
         lib.skv_budgets.argtypes = [vp, i32, ctypes.c_double, i32, ctypes.c_double, i64, vp, vp]
         for f in ("skv_workspace_init", "skv_score", "skv_select", "skv_attend_sparse",
-                  "skv_attend_dense", "skv_verify", "skv_gather", "skv_budgets"):
+                  "skv_attend_dense", "skv_verify", "skv_gather", "skv_select_topp", "skv_budgets"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -197,6 +200,28 @@ def skv_select(score, n: int, n_sink: int, n_recent: int, k_uniform: int, idx, c
                             _ptr(count), ws.ptr, ws.nbytes, _stream(stream))
     if st != SKV_OK:
         raise SkvError(st, "skv_select")
+    return idx, count
+
+
+def skv_select_topp(score, n: int, n_sink: int, n_recent: int, lam: float, prune: float, idx,
+                    count, ws: Workspace, count_r=None, pooled: bool = False, fill_mode: int = 0,
+                    stream=None):
+    """SpecVLM selection on an fp32 score [rows][>=n]: top-P retention (mass >= lam of the
+    total) plus a uniform fill; writes idx, count and (optionally) count_r = |V_R|."""
+    torch = _torch()
+    _check_dev(score, idx, count, count_r)
+    for t in (idx, count) + ((count_r,) if count_r is not None else ()):
+        if t.dtype != torch.int32:
+            raise TypeError("idx, count and count_r are int32")
+    if score.dtype != torch.float32 or score.stride(1) != 1:
+        raise ValueError("score must be fp32 [rows][>=n]")
+    p = problem(score.shape[0], score.shape[0], 128, SKV_BF16, 128, 128)
+    st = _load().skv_select_topp(ctypes.byref(p), _ptr(score), score.stride(0), n, n_sink,
+                                 n_recent, float(lam), float(prune), int(pooled), fill_mode,
+                                 _ptr(idx), idx.stride(0), _ptr(count), _ptr(count_r), ws.ptr,
+                                 ws.nbytes, _stream(stream))
+    if st != SKV_OK:
+        raise SkvError(st, "skv_select_topp")
     return idx, count
 
 

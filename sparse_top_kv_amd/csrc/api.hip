@@ -201,6 +201,9 @@ size_t verify_scratch(const skv_problem* p, int64_t n, int32_t gamma) {
   return part_layout(p, cp.cph, gamma * G).end - SKV_WS_HEADER_BYTES;
 }
 
+// Pooled top-P selection: one 64-bit fixed-point mass per candidate.
+size_t topp_scratch(int64_t n) { return ((size_t)n * 8 + kAlign - 1) / kAlign * kAlign; }
+
 }  // namespace
 
 extern "C" {
@@ -226,6 +229,8 @@ size_t skv_workspace_size(const skv_problem* p, int64_t n_max, int32_t rows_max)
   t = score_step_scratch(p, n_max);
   s = s > t ? s : t;
   t = skv::select_ws_bytes(p->n_kv_heads, n_max);
+  s = s > t ? s : t;
+  t = topp_scratch(n_max);
   s = s > t ? s : t;
   if (p->dtype == SKV_BF16) {
     const int32_t w = rows_max < n_max ? rows_max : (int32_t)n_max;
@@ -407,6 +412,47 @@ skv_status skv_select(const skv_problem* p, const float* score, int64_t score_st
   a.count = count;
   a.n_kv_heads = p->n_kv_heads;
   return hip_status(skv::launch_select(a, (hipStream_t)stream));
+}
+
+skv_status skv_select_topp(const skv_problem* p, const float* score, int64_t score_stride,
+                           int64_t n, int32_t n_sink, int32_t n_recent, double lambda,
+                           double prune_ratio, int32_t pooled, int32_t fill_mode, int32_t* idx,
+                           int64_t idx_stride, int32_t* count, int32_t* count_r, void* ws,
+                           size_t ws_bytes, void* stream) {
+  skv_status st = check_problem(p);
+  if (st != SKV_OK) return st;
+  if (n < 1 || !score || score_stride < n || n_sink < 0 || n_recent < 0 || !count || !idx)
+    return SKV_ERR_INVALID_ARG;
+  if (!(lambda >= 0.0 && lambda <= 1.0) || !(prune_ratio >= 0.0 && prune_ratio <= 1.0) ||
+      (pooled != 0 && pooled != 1) || (fill_mode != 0 && fill_mode != 1))
+    return SKV_ERR_INVALID_ARG;
+  if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
+  const int64_t tail = n - n_recent > 0 ? n - n_recent : 0;
+  const int64_t nsink = n_sink < tail ? n_sink : tail;
+  const int64_t ncand = n_sink < n - n_recent ? n - n_recent - n_sink : 0;
+  if (idx_stride < nsink + ncand) return SKV_ERR_INVALID_ARG;
+  if (pooled && (st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + topp_scratch(n))) != SKV_OK) return st;
+  skv::ToppArgs a{};
+  a.score = score;
+  a.score_stride = score_stride;
+  a.rows = p->n_kv_heads;
+  a.pooled = pooled;
+  a.n = n;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  // lambda = lam_m / 2^lam_sh exactly (53-bit mantissa)
+  int e = 0;
+  const double f = frexp(lambda, &e);
+  a.lam_m = (uint64_t)ldexp(f, 53);
+  a.lam_sh = 53 - e;
+  a.fill_mode = fill_mode;
+  a.budget = llround((1.0 - prune_ratio) * (double)ncand);
+  a.idx = idx;
+  a.idx_stride = idx_stride;
+  a.count = count;
+  a.count_r = count_r;
+  a.mass = pooled ? (uint64_t*)((char*)ws + SKV_WS_HEADER_BYTES) : nullptr;
+  return hip_status(skv::launch_select_topp(a, (hipStream_t)stream));
 }
 
 skv_status skv_verify(const skv_problem* p, const void* q, int32_t gamma, const void* k,

@@ -122,6 +122,26 @@ size_t select_ws_bytes(int32_t n_kv_heads, int64_t n);
 // Causal verify of gamma queries on MFMA (bf16).
 hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t stream);
 
+// Verifier-guided top-P retention + uniform fill (skv_select_topp).
+struct ToppArgs {
+  const float* score;
+  int64_t score_stride;
+  int32_t rows;             // score rows (kv heads)
+  int32_t pooled;           // 1: one selection on the sum over rows, given to every row
+  int64_t n;
+  int32_t n_sink, n_recent;
+  uint64_t lam_m;           // lambda = lam_m / 2^lam_sh exactly
+  int32_t lam_sh;
+  int32_t fill_mode;        // 0: fill up to the budget; 1: budget uniform picks
+  int64_t budget;           // round((1 - r) * candidates)
+  int32_t* idx;
+  int64_t idx_stride;
+  int32_t* count;
+  int32_t* count_r;         // may be null
+  uint64_t* mass;           // pooled: candidates x 8 bytes of scratch
+};
+hipError_t launch_select_topp(const ToppArgs& a, hipStream_t stream);
+
 // Compaction of a kept set (skv_gather).
 struct GatherArgs {
   const char* k;

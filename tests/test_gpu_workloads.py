@@ -169,6 +169,28 @@ def test_qwen_video_sparse_to_dense_round():
     for h in range(Hkv):
         _near_tie_ok(gi[h], gc[h], o_idx[h], o_cnt[h], s64[h], 0, m_v, K)
         assert gi[h, :gc[h]].max() < m_v
+    banner("qwen StD: SpecVLM top-P + uniform fill on the oracle's scores")
+    s32t = dev(s32)
+    vidx = torch.empty((Hkv, m_v), dtype=torch.int32, device="cuda")
+    vcnt = torch.empty(Hkv, dtype=torch.int32, device="cuda")
+    vcr = torch.empty(Hkv, dtype=torch.int32, device="cuda")
+    for pooled in (False, True):
+        skv.skv_select_topp(s32t, m, 0, m_t, 0.5, 0.9, vidx, vcnt, ws, count_r=vcr, pooled=pooled)
+        torch.cuda.synchronize()
+        t_idx, t_cnt, t_cr = oracle.select_topp(s32, 0, m_t, 0.5, 0.9, pooled=pooled, idx_stride=m_v)
+        vi, vc = host(vidx), host(vcnt)
+        assert np.array_equal(vc, t_cnt) and np.array_equal(host(vcr), t_cr)
+        assert all(np.array_equal(vi[h, :vc[h]], t_idx[h, :t_cnt[h]]) for h in range(Hkv))
+        budget = int(np.floor((1.0 - 0.9) * m_v + 0.5))  # r = 90 %: 10 % of the video tokens
+        assert np.array_equal(vc, np.maximum(t_cr, budget))
+    qt = dev(np.ascontiguousarray(w.extra["q_draft"][0]))
+    out = torch.empty((H, d), device="cuda")
+    lse = torch.empty(H, device="cuda")
+    skv.skv_attend_sparse(qt, kt, vt, m + 1, vidx, vcnt, m_v, out, lse, ws)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attend_sparse(np.ascontiguousarray(w.extra["q_draft"][0]), w.k, w.v, m + 1,
+                                  t_idx, t_cnt, m_v)
+    assert np.abs(host(out) - ro).max() <= ATOL and np.abs(host(lse) - rl).max() <= LSE_ATOL
     banner("qwen StD: 5 draft steps + verify")
     qd = w.extra["q_draft"]
     for t in range(gamma):
