@@ -24,7 +24,8 @@ dense steps at 2K-128K, the
 per-step top-K pipeline at 128K (score -> select -> gathered attention), the
 Sparse-to-Dense round of the Qwen2-7B video workload (5 sparse drafts + one
 gamma=5 verify), the SpecVLM selection on it (top-P 0.5 + uniform fill to
-10 % of the video tokens) and the round over that set, one-time selection costs, and the byte-count speedup bounds.
+10 % of the video tokens) and the round over that set, sweeps of the round
+over gamma = 1..13 and over K (measured vs I/O-model break-even acceptance), one-time selection costs, and the byte-count speedup bounds.
 `--sections all` adds the 1024-head SparseMM batched step (17 GB of cache).
 
 cpu_baseline: the fp64 oracle (test infrastructure) timed on this host on a
@@ -306,12 +307,16 @@ def main():
         m = m_v + m_t
         hq4, hkv4 = wq.n_q_heads, wq.n_kv_heads
         L4 = 12  # 12 x 52 MB of K+V: beyond the Infinity Cache
-        kv4 = [(dev(wq.k), dev(wq.v))] + [(dev(np.roll(wq.k, l, axis=1)), dev(np.roll(wq.v, l, axis=1)))
-                                          for l in range(1, L4)]
+        # room for up to 16 drafted entries (the gamma sweep below)
+        pad = synth.bf16_bits(np.random.default_rng(5).standard_normal(
+            (hkv4, m + 16 - wq.k.shape[1], d)).astype(np.float32))
+        k4h, v4h = np.concatenate([wq.k, pad], axis=1), np.concatenate([wq.v, pad], axis=1)
+        kv4 = [(dev(k4h), dev(v4h))] + [(dev(np.roll(k4h, l, axis=1)), dev(np.roll(v4h, l, axis=1)))
+                                        for l in range(1, L4)]
         qo4 = dev(wq.q_obs)
         qd4 = [dev(np.ascontiguousarray(wq.extra["q_draft"][t])) for t in range(gamma)]
         qv4 = dev(wq.extra["q_verify"])
-        ws4 = skv.Workspace.for_problem(skv.problem_for(qo4, kv4[0][0]), m + gamma, m_t)
+        ws4 = skv.Workspace.for_problem(skv.problem_for(qo4, kv4[0][0]), m + 16, m_t)
         sc4 = torch.empty((hkv4, m), device="cuda")
         idx4 = torch.empty((hkv4, wq.k_top), dtype=torch.int32, device="cuda")
         cnt4 = torch.empty(hkv4, dtype=torch.int32, device="cuda")
@@ -393,6 +398,47 @@ def main():
             "specvlm_round_5_drafts_plus_verify_us": round(rv_us, 2),
             "round_speedup_byte_bound_alpha1": round(dense_round_bytes / (draft_bytes + v_bytes), 3),
         }
+        # Sparse-to-Dense sweeps: draft length gamma (K fixed) and kept K
+        # (gamma = 5).  Per accepted token a round costs T_round / (alpha gamma)
+        # against T_dense for vanilla decoding, so the measured break-even
+        # acceptance is T_round / (gamma T_dense); the I/O model's is
+        # (K + m_t) / (m_v + m_t) + 1 / gamma.
+        log("Sparse-to-Dense sweeps over gamma and K")
+        dense1_us, _ = time_steps(lambda i: skv.skv_attend_dense(qd4[0], kv4[i % L4][0], kv4[i % L4][1],
+                                                                m + 1, o4, l4, ws4),
+                                  args.steps, args.warmup, 3)
+        rng4 = np.random.default_rng(7)
+        qv_all = dev(synth.bf16_bits(rng4.standard_normal((16, hq4, d)).astype(np.float32)))
+        ov16 = torch.empty((16, hq4, d), device="cuda")
+        lv16 = torch.empty((16, hq4), device="cuda")
+
+        def round_g(gam, kidx, kcnt):
+            def step(i):
+                k4, v4 = kv4[i % L4]
+                for t in range(gam):
+                    skv.skv_attend_sparse(qd4[t % gamma], k4, v4, m + t + 1, kidx, kcnt, m_v, o4, l4, ws4)
+                skv.skv_verify(qv_all[:gam], k4, v4, m + gam, ov16[:gam], lv16[:gam], ws4)
+            return step
+
+        def sweep_entry(gam, k_sel, kidx, kcnt):
+            us, _ = time_steps(round_g(gam, kidx, kcnt), 10, 2, 3)
+            vus, _ = time_steps(lambda i: skv.skv_verify(qv_all[:gam], kv4[i % L4][0], kv4[i % L4][1], m + gam,
+                                                         ov16[:gam], lv16[:gam], ws4), 20, 2, 3)
+            return {"round_us": round(us, 2), "verify_us": round(vus, 2),
+                    "alpha_break_even_measured": round(us / (gam * dense1_us), 3),
+                    "alpha_break_even_io_model": round(rf.std_break_even_alpha(gam, k_sel, m_t, m_v), 3)}
+
+        g_sweep = {str(g): sweep_entry(g, wq.k_top, idx4, cnt4) for g in range(1, 14)}
+        k_sweep = {}
+        for frac in (0.05, 0.1, 0.2, 0.3, 0.5):
+            kk = int(frac * m_v)
+            kidx = torch.empty((hkv4, kk), dtype=torch.int32, device="cuda")
+            kcnt = torch.empty(hkv4, dtype=torch.int32, device="cuda")
+            skv.skv_score(qo4, kv4[0][0], m, sc4, ws4)
+            skv.skv_select(sc4, m, 0, m_t, kk, kidx, kcnt, ws4)
+            k_sweep[str(kk)] = sweep_entry(gamma, kk, kidx, kcnt)
+        details["qwen_std_sweeps"] = {"dense_step_us": round(dense1_us, 3), "gamma": g_sweep,
+                                      "K_at_gamma5": k_sweep}
         del kv4
         torch.cuda.empty_cache()
 

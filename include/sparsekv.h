@@ -169,7 +169,9 @@ skv_status skv_attend_dense(const skv_problem* p, const void* q, const void* k,
  * one pass over the full cache).  The gamma new entries already occupy
  * positions n - gamma .. n - 1; query t (q [gamma][Hq][d]) sits at n - gamma + t
  * and sees keys [0, n - gamma + t].  out [gamma][Hq][d], lse [gamma][Hq] (may be
- * NULL).  Requires bf16 and 1 <= gamma <= min(n, 16). */
+ * NULL).  Requires bf16 and 1 <= gamma <= min(n, 16).  A kernel pass holds at
+ * most 64 query rows (gamma * G) per kv head; more run as successive passes of
+ * floor(64 / G) queries, each over the prefix its queries see. */
 skv_status skv_verify(const skv_problem* p, const void* q, int32_t gamma, const void* k,
                       const void* v, int64_t n, float* out, float* lse, void* ws,
                       size_t ws_bytes, void* stream);

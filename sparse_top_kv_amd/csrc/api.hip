@@ -195,10 +195,31 @@ ChunkPlan verify_plan(const skv_problem* p, int64_t n, int32_t gamma) {
   return plan_chunks(n, p->n_kv_heads, skv::attend_mfma_granule(rows, p->head_dim), 1 << 20);
 }
 
-size_t verify_scratch(const skv_problem* p, int64_t n, int32_t gamma) {
-  const ChunkPlan cp = verify_plan(p, n, gamma);
+// Verify queries per pass: one pass of the matrix-core kernel holds at most
+// attend_mfma_max_rows() query rows per kv head.
+int32_t verify_pass_queries(const skv_problem* p, int32_t gamma) {
+  const int qc = skv::attend_mfma_max_rows() / (p->n_q_heads / p->n_kv_heads);
+  return gamma < qc ? gamma : qc;
+}
+
+// Scratch of one verify pass of g queries over a cache of n entries.
+size_t verify_pass_scratch(const skv_problem* p, int64_t n, int32_t g) {
+  const ChunkPlan cp = verify_plan(p, n, g);
   const int G = p->n_q_heads / p->n_kv_heads;
-  return part_layout(p, cp.cph, gamma * G).end - SKV_WS_HEADER_BYTES;
+  return part_layout(p, cp.cph, g * G).end - SKV_WS_HEADER_BYTES;
+}
+
+// Scratch of a whole verify call: its passes run one after another on one
+// workspace, so the largest pass decides.
+size_t verify_scratch(const skv_problem* p, int64_t n, int32_t gamma) {
+  const int32_t qc = verify_pass_queries(p, gamma);
+  size_t s = 0;
+  for (int32_t t0 = 0; t0 < gamma; t0 += qc) {
+    const int32_t g = gamma - t0 < qc ? gamma - t0 : qc;
+    const size_t t = verify_pass_scratch(p, n - gamma + t0 + g, g);
+    s = s > t ? s : t;
+  }
+  return s;
 }
 
 // Pooled top-P selection: one 64-bit fixed-point mass per candidate.
@@ -237,8 +258,10 @@ size_t skv_workspace_size(const skv_problem* p, int64_t n_max, int32_t rows_max)
     t = score_obs_scratch(p, n_max, w);
     s = s > t ? s : t;
     const int32_t g = w < kVerifyMaxGamma ? w : kVerifyMaxGamma;
-    t = verify_scratch(p, n_max, g);
-    s = s > t ? s : t;
+    for (int32_t gg = 1; gg <= g; ++gg) {  // every gamma up to the bound
+      t = verify_scratch(p, n_max, gg);
+      s = s > t ? s : t;
+    }
   }
   return SKV_WS_HEADER_BYTES + s;
 }
@@ -465,33 +488,45 @@ skv_status skv_verify(const skv_problem* p, const void* q, int32_t gamma, const 
       !aligned16(out))
     return SKV_ERR_INVALID_ARG;
   const int G = p->n_q_heads / p->n_kv_heads;
-  if (gamma * G > skv::attend_mfma_max_rows()) return SKV_ERR_UNSUPPORTED;
   if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
   if ((st = check_cache(p, k, n)) != SKV_OK || (st = check_cache(p, v, n)) != SKV_OK) return st;
-  const ChunkPlan cp = verify_plan(p, n, gamma);
   if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + verify_scratch(p, n, gamma))) != SKV_OK)
     return st;
+  // Passes of at most qc queries: pass [t0, t0 + g) holds queries at positions
+  // n - gamma + t0 .. n - gamma + t0 + g - 1, i.e. a verify of g queries over
+  // the prefix of n - gamma + t0 + g entries (later entries are masked for it).
+  const int32_t qc = verify_pass_queries(p, gamma);
+  const size_t qrow = (size_t)p->n_q_heads * p->head_dim;
   char* base = (char*)ws;
-  const PartLayout L = part_layout(p, cp.cph, gamma * G);
-  skv::AttendArgs a{};
-  a.q = q;
-  a.k = (const char*)k;
-  a.v = (const char*)v;
-  a.head_stride_b = p->kv_head_stride * 2;
-  a.pos_stride_b = p->kv_pos_stride * 2;
-  a.n = n;
-  a.n_kv_heads = p->n_kv_heads;
-  a.chunk = cp.chunk;
-  a.chunks_per_head = cp.cph;
-  a.scale_log2 = scale_log2(p);
-  a.part_ml = (float*)(base + L.ml);
-  a.part_acc = (float*)(base + L.acc);
-  a.nch = (int32_t*)(base + L.nch);
-  a.group = G;
-  a.n_pos = gamma;
-  if ((st = hip_status(skv::launch_attend_mfma(p->head_dim, false, true, a, (hipStream_t)stream))) != SKV_OK)
-    return st;
-  return launch_partials_merge(p, base, L, cp.cph, gamma * G, false, out, lse, (hipStream_t)stream);
+  for (int32_t t0 = 0; t0 < gamma; t0 += qc) {
+    const int32_t g = gamma - t0 < qc ? gamma - t0 : qc;
+    const int64_t np = n - gamma + t0 + g;
+    const ChunkPlan cp = verify_plan(p, np, g);
+    const PartLayout L = part_layout(p, cp.cph, g * G);
+    skv::AttendArgs a{};
+    a.q = (const char*)q + (size_t)t0 * qrow * 2;
+    a.k = (const char*)k;
+    a.v = (const char*)v;
+    a.head_stride_b = p->kv_head_stride * 2;
+    a.pos_stride_b = p->kv_pos_stride * 2;
+    a.n = np;
+    a.n_kv_heads = p->n_kv_heads;
+    a.chunk = cp.chunk;
+    a.chunks_per_head = cp.cph;
+    a.scale_log2 = scale_log2(p);
+    a.part_ml = (float*)(base + L.ml);
+    a.part_acc = (float*)(base + L.acc);
+    a.nch = (int32_t*)(base + L.nch);
+    a.group = G;
+    a.n_pos = g;
+    if ((st = hip_status(skv::launch_attend_mfma(p->head_dim, false, true, a, (hipStream_t)stream))) != SKV_OK)
+      return st;
+    if ((st = launch_partials_merge(p, base, L, cp.cph, g * G, false, out + (size_t)t0 * qrow,
+                                    lse ? lse + (size_t)t0 * p->n_q_heads : nullptr,
+                                    (hipStream_t)stream)) != SKV_OK)
+      return st;
+  }
+  return SKV_OK;
 }
 
 skv_status skv_gather(const skv_problem* p, const void* k, const void* v, int64_t n,

@@ -84,12 +84,18 @@ def test_sparse_select_score_verify_validation():
                          _vp(0)) == skv.SKV_ERR_UNSUPPORTED
     assert lib.skv_verify(ctypes.byref(pf), _vp(FAKE), 4, _vp(FAKE), _vp(FAKE), 100, _vp(FAKE), _vp(0),
                           _vp(FAKE), big, _vp(0)) == skv.SKV_ERR_UNSUPPORTED
-    # gamma > n, and more than 64 verify rows per kv head
+    # gamma > n, gamma above 16
     assert lib.skv_verify(b, _vp(FAKE), 8, _vp(FAKE), _vp(FAKE), 5, _vp(FAKE), _vp(0), _vp(FAKE), big,
                           _vp(0)) == skv.SKV_ERR_INVALID_ARG
+    assert lib.skv_verify(b, _vp(FAKE), 17, _vp(FAKE), _vp(FAKE), 100, _vp(FAKE), _vp(0), _vp(FAKE), big,
+                          _vp(0)) == skv.SKV_ERR_INVALID_ARG
+    # more than 64 rows per kv head run in passes; the workspace covers every gamma
     p7 = _p(hq=56, hkv=8)
-    assert lib.skv_verify(ctypes.byref(p7), _vp(FAKE), 10, _vp(FAKE), _vp(FAKE), 100, _vp(FAKE), _vp(0),
-                          _vp(FAKE), big, _vp(0)) == skv.SKV_ERR_UNSUPPORTED
+    need = skv.skv_workspace_size(p7, 100, 16)
+    for g in (9, 10, 13, 16):
+        assert lib.skv_verify(ctypes.byref(p7), _vp(FAKE), g, _vp(FAKE), _vp(FAKE), 100, _vp(FAKE), _vp(0),
+                              _vp(FAKE), 1024, _vp(0)) == skv.SKV_ERR_WORKSPACE
+    assert need > skv.SKV_WS_HEADER_BYTES
 
 
 def test_workspace_size_is_monotone_and_zero_for_bad_problems():
