@@ -18,7 +18,9 @@ roofline figure divides the algorithmic bytes by the whole step time, so the
 merge counts against it.  Eager (one host launch per call) times are reported
 beside the graph times.
 
-Also reported in `details` (default sections): compaction of the 32K kept
+Also reported in `details` (default sections): the 30 % sink-plus-recent
+window against dense decoding through masked, fused and split-K attention
+(2K-128K; the masked and fused paths are PyTorch baselines), compaction of the 32K kept
 sets into contiguous caches (gather once, then the dense step over them),
 dense steps at 2K-128K, the
 per-step top-K pipeline at 128K (score -> select -> gathered attention), the
@@ -125,6 +127,75 @@ def main():
             per.append(e0.elapsed_time(e1) * 1000.0 / nsteps)
         per.sort()
         return per[len(per) // 2], per
+
+    def attention_baselines(big, hq, hkv, d, out, lse):
+        """The same 30 % sink-plus-recent window against dense decoding when
+        both read the cache through masked (eager ops with an explicit mask),
+        fused (one attention kernel, no split over the sequence) or split-K
+        attention ("Where Activation Sparsity and KV-Cache Sparsity Cross",
+        "The Attention Baseline").  The masked and fused paths are PyTorch's
+        own (matmul + softmax, and SDPA's flash kernel); they are baselines
+        only.  Returns speedups, each path's HBM fraction and the byte bounds."""
+        import torch.nn.functional as F
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        G = hq // hkv
+        scale = 1.0 / math.sqrt(d)
+        res = {}
+        for nn in (2048, 8192, 32768, 131072):
+            w = int(round(0.3 * nn))
+            recent = w - 4
+            # window caches as a sink cache would hold them (contiguous)
+            win = [(torch.cat([b["k"][:, :4], b["k"][:, nn - recent:nn]], 1).contiguous(),
+                    torch.cat([b["v"][:, :4], b["v"][:, nn - recent:nn]], 1).contiguous()) for b in big]
+            mask = {L: torch.zeros((L, 1), device="cuda") for L in (nn, w)}
+            sink_idx = torch.arange(4, dtype=torch.int32, device="cuda").repeat(hkv, 1).contiguous()
+            sink_cnt = torch.full((hkv,), 4, dtype=torch.int32, device="cuda")
+
+            def masked(q, k, v, L):
+                qg = q.view(hkv, G, d).transpose(1, 2).contiguous()          # [Hkv][d][G]
+                lg = torch.matmul(k[:, :L], qg).float() * scale + mask[L]    # [Hkv][L][G]
+                pr = torch.softmax(lg, dim=1).to(q.dtype).transpose(1, 2).contiguous()
+                return torch.matmul(pr, v[:, :L])                            # [Hkv][G][d]
+
+            def fused(q, k, v, L):
+                with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                    return F.scaled_dot_product_attention(q.view(1, hkv, G, d), k[None, :, :L],
+                                                          v[None, :, :L], scale=scale)
+
+            paths = {
+                "masked": (lambda i: masked(big[i % 2]["q"], big[i % 2]["k"], big[i % 2]["v"], nn),
+                           lambda i: masked(big[i % 2]["q"], win[i % 2][0], win[i % 2][1], w), False),
+                "fused": (lambda i: fused(big[i % 2]["q"], big[i % 2]["k"], big[i % 2]["v"], nn),
+                          lambda i: fused(big[i % 2]["q"], win[i % 2][0], win[i % 2][1], w), False),
+                "split_k": (lambda i: skv.skv_attend_dense(big[i % 2]["q"], big[i % 2]["k"], big[i % 2]["v"],
+                                                           nn, out, lse, ws),
+                            lambda i: skv.skv_attend_sparse(big[i % 2]["q"], big[i % 2]["k"], big[i % 2]["v"],
+                                                            nn, sink_idx, sink_cnt, nn - recent, out, lse,
+                                                            ws), True),
+            }
+            by_d = rf.dense_step_bytes(hq, hkv, d, nn, "bf16")
+            by_w = rf.dense_step_bytes(hq, hkv, d, w, "bf16")
+            layer = 2 * rf.projection_params(4096, 14336) + rf.kv_bytes_per_layer(nn)
+            entry = {"window": w, "byte_bound_attention": round(by_d / by_w, 3),
+                     "byte_bound_layer_with_projections": round(
+                         rf.speedup_bound(layer, rf.kv_bytes_per_layer(nn) - rf.kv_bytes_per_layer(w)), 3)}
+            for name, (dstep, wstep, graph) in paths.items():
+                try:
+                    nst = 20 if nn < 131072 else 10
+                    td, _ = time_steps(dstep, nst, 3, 3, graph=graph)
+                    tw, _ = time_steps(wstep, nst, 3, 3, graph=graph)
+                    entry[name] = {"dense_us": round(td, 2), "window_us": round(tw, 2),
+                                   "speedup": round(td / tw, 3),
+                                   "dense_hbm_frac": round(rf.roofline_fraction(by_d, td * 1e-6), 4)}
+                    if graph:
+                        te, _ = time_steps(dstep, nst, 3, 1, graph=False)
+                        tew, _ = time_steps(wstep, nst, 3, 1, graph=False)
+                        entry[name]["eager_speedup"] = round(te / tew, 3)
+                except RuntimeError as e:  # e.g. no flash kernel for this shape
+                    entry[name] = {"error": str(e).splitlines()[0][:160]}
+            res[str(nn)] = entry
+            del win
+        return res
 
     # ------------------------------------------------------------------
     # headline: Llama-3.1-8B shape, 32K, 30 % kept via window score once
@@ -278,6 +349,7 @@ def main():
             by = rf.dense_step_bytes(hq, hkv, d, nn, "bf16")
             sweep[str(nn)] = {"us": round(us, 3), "hbm_frac": round(rf.roofline_fraction(by, us * 1e-6), 4)}
         details["dense_sweep"] = sweep
+        details["attention_baselines"] = attention_baselines(big, hq, hkv, d, out, lse)
         score3 = torch.empty((hkv, n3), device="cuda")
         idx3 = torch.empty((hkv, S + K3), dtype=torch.int32, device="cuda")
         cnt3 = torch.empty(hkv, dtype=torch.int32, device="cuda")
