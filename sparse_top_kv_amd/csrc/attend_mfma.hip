@@ -44,7 +44,7 @@
 namespace skv {
 namespace {
 
-constexpr int kSparseMaxChunk = 512;      // rows per workgroup (LDS offset list)
+constexpr int kSparseMaxChunk = 2048;     // rows per workgroup (LDS offset list)
 constexpr float kSlack = 30.0f;
 
 // W waves of 64 lanes, S-tile ring per wave, NG groups of 16 query rows.
@@ -91,6 +91,7 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
     if (a.count_max > 0) {  // uniform: idx may be null when no entry is usable
 #pragma unroll
       for (int k = 0; k < kSpec; ++k) {
+        if (k * kT >= a.chunk) break;  // uniform
         const int64_t r = rs0 + tid + k * kT;
         spec[k] = ih[r < a.count_max ? r : a.count_max - 1];
       }
@@ -153,6 +154,7 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
 #pragma unroll
     for (int k = 0; k < kSpec; ++k) {
       const int i = tid + k * kT;
+      if (k * kT >= a.chunk) break;  // uniform
       if (i < kSparseMaxChunk) {
         const int64_t r = r0 + i;
         int32_t p = 0;
