@@ -113,23 +113,25 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
 // ---------------------------------------------------------------------------
 // Block-parallel path for long caches with few kv heads (a one-workgroup-per-
 // head select would leave most CUs idle).  Candidates are cut into blocks of
-// kBlk; five short kernels, no global atomics, so the result is identical run
-// to run:
+// kBlk; three kernels, no global atomics, so the result is identical run to
+// run.  The per-head steps between them are recomputed by every block of the
+// head from the same data (cheaper than a one-workgroup-per-head launch):
 //   1 per block: histogram of key bits [31:21]
-//   2 per head : the bin d1 holding the K-th key, how many to take from it,
-//                where each block's bin members go; sinks and count
-//   3 per block: copy bin members (key, index) in index order; count keys
-//                above the bin
-//   4 per head : finish the radix select on the bin members (bits [20:10],
-//                [9:0]) -> threshold key T, tie cutoff index jT; output
-//                offset of every block
-//   5 per block: write kept indices (key > T, or key == T and index <= jT)
+//   2 per block: from all block histograms of its head, the bin d1 holding the
+//                K-th key and how many to take from it, and where this block's
+//                bin members go; copy them (key, index) in index order and
+//                count the keys above the bin.  Block 0 records the head's
+//                state, the sinks and the count.
+//   3 per block: finish the radix select on the head's bin members (bits
+//                [20:10], [9:0]) -> threshold key T and how many keys equal to
+//                T are kept, lowest index first; this block's output offset;
+//                write its kept indices
 // ---------------------------------------------------------------------------
 constexpr int kBlk = 4096;                 // candidates per block
 constexpr int kStageCand = 8192;           // threshold-bin members staged in LDS
 constexpr int kBlkPer = kBlk / kSelThreads;
 
-struct SelGeom {  // per-head geometry shared by the five kernels
+struct SelGeom {  // per-head geometry shared by the three kernels
   int64_t c_lo, c_hi, ncand, nsink, K;
   int nb;         // blocks of this head
 };
@@ -154,9 +156,7 @@ __device__ __forceinline__ SelGeom sel_geom(const SelectArgs& a, int h) {
 struct SelWs {
   uint32_t* hist;    // [Hkv][nbm][2048]
   uint32_t* above;   // [Hkv][nbm]
-  uint32_t* binoff;  // [Hkv][nbm]
-  uint32_t* outoff;  // [Hkv][nbm]
-  uint32_t* head;    // [Hkv][8]: mode, d1, krem, cbin, T, jT
+  uint32_t* head;    // [Hkv][8]: mode, d1, krem, cbin
   uint32_t* ckey;    // [Hkv][n]
   int32_t* cidx;     // [Hkv][n]
   int nbm;
@@ -175,8 +175,6 @@ __host__ __device__ inline SelWs sel_ws(void* ws, int hkv, int64_t n) {
   };
   w.hist = (uint32_t*)take((size_t)hkv * w.nbm * 2048 * 4);
   w.above = (uint32_t*)take((size_t)hkv * w.nbm * 4);
-  w.binoff = (uint32_t*)take((size_t)hkv * w.nbm * 4);
-  w.outoff = (uint32_t*)take((size_t)hkv * w.nbm * 4);
   w.head = (uint32_t*)take((size_t)hkv * 8 * 4);
   w.ckey = (uint32_t*)take((size_t)hkv * n * 4);
   w.cidx = (int32_t*)take((size_t)hkv * n * 4);
@@ -207,93 +205,78 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist1_kernel(const SelectArgs
   for (int i = tid; i < kBins; i += kSelThreads) out[i] = hist[i];
 }
 
-__global__ __launch_bounds__(kSelThreads) void sel_pick1_kernel(const SelectArgs a) {
-  __shared__ uint32_t sm_w[kSelWaves + 1];
-  __shared__ uint32_t sm_digit, sm_krem;
-  const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
-  const int h = blockIdx.x, tid = threadIdx.x;
-  const SelGeom g = sel_geom(a, h);
-  int32_t* out = a.idx + (int64_t)h * a.idx_stride;
-  for (int64_t i = tid; i < g.nsink; i += kSelThreads) out[i] = (int32_t)i;
-  if (tid == 0) a.count[h] = (int32_t)(g.nsink + g.K);
-  uint32_t* hd = w.head + (int64_t)h * 8;
-  uint32_t* outoff = w.outoff + (int64_t)h * w.nbm;
-  if (g.K == 0 || g.K == g.ncand) {  // nothing or everything: no radix passes
-    if (tid == 0) {
-      hd[0] = g.K == 0 ? kModeNone : kModeAll;
-      hd[4] = g.K == 0 ? 0xFFFFFFFFu : 0u;
-      hd[5] = g.K == 0 ? 0xFFFFFFFFu : 0x7FFFFFFFu;
-    }
-    for (int b = tid; b < g.nb; b += kSelThreads) outoff[b] = (uint32_t)(g.nsink + (int64_t)b * kBlk);
-    return;
-  }
-  const uint32_t* hist = w.hist + (int64_t)h * w.nbm * kBins;
-  const int top = kBins - 1 - tid * 2;  // this thread's bins: top, top-1 (visited from the top)
-  uint32_t c0 = 0, c1 = 0;
-  // bins top - 1 and top are adjacent: one 8-byte load per block, eight
-  // blocks in flight per round
-  const uint2* hp = reinterpret_cast<const uint2*>(hist + top - 1);
-  int b = 0;
-  for (; b + 8 <= g.nb; b += 8) {
-    uint2 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = hp[(int64_t)(b + u) * (kBins / 2)];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      c0 += v[u].y;
-      c1 += v[u].x;
-    }
-  }
-  for (; b < g.nb; ++b) {
-    const uint2 v = hp[(int64_t)b * (kBins / 2)];
-    c0 += v.y;
-    c1 += v.x;
-  }
-  uint32_t total;
-  const uint32_t krem = (uint32_t)g.K;
-  const uint32_t above = block_excl_scan(c0 + c1, sm_w, &total);
-  if (above < krem && krem <= above + c0 + c1) {
-    if (krem <= above + c0) {
-      sm_digit = (uint32_t)top;
-      sm_krem = krem - above;
-    } else {
-      sm_digit = (uint32_t)(top - 1);
-      sm_krem = krem - above - c0;
-    }
-  }
-  __syncthreads();
-  const uint32_t d1 = sm_digit;
-  // members of bin d1 per block, and where each block's members start
-  uint32_t mine = 0;
-  if (tid < g.nb) mine = hist[(int64_t)tid * kBins + d1];
-  uint32_t cbin;
-  const uint32_t off = block_excl_scan(mine, sm_w, &cbin);
-  if (tid < g.nb) w.binoff[(int64_t)h * w.nbm + tid] = off;
-  if (tid == 0) {
-    hd[0] = kModeRadix;
-    hd[1] = d1;
-    hd[2] = sm_krem;
-    hd[3] = cbin;
-  }
-}
-
 __global__ __launch_bounds__(kSelThreads) void sel_collect_kernel(const SelectArgs a) {
   __shared__ uint32_t sm_w[kSelWaves + 1];
+  __shared__ uint32_t sm_digit, sm_krem, sm_base;
   const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
   const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
   const SelGeom g = sel_geom(a, h);
   if (b >= g.nb) return;
   const float* s = a.score + (int64_t)h * a.score_stride;
   const int tid = threadIdx.x;
-  // every load of the kernel in one round: scores, head state, block offset
   const int64_t j0 = g.c_lo + (int64_t)b * kBlk + kBlkPer * tid;
   float sv[kBlkPer];
 #pragma unroll
   for (int u = 0; u < kBlkPer; ++u) sv[u] = j0 + u < g.c_hi ? s[j0 + u] : 0.0f;
-  const uint32_t* hd = w.head + (int64_t)h * 8;
-  const uint32_t mode = hd[0], d1 = hd[1];
-  const uint32_t base = w.binoff[(int64_t)h * w.nbm + b];
-  if (mode != kModeRadix) return;  // uniform
+  uint32_t* hd = w.head + (int64_t)h * 8;
+  if (b == 0) {
+    int32_t* out = a.idx + (int64_t)h * a.idx_stride;
+    for (int64_t i = tid; i < g.nsink; i += kSelThreads) out[i] = (int32_t)i;
+    if (tid == 0) a.count[h] = (int32_t)(g.nsink + g.K);
+  }
+  if (g.K == 0 || g.K == g.ncand) {  // nothing or everything: no radix passes
+    if (b == 0 && tid == 0) hd[0] = g.K == 0 ? kModeNone : kModeAll;
+    return;
+  }
+  // the top-11-bit bin of the K-th key, summed over the head's blocks
+  const uint32_t* hist = w.hist + (int64_t)h * w.nbm * kBins;
+  const int top = kBins - 1 - tid * 2;  // this thread's bins: top, top-1 (visited from the top)
+  uint32_t c0 = 0, c1 = 0;
+  // bins top - 1 and top are adjacent: one 8-byte load per block, eight
+  // blocks in flight per round
+  const uint2* hp = reinterpret_cast<const uint2*>(hist + top - 1);
+  int bb = 0;
+  for (; bb + 8 <= g.nb; bb += 8) {
+    uint2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = hp[(int64_t)(bb + u) * (kBins / 2)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      c0 += v[u].y;
+      c1 += v[u].x;
+    }
+  }
+  for (; bb < g.nb; ++bb) {
+    const uint2 v = hp[(int64_t)bb * (kBins / 2)];
+    c0 += v.y;
+    c1 += v.x;
+  }
+  uint32_t total;
+  const uint32_t krem = (uint32_t)g.K;
+  const uint32_t above_bins = block_excl_scan(c0 + c1, sm_w, &total);
+  if (above_bins < krem && krem <= above_bins + c0 + c1) {
+    if (krem <= above_bins + c0) {
+      sm_digit = (uint32_t)top;
+      sm_krem = krem - above_bins;
+    } else {
+      sm_digit = (uint32_t)(top - 1);
+      sm_krem = krem - above_bins - c0;
+    }
+  }
+  __syncthreads();
+  const uint32_t d1 = sm_digit;
+  // members of bin d1 in the blocks before this one
+  const uint32_t mine = tid < g.nb ? hist[(int64_t)tid * kBins + d1] : 0u;
+  uint32_t cbin;
+  const uint32_t off = block_excl_scan(mine, sm_w, &cbin);
+  if (tid == b) sm_base = off;
+  if (b == 0 && tid == 0) {
+    hd[0] = kModeRadix;
+    hd[1] = d1;
+    hd[2] = sm_krem;
+    hd[3] = cbin;
+  }
+  __syncthreads();
   // candidates in the threshold bin (kept in index order) and above it
   uint32_t key[kBlkPer], n_in = 0, n_ab = 0;
 #pragma unroll
@@ -305,7 +288,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect_kernel(const SelectAr
   }
   uint32_t tot;  // counts <= kBlk < 2^16: both in one scan
   const uint32_t ex = block_excl_scan((n_in << 16) | n_ab, sm_w, &tot);
-  uint32_t r = base + (ex >> 16);
+  uint32_t r = sm_base + (ex >> 16);
   uint32_t* ck = w.ckey + (int64_t)h * a.n;
   int32_t* ci = w.cidx + (int64_t)h * a.n;
 #pragma unroll
@@ -319,23 +302,31 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect_kernel(const SelectAr
   if (tid == 0) w.above[(int64_t)h * w.nbm + b] = tot & 0xFFFFu;
 }
 
-__global__ __launch_bounds__(kSelThreads) void sel_pick2_kernel(const SelectArgs a) {
+__global__ __launch_bounds__(kSelThreads) void sel_write_kernel(const SelectArgs a) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t sm_w[kSelWaves + 1];
-  __shared__ uint32_t sm_digit, sm_krem, sm_jt;
-  __shared__ uint32_t sm_kept[1024];
-  // bin members staged in LDS when they fit (the usual case): the three
-  // passes below then read LDS instead of global memory
+  __shared__ uint32_t sm_digit, sm_krem, sm_jt, sm_base;
+  __shared__ uint32_t sm_kept[kSelThreads];
+  // bin members staged in LDS when they fit (the usual case): the passes
+  // below then read LDS instead of global memory
   __shared__ uint32_t sm_ck[kStageCand];
   __shared__ int32_t sm_ci[kStageCand];
   const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
-  const int h = blockIdx.x, tid = threadIdx.x;
+  const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
   const SelGeom g = sel_geom(a, h);
-  uint32_t* hd = w.head + (int64_t)h * 8;
+  if (b >= g.nb) return;
+  const int tid = threadIdx.x;
+  const uint32_t* hd = w.head + (int64_t)h * 8;
   const uint32_t* ck = w.ckey + (int64_t)h * a.n;
   const int32_t* ci = w.cidx + (int64_t)h * a.n;
-  // every independent load in one round: head state, the blocks' counts
-  // above the bin, and (speculatively) the first kStageCand bin members
+  // every independent load in one round: this block's scores, head state, the
+  // blocks' counts above the bin, and (speculatively) the first kStageCand
+  // bin members
+  const float* s = a.score + (int64_t)h * a.score_stride;
+  const int64_t j0 = g.c_lo + (int64_t)b * kBlk + kBlkPer * tid;
+  float sv[kBlkPer];
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u) sv[u] = j0 + u < g.c_hi ? s[j0 + u] : 0.0f;
   constexpr int kPre = kStageCand / kSelThreads;
   uint32_t pk[kPre];
   int32_t pi[kPre];
@@ -345,128 +336,115 @@ __global__ __launch_bounds__(kSelThreads) void sel_pick2_kernel(const SelectArgs
     pi[u] = ci[tid * kPre + u];
   }
   const uint32_t abv = tid < g.nb ? w.above[(int64_t)h * w.nbm + tid] : 0u;
-  const uint32_t mode = hd[0], d1h = hd[1], krem0 = hd[2], C = hd[3];
-  if (mode != kModeRadix) return;  // uniform
-  const bool staged = C <= (uint32_t)kStageCand;
-  if (staged) {
-#pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-      sm_ck[tid * kPre + u] = pk[u];
-      sm_ci[tid * kPre + u] = pi[u];
-    }
-    __syncthreads();
-    ck = sm_ck;
-    ci = sm_ci;
-  }
-  uint32_t prefix = d1h << 21, mask = 0xFFE00000u;
-  uint32_t krem = krem0;
-#pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = pass == 0 ? 10 : 0;
-    const int nb = pass == 0 ? 2048 : 1024;
-    for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0u;
-    __syncthreads();
-    for (uint32_t i = tid; i < C; i += kSelThreads) {
-      const uint32_t key = ck[i];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
-    }
-    __syncthreads();
-    const int per = nb / kSelThreads;
-    const int top = nb - 1 - tid * per;
-    uint32_t mine = 0;
-    for (int i = 0; i < per; ++i) mine += hist[top - i];
-    uint32_t total;
-    uint32_t above = block_excl_scan(mine, sm_w, &total);
-    if (above < krem && krem <= above + mine) {
-      for (int i = 0; i < per; ++i) {
-        const uint32_t cb = hist[top - i];
-        if (krem <= above + cb) {
-          sm_digit = (uint32_t)(top - i);
-          sm_krem = krem - above;
-          break;
-        }
-        above += cb;
-      }
-    }
-    __syncthreads();
-    prefix |= sm_digit << shift;
-    mask |= (uint32_t)(nb - 1) << shift;
-    krem = sm_krem;
-    __syncthreads();
-  }
-  const uint32_t T = prefix, take = krem;
-  // bin members in index order: the first `take` equal to T are kept
-  for (int b = tid; b < 1024; b += kSelThreads) sm_kept[b] = 0u;
-  if (tid == 0) sm_jt = 0xFFFFFFFFu;
-  __syncthreads();
-  auto keep_member = [&](uint32_t i, uint32_t key, uint32_t eq_rank) {
-    const bool eq = key == T;
-    if (key > T || (eq && eq_rank < take)) {
-      const int32_t j = ci[i];
-      atomicAdd(&sm_kept[(j - g.c_lo) / kBlk], 1u);
-      if (eq && eq_rank == take - 1) sm_jt = (uint32_t)j;
-    }
-  };
-  if (staged) {
-    // kPre consecutive members per thread: one scan ranks the equal keys
-    const uint32_t i0 = (uint32_t)tid * kPre;
-    uint32_t n_eq = 0;
-#pragma unroll
-    for (int u = 0; u < kPre; ++u) n_eq += (i0 + u < C && ck[i0 + u] == T) ? 1u : 0u;
-    uint32_t tot_eq;
-    uint32_t eq_rank = block_excl_scan(n_eq, sm_w, &tot_eq);
-#pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-      const uint32_t i = i0 + u;
-      if (i < C) {
-        const uint32_t key = ck[i];
-        keep_member(i, key, eq_rank);
-        eq_rank += key == T ? 1u : 0u;
-      }
-    }
-  } else {
-    uint32_t eq_seen = 0;
-#pragma unroll 1
-    for (uint32_t t0 = 0; t0 < C; t0 += kSelThreads) {
-      const uint32_t i = t0 + tid;
-      const bool valid = i < C;
-      const uint32_t key = valid ? ck[i] : 0u;
-      uint32_t n_eq;
-      const uint32_t eq_rank = eq_seen + block_flag_rank(valid && key == T, sm_w, &n_eq);
-      if (valid) keep_member(i, key, eq_rank);
-      eq_seen += n_eq;
-    }
-  }
-  __syncthreads();
-  // output offset of each block: sinks, then blocks in order
-  uint32_t mine = 0;
-  if (tid < g.nb) mine = abv + sm_kept[tid];
-  uint32_t total;
-  const uint32_t off = block_excl_scan(mine, sm_w, &total);
-  if (tid < g.nb) w.outoff[(int64_t)h * w.nbm + tid] = (uint32_t)g.nsink + off;
-  if (tid == 0) {
-    hd[4] = T;
-    hd[5] = take == 0 ? 0xFFFFFFFFu : sm_jt;  // 0xFFFFFFFF: no equal key kept
-  }
-}
-
-__global__ __launch_bounds__(kSelThreads) void sel_write_kernel(const SelectArgs a) {
-  __shared__ uint32_t sm_w[kSelWaves + 1];
-  const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
-  const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
-  const SelGeom g = sel_geom(a, h);
-  if (b >= g.nb) return;
-  const float* s = a.score + (int64_t)h * a.score_stride;
-  const int tid = threadIdx.x;
-  const int64_t j0 = g.c_lo + (int64_t)b * kBlk + kBlkPer * tid;
-  float sv[kBlkPer];
-#pragma unroll
-  for (int u = 0; u < kBlkPer; ++u) sv[u] = j0 + u < g.c_hi ? s[j0 + u] : 0.0f;
-  const uint32_t* hd = w.head + (int64_t)h * 8;
-  const uint32_t mode = hd[0], T = hd[4], jtw = hd[5];
-  const uint32_t base = w.outoff[(int64_t)h * w.nbm + b];
+  const uint32_t mode = hd[0];
   if (mode == kModeNone) return;  // uniform
-  const int64_t jt = jtw == 0xFFFFFFFFu ? -1 : (mode == kModeAll ? INT64_MAX : (int64_t)jtw);
+  uint32_t T = 0;
+  int64_t jt = INT64_MAX;  // every key >= T kept (mode all)
+  uint32_t base = (uint32_t)(g.nsink + (int64_t)b * kBlk);
+  if (mode == kModeRadix) {
+    const uint32_t d1h = hd[1], krem0 = hd[2], C = hd[3];
+    const bool staged = C <= (uint32_t)kStageCand;
+    if (staged) {
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) {
+        sm_ck[tid * kPre + u] = pk[u];
+        sm_ci[tid * kPre + u] = pi[u];
+      }
+      __syncthreads();
+      ck = sm_ck;
+      ci = sm_ci;
+    }
+    uint32_t prefix = d1h << 21, mask = 0xFFE00000u;
+    uint32_t krem = krem0;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 10 : 0;
+      const int nb = pass == 0 ? 2048 : 1024;
+      for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0u;
+      __syncthreads();
+      for (uint32_t i = tid; i < C; i += kSelThreads) {
+        const uint32_t key = ck[i];
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
+      __syncthreads();
+      const int per = nb / kSelThreads;
+      const int top = nb - 1 - tid * per;
+      uint32_t mine = 0;
+      for (int i = 0; i < per; ++i) mine += hist[top - i];
+      uint32_t total;
+      uint32_t above = block_excl_scan(mine, sm_w, &total);
+      if (above < krem && krem <= above + mine) {
+        for (int i = 0; i < per; ++i) {
+          const uint32_t cb = hist[top - i];
+          if (krem <= above + cb) {
+            sm_digit = (uint32_t)(top - i);
+            sm_krem = krem - above;
+            break;
+          }
+          above += cb;
+        }
+      }
+      __syncthreads();
+      prefix |= sm_digit << shift;
+      mask |= (uint32_t)(nb - 1) << shift;
+      krem = sm_krem;
+      __syncthreads();
+    }
+    T = prefix;
+    const uint32_t take = krem;
+    // bin members in index order: the first `take` equal to T are kept;
+    // count the kept members of every block
+    sm_kept[tid] = 0u;
+    if (tid == 0) sm_jt = 0xFFFFFFFFu;
+    __syncthreads();
+    auto keep_member = [&](uint32_t i, uint32_t key, uint32_t eq_rank) {
+      const bool eq = key == T;
+      if (key > T || (eq && eq_rank < take)) {
+        const int32_t j = ci[i];
+        atomicAdd(&sm_kept[(j - g.c_lo) / kBlk], 1u);
+        if (eq && eq_rank == take - 1) sm_jt = (uint32_t)j;
+      }
+    };
+    if (staged) {
+      // kPre consecutive members per thread: one scan ranks the equal keys
+      const uint32_t i0 = (uint32_t)tid * kPre;
+      uint32_t n_eq = 0;
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) n_eq += (i0 + u < C && ck[i0 + u] == T) ? 1u : 0u;
+      uint32_t tot_eq;
+      uint32_t eq_rank = block_excl_scan(n_eq, sm_w, &tot_eq);
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) {
+        const uint32_t i = i0 + u;
+        if (i < C) {
+          const uint32_t key = ck[i];
+          keep_member(i, key, eq_rank);
+          eq_rank += key == T ? 1u : 0u;
+        }
+      }
+    } else {
+      uint32_t eq_seen = 0;
+#pragma unroll 1
+      for (uint32_t t0 = 0; t0 < C; t0 += kSelThreads) {
+        const uint32_t i = t0 + tid;
+        const bool valid = i < C;
+        const uint32_t key = valid ? ck[i] : 0u;
+        uint32_t n_eq;
+        const uint32_t eq_rank = eq_seen + block_flag_rank(valid && key == T, sm_w, &n_eq);
+        if (valid) keep_member(i, key, eq_rank);
+        eq_seen += n_eq;
+      }
+    }
+    __syncthreads();
+    // this block's output offset: sinks, then the kept keys of earlier blocks
+    const uint32_t mine = tid < g.nb ? abv + sm_kept[tid] : 0u;
+    uint32_t total;
+    const uint32_t off = block_excl_scan(mine, sm_w, &total);
+    if (tid == b) sm_base = (uint32_t)g.nsink + off;
+    __syncthreads();
+    base = sm_base;
+    jt = take == 0 ? -1 : (int64_t)sm_jt;
+  }
   bool keep[kBlkPer];
   uint32_t n_keep = 0;
 #pragma unroll
@@ -509,11 +487,8 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const unsigned grid_b = (unsigned)(a.n_kv_heads * sel_blocks_max(a.n));
-  const unsigned grid_h = (unsigned)a.n_kv_heads;
   hipLaunchKernelGGL(sel_hist1_kernel, dim3(grid_b), dim3(kSelThreads), 0, stream, a);
-  hipLaunchKernelGGL(sel_pick1_kernel, dim3(grid_h), dim3(kSelThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_collect_kernel, dim3(grid_b), dim3(kSelThreads), 0, stream, a);
-  hipLaunchKernelGGL(sel_pick2_kernel, dim3(grid_h), dim3(kSelThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_write_kernel, dim3(grid_b), dim3(kSelThreads), 0, stream, a);
   return hipGetLastError();
 }
