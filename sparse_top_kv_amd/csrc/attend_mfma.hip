@@ -283,8 +283,8 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
   // max over the tile's keys of the lane's row (all four q4 lanes agree)
   auto row_max = [&](const float (&x)[4]) {
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    return fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = xor16_max(mx);
+    return xor32_max(mx);
   };
   // probabilities against the reference, into the sums and the P.V MFMAs
   auto accumulate = [&](const char* base, const float (&sv)[NG][4]) {
@@ -401,8 +401,8 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
       const int gi = g0 + u;
       if (gi < NG) {
         float lg = l[gi];
-        lg += __shfl_xor(lg, 16, 64);
-        lg += __shfl_xor(lg, 32, 64);
+        lg = xor16_sum(lg);
+        lg = xor32_sum(lg);
         if (lane < 16) {
           sm_m[u][wave][lane] = nst == 0 ? kNegInf : m[gi];
           sm_l[u][wave][lane] = nst == 0 ? 0.0f : lg;

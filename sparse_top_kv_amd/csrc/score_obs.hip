@@ -18,6 +18,7 @@
 // per key over the rows (DPP sum over the 16 row lanes at the end).
 #include "skv_kernels.h"
 #include "skv_mfma.h"
+#include "skv_tile.h"
 
 namespace skv {
 namespace {
@@ -57,15 +58,71 @@ __device__ __forceinline__ void load_k_tiles(const ScoreObsArgs& a, int h, int64
   }
 }
 
+// Query rows reach the waves through LDS: a workgroup stages kChunk 16-row
+// tiles of Q at a time (double-buffered), so the four waves share one copy.
+// The next chunk is loaded into registers while the current one is used and
+// written to LDS after it, so one barrier per chunk both publishes a chunk and
+// frees the buffer it replaces.  Rows are XOR-swizzled by row (swz_q) so the
+// B-operand reads (16 rows x one 16-byte piece per 16 lanes) are free of bank
+// conflicts.
+constexpr int kChunk = 8;  // Q tiles per chunk
+
+// Workgroup barrier after this wave's LDS writes have completed; outstanding
+// global loads (the next chunk) and statistics stores stay in flight across
+// it.  The signal fences keep the compiler from moving memory operations
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  wait_lgkm0();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int D>
-__device__ __forceinline__ void load_q_tile(const ScoreObsArgs& a, const RowInfo& ri, int q4,
-                                            bf16x8_t (&qb)[D / 32]) {
+struct QGeom {
+  static constexpr int kRB = D * 2;                  // bytes per query row
+  static constexpr int kPPR = kRB / 16;              // 16-byte pieces per row
+  static constexpr int kTileB = 16 * kRB;            // bytes per 16-row tile
+  static constexpr int kChunkB = kChunk * kTileB;
+  static constexpr int kPPT = kChunkB / 16 / kThreads;  // pieces per thread per chunk
+};
+
+// This thread's pieces of chunk c: piece e = tid + kThreads j is piece e % kPPR
+// of chunk row e / kPPR (rows past the window repeat a valid row).
+template <int D>
+__device__ __forceinline__ void load_q_chunk(const ScoreObsArgs& a, int h, int c, int tid,
+                                             uint4 (&v)[QGeom<D>::kPPT]) {
+  using QG = QGeom<D>;
+  const int R = a.n_obs * a.group;
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (ri.ok) u = ld16(a.q + ri.qoff + ks * 32 + q4 * 8);
-    qb[ks] = as_bf16x8(u);
+  for (int j = 0; j < QG::kPPT; ++j) {
+    const int e = tid + kThreads * j;
+    int row = c * kChunk * 16 + e / QG::kPPR;
+    row = row < R ? row : R - 1;
+    const RowInfo ri = row_info(a, h, row, D);
+    v[j] = ld16(a.q + ri.qoff + (e % QG::kPPR) * 8);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void store_q_chunk(char* dst, int tid, const uint4 (&v)[QGeom<D>::kPPT]) {
+  using QG = QGeom<D>;
+#pragma unroll
+  for (int j = 0; j < QG::kPPT; ++j) {
+    const int e = tid + kThreads * j;
+    const int rloc = e / QG::kPPR, piece = e % QG::kPPR;
+    *reinterpret_cast<uint4*>(dst + rloc * QG::kRB + ((piece ^ swz_q<D>(rloc & 15)) * 16)) = v[j];
+  }
+}
+
+// B operand of tile tt of a staged chunk: row i16, channels [32 ks + 8 q4, +8).
+template <int D>
+__device__ __forceinline__ void read_q_tile(const char* chunk, int tt, int q4, int i16, bf16x8_t (&qb)[D / 32]) {
+  using QG = QGeom<D>;
+  const char* row = chunk + tt * QG::kTileB + i16 * QG::kRB;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    qb[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(row + (((4 * ks + q4) ^ swz_q<D>(i16)) * 16)));
 }
 
 template <int D>
@@ -82,67 +139,50 @@ __device__ __forceinline__ void s_tiles(const bf16x8_t (&kf)[4][D / 32], const b
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs a) {
-  __shared__ float sm_ml[2][kWaves][16][2];
+  using QG = QGeom<D>;
+  __shared__ __attribute__((aligned(16))) char qc[2][QG::kChunkB];
+  __shared__ float sm_ml[2][kChunk][kWaves][16][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, i16 = lane & 15;
   const int h = blockIdx.x / a.n_kblocks;
   const int kb = blockIdx.x - h * a.n_kblocks;
-  const int64_t kw0 = (int64_t)kb * kBlockKeys + wave * 64;
+  const int kw0 = kb * kBlockKeys + wave * 64;  // keys are below 2^31
+  const int n = (int)a.n;
   const int R = a.n_obs * a.group;
   const int RT = (R + 15) / 16;
+  const int NCH = (RT + kChunk - 1) / kChunk;
+  // every window row sees keys <= n - W: no masks for a wave below that
+  const bool all_vis = kw0 + 63 <= n - a.n_obs;
+  // the workgroups of a kv head walk the query chunks from different starting
+  // points, so they do not all fetch the same chunk at the same time
+  const int rot = kb % NCH;
+  auto cid = [&](int c) { return c + rot < NCH ? c + rot : c + rot - NCH; };
 
   bf16x8_t kf[4][D / 32];
   load_k_tiles<D>(a, h, kw0, q4, i16, kf);
-  bf16x8_t qb[D / 32];
-  RowInfo ri = row_info(a, h, i16, D);
-  load_q_tile<D>(a, ri, q4, qb);
-
-  for (int rt = 0; rt < RT; ++rt) {
-    floatx4_t s[4];
-    s_tiles<D>(kf, qb, s);
-    const RowInfo cur = ri;
-    if (rt + 1 < RT) {  // next row tile's queries in flight during the softmax work
-      ri = row_info(a, h, (rt + 1) * 16 + i16, D);
-      load_q_tile<D>(a, ri, q4, qb);
-    }
-    float mw = kNegInf;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t key = kw0 + kt * 16 + q4 * 4 + r;
-        const float x = (key < a.n && key <= cur.last) ? s[kt][r] * a.scale_log2 : kNegInf;
-        s[kt][r] = x;
-        mw = fmaxf(mw, x);
-      }
-    }
-    mw = fmaxf(mw, __shfl_xor(mw, 16, 64));
-    mw = fmaxf(mw, __shfl_xor(mw, 32, 64));
-    const float mu = mw == kNegInf ? 0.0f : mw;
-    float lw = 0.0f;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lw += fast_exp2(s[kt][r] - mu);
-    }
-    lw += __shfl_xor(lw, 16, 64);
-    lw += __shfl_xor(lw, 32, 64);
-    const int buf = rt & 1;
-    if (q4 == 0) {
-      sm_ml[buf][wave][i16][0] = mw;
-      sm_ml[buf][wave][i16][1] = lw;
-    }
-    __syncthreads();
-    if (tid < 16) {
-      const int row = rt * 16 + tid;
+  {
+    uint4 v[QG::kPPT];
+    load_q_chunk<D>(a, h, cid(0), tid, v);
+    store_q_chunk<D>(qc[0], tid, v);
+  }
+  // K and the first chunk have landed: inside the loop only the next chunk's
+  // loads are in flight, and the matrix work never waits for them
+  wait_vm<0>();
+  // per-row (max, sum) of the workgroup's keys for the tiles of chunk cc
+  auto combine = [&](int c) {
+    const int cc = cid(c);
+    const int nt = RT - cc * kChunk < kChunk ? RT - cc * kChunk : kChunk;
+    if (tid < nt * 16) {
+      const int tt = tid >> 4, rr = tid & 15;
+      const int row = (cc * kChunk + tt) * 16 + rr;
       float M = kNegInf;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[buf][w][tid][0]);
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[c & 1][tt][w][rr][0]);
       float L = 0.0f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float mw2 = sm_ml[buf][w][tid][0];
-        L += mw2 == kNegInf ? 0.0f : sm_ml[buf][w][tid][1] * fast_exp2(mw2 - M);
+        const float mw2 = sm_ml[c & 1][tt][w][rr][0];
+        L += mw2 == kNegInf ? 0.0f : sm_ml[c & 1][tt][w][rr][1] * fast_exp2(mw2 - M);
       }
       if (row < R) {
         float* ml = a.part_ml + (((int64_t)h * a.n_kblocks + kb) * R + row) * 2;
@@ -150,7 +190,64 @@ __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs 
         ml[1] = L;
       }
     }
+  };
+
+  for (int c = 0; c < NCH; ++c) {
+    uint4 nxt[QG::kPPT];
+    if (c + 1 < NCH) load_q_chunk<D>(a, h, cid(c + 1), tid, nxt);
+    lds_barrier();  // chunk c and the statistics of chunk c - 1 are in LDS
+    if (c > 0) combine(c - 1);
+    const char* qchunk = qc[c & 1];
+    const int ci = cid(c);
+    const int nt = RT - ci * kChunk < kChunk ? RT - ci * kChunk : kChunk;
+    const float c2 = a.scale_log2;
+#pragma unroll
+    for (int tt = 0; tt < kChunk; ++tt) {
+      if (tt >= nt) break;  // uniform
+      bf16x8_t qb[D / 32];
+      read_q_tile<D>(qchunk, tt, q4, i16, qb);
+      floatx4_t s[4];
+      s_tiles<D>(kf, qb, s);
+      // S^T = K Q^T: lane (q4, i16) holds keys 16 kt + 4 q4 + r of query row
+      // 16 rt + i16.  The scale (> 0) is applied after the max, inside the
+      // exponent's fused multiply-add.
+      float mw = kNegInf;
+      if (!all_vis) {
+        const int last = (int)row_info(a, h, (ci * kChunk + tt) * 16 + i16, D).last;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kw0 + kt * 16 + q4 * 4 + r;
+            if (!(key < n && key <= last)) s[kt][r] = kNegInf;
+          }
+        }
+      }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        mw = fmaxf(mw, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
+      mw = xor16_max(mw);
+      mw = xor32_max(mw);
+      const float mu = mw == kNegInf ? 0.0f : mw * c2;
+      float lw = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lw += fast_exp2(fmaf(s[kt][r], c2, -mu));
+      }
+      lw = xor16_sum(lw);
+      lw = xor32_sum(lw);
+      if (q4 == 0) {
+        sm_ml[c & 1][tt][wave][i16][0] = mw == kNegInf ? kNegInf : mu;
+        sm_ml[c & 1][tt][wave][i16][1] = lw;
+      }
+    }
+    // the buffer of chunk c + 1 was last read in iteration c - 1, before the
+    // barrier above
+    if (c + 1 < NCH) store_q_chunk<D>(qc[(c + 1) & 1], tid, nxt);
   }
+  lds_barrier();
+  combine(NCH - 1);
 }
 
 // lse of every window row from its per-block statistics: one wave per row,
@@ -190,22 +287,39 @@ __global__ __launch_bounds__(kThreads) void obs_lse_kernel(const ScoreObsArgs a,
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void obs_pass2_kernel(const ScoreObsArgs a) {
+  using QG = QGeom<D>;
+  constexpr int kL2 = kChunk * 16;  // row normalisers per chunk
+  __shared__ __attribute__((aligned(16))) char qc[2][QG::kChunkB];
+  __shared__ float l2c[2][kL2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, i16 = lane & 15;
   const int h = blockIdx.x / a.n_kblocks;
   const int kb = blockIdx.x - h * a.n_kblocks;
-  const int64_t kw0 = (int64_t)kb * kBlockKeys + wave * 64;
-  if (kw0 >= a.n) return;
+  const int kw0 = kb * kBlockKeys + wave * 64;  // keys are below 2^31
+  const int n = (int)a.n;
   const int R = a.n_obs * a.group;
   const int RT = (R + 15) / 16;
-  const float* lse2 = a.row_lse2 + (int64_t)h * R;
+  const int NCH = (RT + kChunk - 1) / kChunk;
+  // every window row sees keys <= n - W: no masks for a wave below that
+  const bool all_vis = kw0 + 63 <= n - a.n_obs;
+  const int rot = kb % NCH;  // staggered chunk order, as in pass 1
+  auto cid = [&](int c) { return c + rot < NCH ? c + rot : c + rot - NCH; };
+  auto load_l2 = [&](int c) -> float {
+    int row = c * kL2 + tid;
+    row = row < R ? row : R - 1;
+    return tid < kL2 ? a.row_lse2[(int64_t)h * R + row] : 0.0f;
+  };
 
   bf16x8_t kf[4][D / 32];
   load_k_tiles<D>(a, h, kw0, q4, i16, kf);
-  bf16x8_t qb[D / 32];
-  RowInfo ri = row_info(a, h, i16, D);
-  load_q_tile<D>(a, ri, q4, qb);
-  float l2 = ri.ok ? lse2[i16] : 0.0f;
+  {
+    uint4 v[QG::kPPT];
+    load_q_chunk<D>(a, h, cid(0), tid, v);
+    const float l = load_l2(cid(0));
+    store_q_chunk<D>(qc[0], tid, v);
+    if (tid < kL2) l2c[0][tid] = l;
+  }
+  wait_vm<0>();  // K and the first chunk have landed (see pass 1)
 
   float acc[4][4];
 #pragma unroll
@@ -213,36 +327,63 @@ __global__ __launch_bounds__(kThreads) void obs_pass2_kernel(const ScoreObsArgs 
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[kt][r] = 0.0f;
 
-  for (int rt = 0; rt < RT; ++rt) {
-    floatx4_t s[4];
-    s_tiles<D>(kf, qb, s);
-    const RowInfo cur = ri;
-    const float cur_l2 = l2;
-    if (rt + 1 < RT) {
-      const int row = (rt + 1) * 16 + i16;
-      ri = row_info(a, h, row, D);
-      load_q_tile<D>(a, ri, q4, qb);
-      l2 = ri.ok ? lse2[row] : 0.0f;
+  for (int c = 0; c < NCH; ++c) {
+    uint4 nxt[QG::kPPT];
+    float l2n = 0.0f;
+    if (c + 1 < NCH) {
+      load_q_chunk<D>(a, h, cid(c + 1), tid, nxt);
+      l2n = load_l2(cid(c + 1));
     }
-    if (!cur.ok) continue;
+    lds_barrier();  // chunk c is in LDS
+    const char* qchunk = qc[c & 1];
+    const float* l2s = l2c[c & 1];
+    const int ci = cid(c);
+    const int nt = RT - ci * kChunk < kChunk ? RT - ci * kChunk : kChunk;
+    const float c2 = a.scale_log2;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int tt = 0; tt < kChunk; ++tt) {
+      if (tt >= nt) break;  // uniform
+      bf16x8_t qb[D / 32];
+      read_q_tile<D>(qchunk, tt, q4, i16, qb);
+      const float cur_l2 = l2s[tt * 16 + i16];
+      floatx4_t s[4];
+      s_tiles<D>(kf, qb, s);
+      const int row = (ci * kChunk + tt) * 16 + i16;
+      if (row >= R) continue;
+      if (all_vis) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t key = kw0 + kt * 16 + q4 * 4 + r;
-        const bool vis = key < a.n && key <= cur.last;
-        acc[kt][r] += vis ? fast_exp2(s[kt][r] * a.scale_log2 - cur_l2) : 0.0f;
+        for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[kt][r] += fast_exp2(fmaf(s[kt][r], c2, -cur_l2));
+        }
+      } else {
+        const int last = (int)row_info(a, h, row, D).last;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kw0 + kt * 16 + q4 * 4 + r;
+            const bool vis = key < n && key <= last;
+            acc[kt][r] += vis ? fast_exp2(fmaf(s[kt][r], c2, -cur_l2)) : 0.0f;
+          }
+        }
       }
     }
+    // the buffers of chunk c + 1 were last read in iteration c - 1
+    if (c + 1 < NCH) {
+      store_q_chunk<D>(qc[(c + 1) & 1], tid, nxt);
+      if (tid < kL2) l2c[(c + 1) & 1][tid] = l2n;
+    }
   }
+  if (kw0 >= n) return;
   const float inv_w = 1.0f / (float)a.n_obs;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float tot = group_sum<16>(acc[kt][r]);
-      const int64_t key = kw0 + kt * 16 + q4 * 4 + r;
-      if (i16 == 0 && key < a.n) a.score[(int64_t)h * a.score_stride + key] = tot * inv_w;
+      const int key = kw0 + kt * 16 + q4 * 4 + r;
+      if (i16 == 0 && key < n) a.score[(int64_t)h * a.score_stride + key] = tot * inv_w;
     }
   }
 }

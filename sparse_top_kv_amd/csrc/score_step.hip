@@ -138,12 +138,25 @@ __global__ __launch_bounds__(kThreads) void score_logits_kernel(const ScoreStepA
 // sum of probabilities for kFinalizeKeys keys.
 template <int G>
 __global__ __launch_bounds__(kThreads) void score_finalize_kernel(const ScoreStepArgs a, int nblk) {
+  static_assert(kFinalizeKeys == kThreads * 8, "eight keys per thread");
   __shared__ float sm_lse2[G];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x / nblk;
   const int b = blockIdx.x - h * nblk;
   const int cph = a.chunks_per_head;
   const int64_t nchunks = (a.n + a.chunk - 1) / a.chunk;
+  // this thread's eight keys of every head of the group, loaded first (the
+  // logits rows are padded to a multiple of four keys)
+  const int64_t jb = (int64_t)b * kFinalizeKeys + (int64_t)tid * 8;
+  float4 lg[G][2];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float* row = a.logits + (int64_t)(h * G + g) * a.logits_stride;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      lg[g][u] = jb + 4 * u < a.logits_stride ? *reinterpret_cast<const float4*>(row + jb + 4 * u)
+                                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
   const float* ml = a.part_ml + (int64_t)h * cph * G * 2;
   for (int g = wave; g < G; g += kWaves) {
     float M = kNegInf;
@@ -158,16 +171,21 @@ __global__ __launch_bounds__(kThreads) void score_finalize_kernel(const ScoreSte
     if (lane == 0) sm_lse2[g] = M + __log2f(L);
   }
   __syncthreads();
-  float lse2[G];
+  float s[8];
 #pragma unroll
-  for (int g = 0; g < G; ++g) lse2[g] = sm_lse2[g];
-  const int64_t j0 = (int64_t)b * kFinalizeKeys;
-  for (int64_t j = j0 + tid; j < j0 + kFinalizeKeys && j < a.n; j += kThreads) {
-    float s = 0.0f;
+  for (int e = 0; e < 8; ++e) s[e] = 0.0f;
 #pragma unroll
-    for (int g = 0; g < G; ++g) s += fast_exp2(a.logits[(int64_t)(h * G + g) * a.logits_stride + j] - lse2[g]);
-    a.score[(int64_t)h * a.score_stride + j] = s;
+  for (int g = 0; g < G; ++g) {
+    const float l2 = sm_lse2[g];
+    const float v[8] = {lg[g][0].x, lg[g][0].y, lg[g][0].z, lg[g][0].w,
+                        lg[g][1].x, lg[g][1].y, lg[g][1].z, lg[g][1].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] += fast_exp2(v[e] - l2);
   }
+  float* out = a.score + (int64_t)h * a.score_stride;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (jb + e < a.n) out[jb + e] = s[e];
 }
 
 // bf16 caches: phase 1 on the matrix cores.  K streams through a per-wave
@@ -287,11 +305,11 @@ __global__ __launch_bounds__(64 * W) void score_mfma_kernel(const ScoreStepArgs 
   }
 
   // (max, sum) of head li: the four q4 lanes, then the waves
-  float M = fmaxf(m, __shfl_xor(m, 16, 64));
-  M = fmaxf(M, __shfl_xor(M, 32, 64));
+  float M = xor16_max(m);
+  M = xor32_max(M);
   float x = (m == kNegInf) ? 0.0f : l * fast_exp2(m - M);
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
+  x = xor16_sum(x);
+  x = xor32_sum(x);
   if (lane < 16) {
     sm_m[wave][lane] = M;
     sm_l[wave][lane] = x;

@@ -38,6 +38,27 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // reverse within 8 lanes
 constexpr int kDppMirror = 0x140;     // reverse within 16 lanes
 
+// Lane l and lane l ^ 16 (resp. l ^ 32) combined with VALU lane swaps
+// (v_permlane16_swap / v_permlane32_swap) instead of an LDS-routed shuffle.
+// Both lanes of a pair compute the same expression on the same operands (the
+// lower lane's value first), so they hold bit-identical results.
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Sum over aligned groups of N lanes (N in 1..64, power of two); every lane
 // of the group receives the group sum.
 template <int N>
@@ -46,8 +67,8 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 4) x += dpp<kDppXor2>(x);
   if constexpr (N >= 8) x += dpp<kDppHalfMirror>(x);
   if constexpr (N >= 16) x += dpp<kDppMirror>(x);
-  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
+  if constexpr (N >= 32) x = xor16_sum(x);
+  if constexpr (N >= 64) x = xor32_sum(x);
   return x;
 }
 
@@ -57,8 +78,8 @@ __device__ __forceinline__ float group_max(float x) {
   if constexpr (N >= 4) x = fmaxf(x, dpp<kDppXor2>(x));
   if constexpr (N >= 8) x = fmaxf(x, dpp<kDppHalfMirror>(x));
   if constexpr (N >= 16) x = fmaxf(x, dpp<kDppMirror>(x));
-  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16, 64));
-  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32, 64));
+  if constexpr (N >= 32) x = xor16_max(x);
+  if constexpr (N >= 64) x = xor32_max(x);
   return x;
 }
 
