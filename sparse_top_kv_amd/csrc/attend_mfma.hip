@@ -407,11 +407,18 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
           sm_m[u][wave][lane] = nst == 0 ? kNegInf : m[gi];
           sm_l[u][wave][lane] = nst == 0 ? 0.0f : lg;
         }
-        float (*acc_w)[D] = reinterpret_cast<float (*)[D]>(&ring(u)[wave][0]);
+        // the wave's rows 4 q4 .. 4 q4 + 3 of column 16 n + li as one 16-byte
+        // store (column-major, 16 floats per column, the four row quads
+        // XOR-swizzled by column so eight lanes hit distinct banks); rows
+        // past the kv head's query rows are not staged
+        if (16 * gi + 4 * q4 < R) {
+          float* acc_w = reinterpret_cast<float*>(&ring(u)[wave][0]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int n = 0; n < NT; ++n) acc_w[4 * q4 + r][16 * n + li] = o[gi][n][r];
+          for (int n = 0; n < NT; ++n) {
+            const int col = 16 * n + li;
+            *reinterpret_cast<floatx4_t*>(acc_w + col * 16 + 4 * (q4 ^ ((col >> 1) & 3))) = o[gi][n];
+          }
+        }
       }
     }
     __syncthreads();
@@ -437,17 +444,15 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
 #pragma unroll
     for (int u = 0; u < GPR; ++u) {
       const int gi = g0 + u;
-      if (gi < NG) {
-        for (int e = tid; e < 16 * D; e += kT) {
-          const int rr = e / D, dd = e - rr * D;
-          const int row = 16 * gi + rr;
-          if (row < R) {
-            float A = 0.0f;
+      if (gi < NG && 16 * gi < R) {
+        const int rg = R - 16 * gi < 16 ? R - 16 * gi : 16;  // rows of this group
+        for (int e = tid; e < rg * D; e += kT) {
+          const int rr = e % rg, dd = e / rg;  // rows fastest: conflict-free reads
+          const int at = dd * 16 + 4 * ((rr >> 2) ^ ((dd >> 1) & 3)) + (rr & 3);
+          float A = 0.0f;
 #pragma unroll
-            for (int w = 0; w < W; ++w)
-              A += reinterpret_cast<const float (*)[D]>(&ring(u)[w][0])[rr][dd] * sm_l[u][w][rr];
-            a.part_acc[(slot * R + row) * D + dd] = A;
-          }
+          for (int w = 0; w < W; ++w) A += reinterpret_cast<const float*>(&ring(u)[w][0])[at] * sm_l[u][w][rr];
+          a.part_acc[(slot * R + 16 * gi + rr) * D + dd] = A;
         }
       }
     }
