@@ -40,6 +40,7 @@ int target_wgs() {
 struct ChunkPlan {
   int chunk;  // rows per workgroup
   int cph;    // chunks per kv head
+  bool list = false;  // work-list mode (see AttendArgs::items)
 };
 
 // Split rows_bound rows per kv head into chunks: about target_wgs() workgroups
@@ -112,13 +113,26 @@ int attend_granule(const skv_problem* p) {
   return skv::attend_waves() * skv::attend_rows_per_iter(p->dtype, p->head_dim);
 }
 
+// Gathered rows with many kv heads: counts are device values and may be very
+// uneven (per-head budgets), so a grid sized by the largest head would be
+// mostly empty workgroups.  Beyond twice the target workgroup count the call
+// runs in work-list mode with chunks of kListChunk rows.
+constexpr int kListChunk = 512;
+
 ChunkPlan attend_plan(const skv_problem* p, int64_t rows_bound, bool sparse) {
   int max_chunk;
   if (attend_uses_mfma(p))  // dense chunks need no per-row LDS, so they may grow
     max_chunk = sparse ? skv::attend_mfma_sparse_max_chunk() : (1 << 20);
   else
     max_chunk = sparse ? 512 : skv::attend_max_chunk();
-  return plan_chunks(rows_bound, p->n_kv_heads, attend_granule(p), max_chunk);
+  ChunkPlan cp = plan_chunks(rows_bound, p->n_kv_heads, attend_granule(p), max_chunk);
+  if (sparse && attend_uses_mfma(p) && (int64_t)p->n_kv_heads * cp.cph > 2 * (int64_t)target_wgs()) {
+    cp.chunk = kListChunk;
+    cp.cph = (int)((rows_bound + kListChunk - 1) / kListChunk);
+    if (cp.cph < 1) cp.cph = 1;
+    cp.list = true;
+  }
+  return cp;
 }
 
 hipError_t launch_attend_any(const skv_problem* p, bool sparse, const skv::AttendArgs& a,
@@ -131,16 +145,19 @@ hipError_t launch_attend_any(const skv_problem* p, bool sparse, const skv::Atten
 // Split-K scratch: partial (max, sum) and acc[d] per (kv head, chunk, row),
 // then the chunk count of every kv head.
 struct PartLayout {
-  size_t ml, acc, nch, end;
+  size_t ml, acc, nch, items, n_items, end;
 };
 
+// ... then the work list of (kv head, chunk) pairs and its length.
 PartLayout part_layout(const skv_problem* p, int cph, int rows_per_head) {
   const size_t slots = (size_t)p->n_kv_heads * cph * rows_per_head;
   PartLayout L;
   L.ml = SKV_WS_HEADER_BYTES;
   L.acc = L.ml + align_up(slots * 2 * sizeof(float));
   L.nch = L.acc + align_up(slots * p->head_dim * sizeof(float));
-  L.end = L.nch + align_up((size_t)p->n_kv_heads * sizeof(int32_t));
+  L.items = L.nch + align_up((size_t)p->n_kv_heads * sizeof(int32_t));
+  L.n_items = L.items + align_up((size_t)p->n_kv_heads * cph * 2 * sizeof(int32_t));
+  L.end = L.n_items + align_up(sizeof(int32_t));
   return L;
 }
 
@@ -345,6 +362,13 @@ skv_status skv_attend_sparse(const skv_problem* p, const void* q, const void* k,
   a.nch = (int32_t*)(base + L.nch);
   a.group = G;
   a.n_pos = 1;
+  if (cp.list) {
+    a.items = (int2*)(base + L.items);
+    a.n_items = (int32_t*)(base + L.n_items);
+    // four-wave workgroups, two per CU, walking the list
+    const int64_t pairs = (int64_t)p->n_kv_heads * cp.cph, cap = 4 * (int64_t)target_wgs();
+    a.list_grid = (int32_t)(pairs < cap ? pairs : cap);
+  }
   if ((st = hip_status(launch_attend_any(p, true, a, (hipStream_t)stream))) != SKV_OK)
     return st;
   return launch_partials_merge(p, base, L, cp.cph, G, true, out, lse, (hipStream_t)stream);

@@ -40,6 +40,7 @@
 #include "skv_kernels.h"
 #include "skv_mfma.h"
 #include "skv_tile.h"
+#include "skv_block.h"
 
 namespace skv {
 namespace {
@@ -51,7 +52,7 @@ constexpr float kSlack = 30.0f;
 // Query rows of kv head h: r = t * G + g for position t < a.n_pos and group
 // member g < G (decode: one position).  CAUSAL: row r sees keys
 // j <= n - n_pos + t (the verify pass); otherwise every key of the set.
-template <int D, int NG, bool SPARSE, bool CAUSAL, int W, int S>
+template <int D, int NG, bool SPARSE, bool CAUSAL, int W, int S, bool LIST>
 __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a) {
   using TG = TileGeom<D>;
   constexpr int NI = TG::kNI, TB = TG::kTB, PPR = TG::kPPR, KS = TG::kKS, NT = TG::kNT;
@@ -73,8 +74,10 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, li = lane & 15;
   const int cph = a.chunks_per_head;
-  const int h = blockIdx.x / cph;
-  const int c = blockIdx.x - h * cph;
+  static_assert(!LIST || SPARSE, "the work list serves gathered rows");
+
+  // one (kv head, chunk) pair
+  auto body = [&](const int h, const int c) {
   const int G = a.group;
   const int R = G * a.n_pos;  // query rows of this kv head
   const int Hq = a.n_kv_heads * G;
@@ -459,6 +462,52 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
     __syncthreads();
   }
   if (c == 0 && tid == 0) a.nch[h] = nch;
+  };
+
+  if constexpr (LIST) {
+    const int total = *a.n_items;
+    for (int it = blockIdx.x; it < total; it += gridDim.x) {
+      const int2 hc = a.items[it];
+      body(hc.x, hc.y);
+    }
+  } else {
+    body(blockIdx.x / cph, blockIdx.x % cph);
+  }
+}
+
+// The (kv head, chunk) pairs of a gathered-rows call that hold rows, in head
+// order: chunks 0 .. nch_h - 1 of head h, nch_h = clamp(ceil(rows_h / chunk),
+// 1, chunks_per_head), rows_h = clamp(count[h]) + (n - tail_start).  One
+// 1024-thread workgroup; each thread owns consecutive heads.
+__global__ __launch_bounds__(kSelThreads) void attend_items_kernel(const AttendArgs a) {
+  __shared__ uint32_t sm_w[kSelWaves + 1];
+  const int tid = threadIdx.x;
+  const int H = a.n_kv_heads, cph = a.chunks_per_head;
+  const int per = (H + kSelThreads - 1) / kSelThreads;
+  auto nch_of = [&](int h) {
+    int64_t cnt = a.count[h];
+    cnt = cnt < 0 ? 0 : (cnt > a.count_max ? a.count_max : cnt);
+    const int64_t rows = cnt + (a.n - a.tail_start);
+    int64_t nc = (rows + a.chunk - 1) / a.chunk;
+    nc = nc < 1 ? 1 : (nc > cph ? cph : nc);
+    return (uint32_t)nc;
+  };
+  uint32_t mine = 0;
+  for (int k = 0; k < per; ++k) {
+    const int h = tid * per + k;
+    if (h < H) mine += nch_of(h);
+  }
+  uint32_t total;
+  uint32_t base = block_excl_scan(mine, sm_w, &total);
+  for (int k = 0; k < per; ++k) {
+    const int h = tid * per + k;
+    if (h < H) {
+      const uint32_t nc = nch_of(h);
+      for (uint32_t c = 0; c < nc; ++c) a.items[base + c] = make_int2(h, (int)c);
+      base += nc;
+    }
+  }
+  if (tid == 0) *a.n_items = (int32_t)total;
 }
 
 // Eight waves with a two-tile ring (one 128 KB workgroup per CU), the
@@ -472,8 +521,18 @@ template <int D, int NG, bool SPARSE, bool CAUSAL>
 hipError_t launch_k(const AttendArgs& a, hipStream_t s) {
   constexpr int W = mfma_waves<D, NG>();
   constexpr int S = W == 8 ? 2 : 4;
+  if constexpr (SPARSE) {
+    if (a.items) {
+      hipLaunchKernelGGL(attend_items_kernel, dim3(1), dim3(kSelThreads), 0, s, a);
+      // four waves with a two-tile ring (64 KB): two workgroups per CU overlap
+      // one item's start and end with the other's streaming
+      hipLaunchKernelGGL((attend_mfma_kernel<D, NG, SPARSE, CAUSAL, 4, 2, true>), dim3((unsigned)a.list_grid),
+                         dim3(64 * 4), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid((unsigned)(a.n_kv_heads * a.chunks_per_head));
-  hipLaunchKernelGGL((attend_mfma_kernel<D, NG, SPARSE, CAUSAL, W, S>), grid, dim3(64 * W), 0, s, a);
+  hipLaunchKernelGGL((attend_mfma_kernel<D, NG, SPARSE, CAUSAL, W, S, false>), grid, dim3(64 * W), 0, s, a);
   return hipGetLastError();
 }
 

@@ -29,6 +29,12 @@ struct AttendArgs {
   int32_t* nch;             // [Hkv] chunks actually used per kv head
   int32_t group;            // G = Hq / Hkv
   int32_t n_pos;            // query positions (1 for a decode step); R = n_pos * G rows
+  // Work-list mode (gathered rows, many kv heads with ragged counts): a small
+  // kernel lists the (kv head, chunk) pairs that hold rows, and list_grid
+  // workgroups walk that list.  items == nullptr: one workgroup per pair.
+  int2* items;              // [n_kv_heads * chunks_per_head]
+  int32_t* n_items;
+  int32_t list_grid;
 };
 
 hipError_t launch_attend(int dtype, int d, int g, bool sparse, const AttendArgs& a,

@@ -309,3 +309,41 @@ def test_sparse_with_full_set_equals_dense_and_is_deterministic():
     torch.cuda.synchronize()
     assert (o1 - o2).abs().max().item() <= 2e-3
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+@pytest.mark.parametrize("hq,hkv,n,tail", [(600, 600, 3000, 2968), (1024, 512, 2100, 2100)])
+def test_attend_sparse_many_heads_ragged_counts(hq, hkv, n, tail):
+    """Many kv heads with very uneven kept counts (SparseMM-style budgets,
+    empty heads included): the call runs from a device-built work list of
+    (kv head, chunk) pairs instead of one workgroup per pair."""
+    banner(f"sparse many heads hq={hq} hkv={hkv} n={n} tail={tail}")
+    d = 128
+    rng = np.random.default_rng(21)
+    counts = np.minimum(rng.exponential(60, hkv).astype(np.int64), tail)
+    counts[rng.choice(hkv, 8, replace=False)] = tail            # a few heavy heads
+    counts[rng.choice(hkv, 8, replace=False)] = 0               # and some empty index lists
+    stride = int(counts.max())
+    idx = np.full((hkv, stride), -1, np.int32)
+    for h in range(hkv):
+        idx[h, :counts[h]] = np.sort(rng.choice(tail, counts[h], replace=False))
+    cnt = counts.astype(np.int32)
+    q = _rand((hq, d), 22, "bf16")
+    k = _cache(hkv, n, d, 23, "bf16", cap_extra=0)
+    v = _cache(hkv, n, d, 24, "bf16", cap_extra=0)
+    ref_o, ref_l = oracle.attend_sparse(q, k, v, n, idx, cnt, tail)
+    qt, kt, vt = dev(q), dev(k), dev(v)
+    out = torch.full((hq, d), float("nan"), device="cuda")
+    lse = torch.full((hq,), float("nan"), device="cuda")
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n)
+    it, ct = dev(idx), dev(cnt)
+    skv.skv_attend_sparse(qt, kt, vt, n, it, ct, tail, out, lse, ws)
+    out2 = torch.empty_like(out)
+    skv.skv_attend_sparse(qt, kt, vt, n, it, ct, tail, out2, lse, ws)
+    torch.cuda.synchronize()
+    to, tl = TOL["bf16"]
+    o, l = host(out), host(lse)
+    empty = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(l), empty)
+    assert np.abs(o - ref_o).max() <= to
+    assert np.abs(l[~empty] - ref_l[~empty]).max(initial=0) <= tl
+    assert torch.equal(out, out2)  # the work list is deterministic
