@@ -63,7 +63,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=8, help="distinct caches rotated at 32K")
     ap.add_argument("--blocks", type=int, default=5, help="timed blocks (median reported)")
-    ap.add_argument("--sections", default="default", help="headline | default | all")
+    ap.add_argument("--sections", default="default",
+                    help="headline | default | all | mfma (profiling: only the Qwen2-7B matrix-core "
+                         "calls, no bench line)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 512 MiB device copy (counter calibration under a profiler)")
@@ -196,6 +198,25 @@ def main():
             res[str(nn)] = entry
             del win
         return res
+
+    if args.sections == "mfma":
+        # profiling mode for counter runs: the two matrix-core calls of the
+        # Qwen2-7B workload (text-window score, W = 512; gamma = 5 verify)
+        wq = synth.qwen_std()
+        m = wq.extra["m_v"] + wq.extra["m_t"]
+        gq = wq.extra["gamma"]
+        qo4, k4, v4 = dev(wq.q_obs), dev(wq.k), dev(wq.v)
+        qv4 = dev(wq.extra["q_verify"])
+        ws4 = skv.Workspace.for_problem(skv.problem_for(qo4, k4), m + gq, wq.extra["m_t"])
+        sc4 = torch.empty((wq.n_kv_heads, m), device="cuda")
+        ov = torch.empty((gq, wq.n_q_heads, wq.head_dim), device="cuda")
+        lv = torch.empty((gq, wq.n_q_heads), device="cuda")
+        sc_us, _ = time_steps(lambda i: skv.skv_score(qo4, k4, m, sc4, ws4), 3, 1, 1, graph=False)
+        v_us, _ = time_steps(lambda i: skv.skv_verify(qv4, k4, v4, m + gq, ov, lv, ws4), 20, 2, 1,
+                             graph=False)
+        print(json.dumps({"sections": "mfma", "text_window_score_us": round(sc_us, 1),
+                          "verify_us": round(v_us, 2)}), flush=True)
+        return
 
     # ------------------------------------------------------------------
     # headline: Llama-3.1-8B shape, 32K, 30 % kept via window score once
@@ -399,6 +420,8 @@ def main():
             skv.skv_select(sc4, m, 0, m_t, wq.k_top, idx4, cnt4, ws4)
 
         sel4_us, _ = time_steps(sel4, 4, 1, 1, graph=False)
+        obs4_us, _ = time_steps(lambda i: skv.skv_score(qo4, kv4[i % L4][0], m, sc4, ws4), 4, 1, 3)
+        obs4_flops = rf.obs_score_flops(hq4, m, d, m_t)
         o4 = torch.empty((hq4, d), device="cuda")
         l4 = torch.empty(hq4, device="cuda")
         ov = torch.empty((gamma, hq4, d), device="cuda")
@@ -455,6 +478,9 @@ def main():
         dense_round_bytes = sum(rf.dense_step_bytes(hq4, hkv4, d, m + t + 1, "bf16") for t in range(gamma))
         details["qwen_std"] = {
             "text_window_score_plus_select_once_us": round(sel4_us, 1),
+            "text_window_score_us": round(obs4_us, 1),
+            "text_window_score_tflops": round(obs4_flops / (obs4_us * 1e-6) / 1e12, 1),
+            "text_window_score_mfma_frac_of_bf16_peak": round(obs4_flops / (obs4_us * 1e-6) / 2.5e15, 4),
             "round_5_drafts_plus_verify_us": round(r_us, 2),
             "dense_5_steps_us": round(rd_us, 2),
             "verify_us": round(v_us, 3),

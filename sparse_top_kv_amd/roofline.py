@@ -99,6 +99,12 @@ def verify_flops(hq: int, n: int, d: int, gamma: int) -> int:
     return 2 * 2 * hq * d * keys
 
 
+def obs_score_flops(hq: int, n: int, d: int, n_obs: int) -> int:
+    """q.k multiply-adds of the observation-window score: every window row of
+    every query head against every key, computed twice (the two passes)."""
+    return 2 * 2 * hq * n_obs * n * d
+
+
 def roofline_fraction(nbytes: float, seconds: float, peak: float = HBM_PEAK_BYTES_PER_S) -> float:
     return nbytes / seconds / peak
 

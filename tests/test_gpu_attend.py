@@ -311,13 +311,13 @@ def test_sparse_with_full_set_equals_dense_and_is_deterministic():
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
 
 
-@pytest.mark.parametrize("hq,hkv,n,tail", [(600, 600, 3000, 2968), (1024, 512, 2100, 2100)])
-def test_attend_sparse_many_heads_ragged_counts(hq, hkv, n, tail):
+@pytest.mark.parametrize("hq,hkv,n,tail,d", [(600, 600, 3000, 2968, 128), (1024, 512, 2100, 2100, 128),
+                                             (700, 700, 1500, 1400, 64)])
+def test_attend_sparse_many_heads_ragged_counts(hq, hkv, n, tail, d):
     """Many kv heads with very uneven kept counts (SparseMM-style budgets,
     empty heads included): the call runs from a device-built work list of
     (kv head, chunk) pairs instead of one workgroup per pair."""
-    banner(f"sparse many heads hq={hq} hkv={hkv} n={n} tail={tail}")
-    d = 128
+    banner(f"sparse many heads hq={hq} hkv={hkv} n={n} tail={tail} d={d}")
     rng = np.random.default_rng(21)
     counts = np.minimum(rng.exponential(60, hkv).astype(np.int64), tail)
     counts[rng.choice(hkv, 8, replace=False)] = tail            # a few heavy heads
