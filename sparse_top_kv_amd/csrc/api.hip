@@ -40,7 +40,8 @@ int target_wgs() {
 struct ChunkPlan {
   int chunk;  // rows per workgroup
   int cph;    // chunks per kv head
-  bool list = false;  // work-list mode (see AttendArgs::items)
+  bool list = false;    // work-list mode (see AttendArgs::items)
+  bool narrow = false;  // four-wave workgroups (see AttendArgs::narrow)
 };
 
 // Split rows_bound rows per kv head into chunks: about target_wgs() workgroups
@@ -131,6 +132,17 @@ ChunkPlan attend_plan(const skv_problem* p, int64_t rows_bound, bool sparse) {
     cp.cph = (int)((rows_bound + kListChunk - 1) / kListChunk);
     if (cp.cph < 1) cp.cph = 1;
     cp.list = true;
+  }
+  // Small calls (e.g. a draft step over a few thousand kept rows) leave most
+  // CUs idle with eight-wave workgroups: halve the workgroups' width instead.
+  const int G = p->n_q_heads / p->n_kv_heads;
+  if (!cp.list && attend_uses_mfma(p) && G <= 16 &&
+      (int64_t)p->n_kv_heads * cp.cph <= (int64_t)target_wgs() / 2) {
+    const ChunkPlan n4 = plan_chunks(rows_bound, p->n_kv_heads, skv::attend_mfma_narrow_granule(), max_chunk);
+    if (n4.cph > cp.cph) {
+      cp = n4;
+      cp.narrow = true;
+    }
   }
   return cp;
 }
@@ -318,6 +330,7 @@ skv_status skv_attend_dense(const skv_problem* p, const void* q, const void* k, 
   a.nch = (int32_t*)(base + L.nch);
   a.group = G;
   a.n_pos = 1;
+  a.narrow = cp.narrow;
   if ((st = hip_status(launch_attend_any(p, false, a, (hipStream_t)stream))) != SKV_OK)
     return st;
   return launch_partials_merge(p, base, L, cp.cph, G, false, out, lse, (hipStream_t)stream);
@@ -362,6 +375,7 @@ skv_status skv_attend_sparse(const skv_problem* p, const void* q, const void* k,
   a.nch = (int32_t*)(base + L.nch);
   a.group = G;
   a.n_pos = 1;
+  a.narrow = cp.narrow;
   if (cp.list) {
     a.items = (int2*)(base + L.items);
     a.n_items = (int32_t*)(base + L.n_items);

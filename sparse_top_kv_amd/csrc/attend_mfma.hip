@@ -532,6 +532,12 @@ hipError_t launch_k(const AttendArgs& a, hipStream_t s) {
     }
   }
   const dim3 grid((unsigned)(a.n_kv_heads * a.chunks_per_head));
+  if constexpr (NG == 1 && !CAUSAL) {
+    if (a.narrow) {
+      hipLaunchKernelGGL((attend_mfma_kernel<D, NG, SPARSE, CAUSAL, 4, 2, false>), grid, dim3(64 * 4), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((attend_mfma_kernel<D, NG, SPARSE, CAUSAL, W, S, false>), grid, dim3(64 * W), 0, s, a);
   return hipGetLastError();
 }
@@ -554,6 +560,7 @@ int attend_mfma_granule(int rows, int d) {
   return w * kStep;
 }
 int attend_mfma_sparse_max_chunk() { return kSparseMaxChunk; }
+int attend_mfma_narrow_granule() { return 4 * kStep; }
 int attend_mfma_max_rows() { return 64; }
 
 hipError_t launch_attend_mfma(int d, bool sparse, bool causal, const AttendArgs& a, hipStream_t s) {

@@ -35,6 +35,9 @@ struct AttendArgs {
   int2* items;              // [n_kv_heads * chunks_per_head]
   int32_t* n_items;
   int32_t list_grid;
+  // Four-wave workgroups (chunks a multiple of attend_mfma_narrow_granule())
+  // for decode calls too small to fill the CUs with eight-wave ones.
+  int32_t narrow;
 };
 
 hipError_t launch_attend(int dtype, int d, int g, bool sparse, const AttendArgs& a,
@@ -66,6 +69,7 @@ hipError_t launch_attend_mfma(int d, bool sparse, bool causal, const AttendArgs&
                               hipStream_t stream);
 int attend_mfma_granule(int rows, int d);
 int attend_mfma_sparse_max_chunk();
+int attend_mfma_narrow_granule();
 int attend_mfma_max_rows();
 
 // Per-step score (one decode query): phase 1 writes log2-domain logits and
