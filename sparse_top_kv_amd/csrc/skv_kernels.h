@@ -100,7 +100,7 @@ struct ScoreObsArgs {
   int64_t n;
   int32_t n_obs;            // W
   int32_t n_kv_heads, group;
-  int32_t n_kblocks;        // key blocks of 256 per head
+  int32_t n_kblocks;        // key blocks of score_obs_block_keys() per head
   float scale_log2;
   float* part_ml;           // [Hkv][n_kblocks][R][2], R = W * G
   float* row_lse2;          // [Hkv][R]
@@ -129,7 +129,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 // path is used for this shape).
 size_t select_ws_bytes(int32_t n_kv_heads, int64_t n);
 
-// Causal verify of gamma queries on MFMA (bf16).
+// Fill count words with zero (a kernel, so it may sit in a captured graph).
 hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t stream);
 
 // Verifier-guided top-P retention + uniform fill (skv_select_topp).
