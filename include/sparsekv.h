@@ -45,6 +45,11 @@
  *     returns SKV_ERR_HIP.
  *   - Determinism: identical inputs give bit-identical outputs (fixed
  *     reduction orders, no floating-point atomics).
+ *   - Tuning: the environment variable SKV_TARGET_WGS (read once, default
+ *     256, clamped to [1, 65536]) sets the workgroup count the split-K plans
+ *     aim for.  It changes how a key set is cut into chunks, hence the
+ *     summation order: results stay deterministic for a fixed setting and
+ *     may differ in the last bits between settings.
  */
 #ifndef SPARSEKV_H
 #define SPARSEKV_H

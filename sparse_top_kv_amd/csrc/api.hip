@@ -33,7 +33,10 @@ int env_int(const char* name, int dflt) {
 // Workgroup count the split-K attention aims for: one per CU on 256 CUs
 // (measured best on MI355X for 32K-128K; more chunks only add merge work).
 int target_wgs() {
-  static const int t = env_int("SKV_TARGET_WGS", 256);
+  static const int t = [] {
+    const int v = env_int("SKV_TARGET_WGS", 256);
+    return v < 1 ? 1 : (v > 65536 ? 65536 : v);
+  }();
   return t;
 }
 
