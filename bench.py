@@ -18,7 +18,8 @@ roofline figure divides the algorithmic bytes by the whole step time, so the
 merge counts against it.  Eager (one host launch per call) times are reported
 beside the graph times.
 
-Also reported in `details` (default sections): the 30 % sink-plus-recent
+Also reported in `details` (default sections): the tiny fp32 MHA parity
+configuration (per-step top-K and dense at 2K), the 30 % sink-plus-recent
 window against dense decoding through masked, fused and split-K attention
 (2K-128K; the masked and fused paths are PyTorch baselines), compaction of the 32K kept
 sets into contiguous caches (gather once, then the dense step over them),
@@ -394,6 +395,28 @@ def main():
         # ------------------------------------------------------------------
         # Qwen2-7B video Sparse-to-Dense round: 5 sparse drafts + 1 verify
         # ------------------------------------------------------------------
+        # tiny MHA fp32 (the parity configuration): per-step top-K and dense
+        wt = synth.tiny_mha()
+        qt1, kt1, vt1 = dev(wt.q), dev(wt.k), dev(wt.v)
+        wst = skv.Workspace.for_problem(skv.problem_for(qt1, kt1), wt.n)
+        sct = torch.empty((wt.n_kv_heads, wt.n), device="cuda")
+        idxt = torch.empty((wt.n_kv_heads, wt.n_sink + wt.k_top), dtype=torch.int32, device="cuda")
+        cntt = torch.empty(wt.n_kv_heads, dtype=torch.int32, device="cuda")
+        ot = torch.empty((wt.n_q_heads, wt.head_dim), device="cuda")
+        lt = torch.empty(wt.n_q_heads, device="cuda")
+
+        def tiny_topk(i):
+            skv.skv_score(qt1, kt1, wt.n, sct, wst)
+            skv.skv_select(sct, wt.n, wt.n_sink, wt.n_recent, wt.k_top, idxt, cntt, wst)
+            skv.skv_attend_sparse(qt1, kt1, vt1, wt.n, idxt, cntt, wt.n - wt.n_recent, ot, lt, wst)
+
+        tk_us, _ = time_steps(tiny_topk, args.steps, args.warmup, 3)
+        td_us, _ = time_steps(lambda i: skv.skv_attend_dense(qt1, kt1, vt1, wt.n, ot, lt, wst),
+                              args.steps, args.warmup, 3)
+        details["tiny_mha_fp32_2k"] = {"topk_step_us": round(tk_us, 2), "dense_step_us": round(td_us, 2),
+                                       "note": "launch-bound parity configuration (8 heads, d = 64, fp32)"}
+        del qt1, kt1, vt1
+
         log("generating the Qwen2-7B video workload")
         wq = synth.qwen_std()
         m_v, m_t, gamma = wq.extra["m_v"], wq.extra["m_t"], wq.extra["gamma"]
