@@ -8,11 +8,12 @@
 // from the SparseMM budgets).  Order: score descending, index ascending.
 //
 // One 1024-thread workgroup per kv head.  Scores map to order-preserving
-// 32-bit keys (score_key); three counting passes over the candidates with
-// 2048/2048/1024-bin LDS histograms fix the key T of the K-th entry and how
-// many entries equal to T are taken.  A final pass in index order writes, via
-// block-wide ballots, every key > T and the lowest-index `take` keys == T, so
-// the output is ascending without a sort and ties go to the lowest index.
+// 32-bit keys (score_key); the first kStage keys are loaded once into LDS (one
+// round of global loads), the rest, if any, are re-read per pass.  Three
+// counting passes with 2048/2048/1024-bin LDS histograms fix the key T of the
+// K-th entry and how many entries equal to T are taken.  A final pass in index
+// order writes every key > T and the lowest-index `take` keys == T, so the
+// output is ascending without a sort and ties go to the lowest index.
 #include "skv_common.h"
 #include "skv_kernels.h"
 #include "skv_block.h"
@@ -22,8 +23,16 @@ namespace {
 
 constexpr int kBins = 2048;
 
+constexpr int kStage = 16384;                 // keys staged in LDS (64 KB)
+constexpr int kStagePer = kStage / kSelThreads;
+constexpr int kStageFrom = 4096;              // staging pays from this many candidates
+
+// STAGE: stage the first kStage candidates in LDS (longer rows; the 64 KB
+// would cost occupancy for short rows, whose passes hit the caches anyway).
+template <bool STAGE>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a) {
   __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t sm_key[STAGE ? kStage : 1];
   __shared__ uint32_t sm_w[kSelWaves + 1];
   __shared__ uint32_t sm_digit, sm_krem;
 
@@ -36,6 +45,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
   const int64_t nsink = a.n_sink < tail ? a.n_sink : tail;
   const int64_t c_lo = a.n_sink, c_hi = n - a.n_recent;
   const int64_t ncand = c_lo < c_hi ? c_hi - c_lo : 0;
+  const int64_t nst = !STAGE ? 0 : (ncand < kStage ? ncand : kStage);  // staged candidates
   int64_t K = a.k_per_head ? a.k_per_head[h] : a.k_uniform;
   K = K < 0 ? 0 : K;
   K = K > ncand ? ncand : K;
@@ -49,6 +59,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
     return;
   }
 
+  // ---- stage: every load of the first kStage candidates in one round -------
+  if constexpr (STAGE) {
+    float v[kStagePer];
+#pragma unroll
+    for (int u = 0; u < kStagePer; ++u) {
+      const int64_t i = tid + (int64_t)u * kSelThreads;
+      v[u] = i < nst ? s[c_lo + i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kStagePer; ++u) {
+      const int64_t i = tid + (int64_t)u * kSelThreads;
+      if (i < nst) sm_key[i] = score_key(v[u]);
+    }
+  }
+  // candidate i (0-based from c_lo): LDS when staged, else global
+  auto key_at = [&](int64_t i) -> uint32_t { return i < nst ? sm_key[i] : score_key(s[c_lo + i]); };
+
   // ---- radix passes: digits [31:21], [20:10], [9:0] of the key ----------
   uint32_t prefix = 0, mask = 0;
   uint32_t krem = (uint32_t)K;  // how many of the remaining keys still to take
@@ -57,10 +84,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int nb = pass == 2 ? 1024 : 2048;
     for (int b = tid; b < kBins; b += kSelThreads) hist[b] = 0u;
-    __syncthreads();
-    for (int64_t j = c_lo + tid; j < c_hi; j += kSelThreads) {
-      const uint32_t key = score_key(s[j]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+    __syncthreads();  // also orders the staging stores before the first pass
+    for (int64_t i0 = 0; i0 < ncand; i0 += kSelThreads) {  // wave-uniform trip count
+      const int64_t i = i0 + tid;
+      const bool valid = i < ncand;
+      const uint32_t key = valid ? key_at(i) : 0u;
+      if (valid && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
     }
     __syncthreads();
     // bins are visited from the top; thread t owns nb/1024 consecutive bins
@@ -89,21 +118,49 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
   }
   const uint32_t T = prefix;
   const uint32_t take = krem;  // keys equal to T to keep, lowest index first
+  const uint32_t limit = (uint32_t)(nsink + K);
 
   // ---- compaction in index order ------------------------------------------
+  if (STAGE && nst == ncand) {
+    // all staged: thread t owns the run [t P, t P + P) of candidates, so two
+    // workgroup scans rank the equal keys and the kept keys
+    const int64_t P = (ncand + kSelThreads - 1) / kSelThreads;
+    const int64_t i0 = tid * P;
+    const int64_t i1 = i0 + P < ncand ? i0 + P : ncand;
+    uint32_t n_eq = 0, n_gt = 0;
+    for (int64_t i = i0; i < i1; ++i) {
+      const uint32_t key = sm_key[i];
+      n_eq += key == T ? 1u : 0u;
+      n_gt += key > T ? 1u : 0u;
+    }
+    uint32_t tot;
+    uint32_t eq_rank = block_excl_scan(n_eq, sm_w, &tot);
+    const uint32_t gt_before = block_excl_scan(n_gt, sm_w, &tot);
+    uint32_t pos = (uint32_t)nsink + gt_before + (eq_rank < take ? eq_rank : take);
+    for (int64_t i = i0; i < i1; ++i) {
+      const uint32_t key = sm_key[i];
+      const bool eq = key == T;
+      if (key > T || (eq && eq_rank < take)) {
+        if (pos < limit) out[pos] = (int32_t)(c_lo + i);  // never past the row
+        ++pos;
+      }
+      eq_rank += eq ? 1u : 0u;
+    }
+    return;
+  }
   uint32_t base = (uint32_t)nsink, eq_seen = 0;
 #pragma unroll 1
-  for (int64_t t0 = c_lo; t0 < c_hi; t0 += kSelThreads) {
-    const int64_t j = t0 + tid;
-    const bool valid = j < c_hi;
-    const uint32_t key = valid ? score_key(s[j]) : 0u;
+  for (int64_t t0 = 0; t0 < ncand; t0 += kSelThreads) {
+    const int64_t i = t0 + tid;
+    const bool valid = i < ncand;
+    const uint32_t key = valid ? key_at(i) : 0u;
     const bool eq = valid && key == T;
     uint32_t n_eq;
     const uint32_t eq_rank = eq_seen + block_flag_rank(eq, sm_w, &n_eq);
     const bool keep = valid && (key > T || (eq && eq_rank < take));
     uint32_t n_keep;
     const uint32_t pos = base + block_flag_rank(keep, sm_w, &n_keep);
-    if (keep && pos < (uint32_t)(nsink + K)) out[pos] = (int32_t)j;  // never past the row
+    if (keep && pos < limit) out[pos] = (int32_t)(c_lo + i);  // never past the row
     base += n_keep;
     eq_seen += n_eq;
   }
@@ -113,25 +170,35 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
 // ---------------------------------------------------------------------------
 // Block-parallel path for long caches with few kv heads (a one-workgroup-per-
 // head select would leave most CUs idle).  Candidates are cut into blocks of
-// kBlk; three kernels, no global atomics, so the result is identical run to
-// run.  The per-head steps between them are recomputed by every block of the
-// head from the same data (cheaper than a one-workgroup-per-head launch):
-//   1 per block: histogram of key bits [31:21]
-//   2 per block: from all block histograms of its head, the bin d1 holding the
-//                K-th key and how many to take from it, and where this block's
-//                bin members go; copy them (key, index) in index order and
-//                count the keys above the bin.  Block 0 records the head's
-//                state, the sinks and the count.
-//   3 per block: finish the radix select on the head's bin members (bits
-//                [20:10], [9:0]) -> threshold key T and how many keys equal to
-//                T are kept, lowest index first; this block's output offset;
-//                write its kept indices
+// kBlk.  Radix digits: key bits [31:20] (4096 bins), [19:9] (2048), [8:0]
+// (512).  Integer histogram totals are the only global atomics, so the result
+// is identical run to run.  A clear kernel zeroes the head totals, then:
+//   1 per block: histogram of the first digit, kept per block and added into
+//                the head's first-level totals
+//   2 per block: from the head totals, the bin d1 holding the K-th key and the
+//                rank left inside it; copy this block's bin-d1 keys (key,
+//                index) in index order (offset from the other blocks' bin-d1
+//                counts), count its keys above the bin, and add the histogram
+//                of the second digit of its bin-d1 keys into the head's
+//                second-level totals
+//   3 per block: from the second-level totals, the bin d2 of the K-th key;
+//                last radix pass over the bin-d1 keys with the prefix (d1, d2)
+//                -> threshold key T and how many keys equal to T are kept,
+//                lowest index first; the kept bin-d1 keys of every block ->
+//                this block's output offset; write its kept indices.  Block 0
+//                writes the sinks and the count.
+// The per-head steps inside kernels 2 and 3 are recomputed by every block of
+// the head from the same totals (cheaper than a one-workgroup-per-head launch).
 // ---------------------------------------------------------------------------
 constexpr int kBlk = 4096;                 // candidates per block
-constexpr int kStageCand = 8192;           // threshold-bin members staged in LDS
 constexpr int kBlkPer = kBlk / kSelThreads;
+constexpr int kBins1 = 4096;               // first digit: key >> 20
+constexpr int kBins2 = 2048;               // second digit: (key >> 9) & 2047
+constexpr int kStageMem = 16384;           // bin-d1 keys staged in LDS
+constexpr int kPreMem = 4;                 // ... of which kPreMem per thread loaded up front
+constexpr int kBatch = 8;                  // loads in flight per thread when reading global keys
 
-struct SelGeom {  // per-head geometry shared by the three kernels
+struct SelGeom {  // per-head geometry shared by the kernels
   int64_t c_lo, c_hi, ncand, nsink, K;
   int nb;         // blocks of this head
 };
@@ -154,10 +221,13 @@ __device__ __forceinline__ SelGeom sel_geom(const SelectArgs& a, int h) {
 
 // Scratch layout (per kv head, nbm = blocks for the longest head).
 struct SelWs {
-  uint32_t* hist;    // [Hkv][nbm][2048]
-  uint32_t* above;   // [Hkv][nbm]
-  uint32_t* head;    // [Hkv][8]: mode, d1, krem, cbin
-  uint32_t* ckey;    // [Hkv][n]
+  uint32_t* tot1;    // [Hkv][4096] head histogram of the first digit
+  uint32_t* tot2;    // [Hkv][2048] head histogram of the second digit of the bin-d1 keys
+  uint32_t* hist1;   // [Hkv][nbm][4096] block histograms of the first digit
+  uint32_t* above;   // [Hkv][nbm] keys above bin d1 per block
+  uint32_t* moff;    // [Hkv][nbm + 1] first bin-d1 key of each block in ckey; [nb] = all
+  uint32_t* head;    // [Hkv][8]: d1, rank left inside d1
+  uint32_t* ckey;    // [Hkv][n] bin-d1 keys, index order
   int32_t* cidx;     // [Hkv][n]
   int nbm;
 };
@@ -173,118 +243,119 @@ __host__ __device__ inline SelWs sel_ws(void* ws, int hkv, int64_t n) {
     p += (bytes + 255) / 256 * 256;
     return q;
   };
-  w.hist = (uint32_t*)take((size_t)hkv * w.nbm * 2048 * 4);
+  w.tot1 = (uint32_t*)take((size_t)hkv * (kBins1 + kBins2) * 4);  // tot1 and tot2: one clear
+  w.tot2 = w.tot1 + (size_t)hkv * kBins1;
+  w.hist1 = (uint32_t*)take((size_t)hkv * w.nbm * kBins1 * 4);
   w.above = (uint32_t*)take((size_t)hkv * w.nbm * 4);
+  w.moff = (uint32_t*)take((size_t)hkv * (w.nbm + 1) * 4);
   w.head = (uint32_t*)take((size_t)hkv * 8 * 4);
   w.ckey = (uint32_t*)take((size_t)hkv * n * 4);
   w.cidx = (int32_t*)take((size_t)hkv * n * 4);
   return w;
 }
 
-enum { kModeRadix = 0, kModeAll = 1, kModeNone = 2 };
+__device__ __forceinline__ bool sel_radix(const SelGeom& g) { return g.K > 0 && g.K < g.ncand; }
+
+// This block's candidates: thread t holds kBlkPer consecutive ones.
+__device__ __forceinline__ void load_block_scores(const SelectArgs& a, const SelGeom& g, int h, int b,
+                                                  float (&sv)[kBlkPer], int64_t& j0) {
+  const float* s = a.score + (int64_t)h * a.score_stride;
+  j0 = g.c_lo + (int64_t)b * kBlk + kBlkPer * threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kBlkPer; ++u) sv[u] = j0 + u < g.c_hi ? s[j0 + u] : 0.0f;
+}
+
+// Bin of the krem-th largest key of a histogram whose NB = PER * kSelThreads
+// bins are held PER per thread, thread t holding bins NB-1-PER t downwards
+// (c[0] the highest); -> sm_digit, sm_krem (the rank left inside that bin).
+template <int PER>
+__device__ __forceinline__ void pick_bin(const uint32_t (&c)[PER], uint32_t krem, uint32_t* sm_w,
+                                         uint32_t* sm_digit, uint32_t* sm_krem) {
+  const int top = PER * kSelThreads - 1 - PER * (int)threadIdx.x;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) mine += c[i];
+  uint32_t total;
+  uint32_t above = block_excl_scan(mine, sm_w, &total);
+  if (above < krem && krem <= above + mine) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (above < krem && krem <= above + c[i]) {
+        *sm_digit = (uint32_t)(top - i);
+        *sm_krem = krem - above;
+      }
+      above += c[i];
+    }
+  }
+  __syncthreads();
+}
 
 __global__ __launch_bounds__(kSelThreads) void sel_hist1_kernel(const SelectArgs a) {
-  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t hist[kBins1];
   const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
   const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
   const SelGeom g = sel_geom(a, h);
-  if (b >= g.nb) return;
-  const float* s = a.score + (int64_t)h * a.score_stride;
+  if (b >= g.nb || !sel_radix(g)) return;
   const int tid = threadIdx.x;
-  const int64_t j0 = g.c_lo + (int64_t)b * kBlk + kBlkPer * tid;  // this thread's candidates
   float sv[kBlkPer];
-#pragma unroll
-  for (int u = 0; u < kBlkPer; ++u) sv[u] = j0 + u < g.c_hi ? s[j0 + u] : 0.0f;
-  for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0u;
+  int64_t j0;
+  load_block_scores(a, g, h, b, sv, j0);
+  for (int i = tid; i < kBins1; i += kSelThreads) hist[i] = 0u;
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < kBlkPer; ++u)
-    if (j0 + u < g.c_hi) atomicAdd(&hist[score_key(sv[u]) >> 21], 1u);
+    if (j0 + u < g.c_hi) atomicAdd(&hist[score_key(sv[u]) >> 20], 1u);
   __syncthreads();
-  uint32_t* out = w.hist + ((int64_t)h * w.nbm + b) * kBins;
-  for (int i = tid; i < kBins; i += kSelThreads) out[i] = hist[i];
+  uint32_t* out = w.hist1 + ((int64_t)h * w.nbm + b) * kBins1;
+  uint32_t* t1 = w.tot1 + (int64_t)h * kBins1;
+  for (int i = tid; i < kBins1; i += kSelThreads) {
+    const uint32_t c = hist[i];
+    out[i] = c;
+    if (c) atomicAdd(&t1[i], c);
+  }
 }
 
 __global__ __launch_bounds__(kSelThreads) void sel_collect_kernel(const SelectArgs a) {
+  __shared__ uint32_t hist[kBins2];
   __shared__ uint32_t sm_w[kSelWaves + 1];
   __shared__ uint32_t sm_digit, sm_krem, sm_base;
   const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
   const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
   const SelGeom g = sel_geom(a, h);
-  if (b >= g.nb) return;
-  const float* s = a.score + (int64_t)h * a.score_stride;
+  if (b >= g.nb || !sel_radix(g)) return;
   const int tid = threadIdx.x;
-  const int64_t j0 = g.c_lo + (int64_t)b * kBlk + kBlkPer * tid;
   float sv[kBlkPer];
-#pragma unroll
-  for (int u = 0; u < kBlkPer; ++u) sv[u] = j0 + u < g.c_hi ? s[j0 + u] : 0.0f;
-  uint32_t* hd = w.head + (int64_t)h * 8;
-  if (b == 0) {
-    int32_t* out = a.idx + (int64_t)h * a.idx_stride;
-    for (int64_t i = tid; i < g.nsink; i += kSelThreads) out[i] = (int32_t)i;
-    if (tid == 0) a.count[h] = (int32_t)(g.nsink + g.K);
-  }
-  if (g.K == 0 || g.K == g.ncand) {  // nothing or everything: no radix passes
-    if (b == 0 && tid == 0) hd[0] = g.K == 0 ? kModeNone : kModeAll;
-    return;
-  }
-  // the top-11-bit bin of the K-th key, summed over the head's blocks
-  const uint32_t* hist = w.hist + (int64_t)h * w.nbm * kBins;
-  const int top = kBins - 1 - tid * 2;  // this thread's bins: top, top-1 (visited from the top)
-  uint32_t c0 = 0, c1 = 0;
-  // bins top - 1 and top are adjacent: one 8-byte load per block, eight
-  // blocks in flight per round
-  const uint2* hp = reinterpret_cast<const uint2*>(hist + top - 1);
-  int bb = 0;
-  for (; bb + 8 <= g.nb; bb += 8) {
-    uint2 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = hp[(int64_t)(bb + u) * (kBins / 2)];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      c0 += v[u].y;
-      c1 += v[u].x;
-    }
-  }
-  for (; bb < g.nb; ++bb) {
-    const uint2 v = hp[(int64_t)bb * (kBins / 2)];
-    c0 += v.y;
-    c1 += v.x;
-  }
-  uint32_t total;
-  const uint32_t krem = (uint32_t)g.K;
-  const uint32_t above_bins = block_excl_scan(c0 + c1, sm_w, &total);
-  if (above_bins < krem && krem <= above_bins + c0 + c1) {
-    if (krem <= above_bins + c0) {
-      sm_digit = (uint32_t)top;
-      sm_krem = krem - above_bins;
-    } else {
-      sm_digit = (uint32_t)(top - 1);
-      sm_krem = krem - above_bins - c0;
-    }
-  }
-  __syncthreads();
+  int64_t j0;
+  load_block_scores(a, g, h, b, sv, j0);
+  for (int i = tid; i < kBins2; i += kSelThreads) hist[i] = 0u;
+  // thread t holds first-level bins 4095 - 4t .. 4092 - 4t
+  const uint4 t1 = *reinterpret_cast<const uint4*>(w.tot1 + (int64_t)h * kBins1 + kBins1 - 4 - 4 * tid);
+  const uint32_t c1[4] = {t1.w, t1.z, t1.y, t1.x};
+  pick_bin<4>(c1, (uint32_t)g.K, sm_w, &sm_digit, &sm_krem);
   const uint32_t d1 = sm_digit;
-  // members of bin d1 in the blocks before this one
-  const uint32_t mine = tid < g.nb ? hist[(int64_t)tid * kBins + d1] : 0u;
-  uint32_t cbin;
-  const uint32_t off = block_excl_scan(mine, sm_w, &cbin);
+  // bin-d1 keys in the blocks before this one
+  const uint32_t* h1 = w.hist1 + (int64_t)h * w.nbm * kBins1;
+  const uint32_t mine = tid < g.nb ? h1[(int64_t)tid * kBins1 + d1] : 0u;
+  uint32_t cmem;
+  const uint32_t off = block_excl_scan(mine, sm_w, &cmem);
   if (tid == b) sm_base = off;
+  uint32_t* hd = w.head + (int64_t)h * 8;
+  uint32_t* mo = w.moff + (int64_t)h * (w.nbm + 1);
   if (b == 0 && tid == 0) {
-    hd[0] = kModeRadix;
-    hd[1] = d1;
-    hd[2] = sm_krem;
-    hd[3] = cbin;
+    hd[0] = d1;
+    hd[1] = sm_krem;
+    mo[g.nb] = cmem;
   }
   __syncthreads();
-  // candidates in the threshold bin (kept in index order) and above it
   uint32_t key[kBlkPer], n_in = 0, n_ab = 0;
 #pragma unroll
   for (int u = 0; u < kBlkPer; ++u) {
     const bool valid = j0 + u < g.c_hi;
     key[u] = score_key(sv[u]);
-    n_in += (valid && (key[u] >> 21) == d1) ? 1u : 0u;
-    n_ab += (valid && (key[u] >> 21) > d1) ? 1u : 0u;
+    const bool in = valid && (key[u] >> 20) == d1;
+    n_in += in ? 1u : 0u;
+    n_ab += (valid && (key[u] >> 20) > d1) ? 1u : 0u;
+    if (in) atomicAdd(&hist[(key[u] >> 9) & (uint32_t)(kBins2 - 1)], 1u);
   }
   uint32_t tot;  // counts <= kBlk < 2^16: both in one scan
   const uint32_t ex = block_excl_scan((n_in << 16) | n_ab, sm_w, &tot);
@@ -293,147 +364,149 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect_kernel(const SelectAr
   int32_t* ci = w.cidx + (int64_t)h * a.n;
 #pragma unroll
   for (int u = 0; u < kBlkPer; ++u) {
-    if (j0 + u < g.c_hi && (key[u] >> 21) == d1) {
+    if (j0 + u < g.c_hi && (key[u] >> 20) == d1) {
       ck[r] = key[u];
       ci[r] = (int32_t)(j0 + u);
       ++r;
     }
   }
-  if (tid == 0) w.above[(int64_t)h * w.nbm + b] = tot & 0xFFFFu;
+  if (tid == 0) {
+    w.above[(int64_t)h * w.nbm + b] = tot & 0xFFFFu;
+    mo[b] = sm_base;
+  }
+  // the block_excl_scan barriers ordered every histogram add before this
+  uint32_t* t2 = w.tot2 + (int64_t)h * kBins2;
+  for (int i = tid; i < kBins2; i += kSelThreads) {
+    const uint32_t c = hist[i];
+    if (c) atomicAdd(&t2[i], c);
+  }
 }
 
 __global__ __launch_bounds__(kSelThreads) void sel_write_kernel(const SelectArgs a) {
-  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t hist[kSelThreads];
   __shared__ uint32_t sm_w[kSelWaves + 1];
   __shared__ uint32_t sm_digit, sm_krem, sm_jt, sm_base;
   __shared__ uint32_t sm_kept[kSelThreads];
-  // bin members staged in LDS when they fit (the usual case): the passes
-  // below then read LDS instead of global memory
-  __shared__ uint32_t sm_ck[kStageCand];
-  __shared__ int32_t sm_ci[kStageCand];
+  __shared__ uint32_t sm_off[kSelThreads + 1];
+  __shared__ uint32_t sm_ck[kStageMem];  // bin-d1 keys when they fit (the usual case)
   const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
   const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
   const SelGeom g = sel_geom(a, h);
-  if (b >= g.nb) return;
+  if (b > 0 && b >= g.nb) return;
   const int tid = threadIdx.x;
-  const uint32_t* hd = w.head + (int64_t)h * 8;
-  const uint32_t* ck = w.ckey + (int64_t)h * a.n;
-  const int32_t* ci = w.cidx + (int64_t)h * a.n;
-  // every independent load in one round: this block's scores, head state, the
-  // blocks' counts above the bin, and (speculatively) the first kStageCand
-  // bin members
-  const float* s = a.score + (int64_t)h * a.score_stride;
-  const int64_t j0 = g.c_lo + (int64_t)b * kBlk + kBlkPer * tid;
-  float sv[kBlkPer];
-#pragma unroll
-  for (int u = 0; u < kBlkPer; ++u) sv[u] = j0 + u < g.c_hi ? s[j0 + u] : 0.0f;
-  constexpr int kPre = kStageCand / kSelThreads;
-  uint32_t pk[kPre];
-  int32_t pi[kPre];
-#pragma unroll
-  for (int u = 0; u < kPre; ++u) {  // rows hold n > kStageCand entries: in bounds
-    pk[u] = ck[tid * kPre + u];
-    pi[u] = ci[tid * kPre + u];
+  if (b == 0) {
+    int32_t* out = a.idx + (int64_t)h * a.idx_stride;
+    for (int64_t i = tid; i < g.nsink; i += kSelThreads) out[i] = (int32_t)i;
+    if (tid == 0) a.count[h] = (int32_t)(g.nsink + g.K);
   }
-  const uint32_t abv = tid < g.nb ? w.above[(int64_t)h * w.nbm + tid] : 0u;
-  const uint32_t mode = hd[0];
-  if (mode == kModeNone) return;  // uniform
+  if (b >= g.nb || g.K == 0) return;
+  const bool radix = g.K < g.ncand;
+  // every independent load in one round: this block's scores, head state, the
+  // blocks' counts and offsets, the second-level totals and (speculatively)
+  // the first kPreMem * kSelThreads bin-d1 keys
+  float sv[kBlkPer];
+  int64_t j0;
+  load_block_scores(a, g, h, b, sv, j0);
   uint32_t T = 0;
-  int64_t jt = INT64_MAX;  // every key >= T kept (mode all)
+  int64_t jt = INT64_MAX;  // every key >= T kept (all candidates)
   uint32_t base = (uint32_t)(g.nsink + (int64_t)b * kBlk);
-  if (mode == kModeRadix) {
-    const uint32_t d1h = hd[1], krem0 = hd[2], C = hd[3];
-    const bool staged = C <= (uint32_t)kStageCand;
+  if (radix) {
+    const uint32_t* hd = w.head + (int64_t)h * 8;
+    const uint32_t* mo = w.moff + (int64_t)h * (w.nbm + 1);
+    const uint32_t* ck = w.ckey + (int64_t)h * a.n;
+    const int32_t* ci = w.cidx + (int64_t)h * a.n;
+    uint32_t pk[kPreMem];
+#pragma unroll
+    for (int u = 0; u < kPreMem; ++u) pk[u] = ck[u * kSelThreads + tid];  // rows hold n > 4096 entries
+    const uint32_t abv = tid < g.nb ? w.above[(int64_t)h * w.nbm + tid] : 0u;
+    const uint32_t moff = tid < g.nb ? mo[tid] : 0u;
+    const uint32_t C = mo[g.nb];  // bin-d1 keys of the head
+    const uint2 t2 = *reinterpret_cast<const uint2*>(w.tot2 + (int64_t)h * kBins2 + kBins2 - 2 - 2 * tid);
+    const uint32_t d1 = hd[0], krem1 = hd[1];
+    if (tid < g.nb) sm_off[tid] = moff;
+    if (tid == 0) sm_off[g.nb] = C;
+    hist[tid] = 0u;
+    sm_kept[tid] = 0u;
+    if (tid == 0) sm_jt = 0xFFFFFFFFu;
+    const uint32_t c2[2] = {t2.y, t2.x};
+    pick_bin<2>(c2, krem1, sm_w, &sm_digit, &sm_krem);  // (its barriers publish the above)
+    const uint32_t P2 = (d1 << 11) | sm_digit;  // key >> 9 of the threshold
+    const uint32_t krem = sm_krem;
+    const bool staged = C <= (uint32_t)kStageMem;
     if (staged) {
 #pragma unroll
-      for (int u = 0; u < kPre; ++u) {
-        sm_ck[tid * kPre + u] = pk[u];
-        sm_ci[tid * kPre + u] = pi[u];
+      for (int u = 0; u < kPreMem; ++u) sm_ck[u * kSelThreads + tid] = pk[u];
+      for (uint32_t i0 = kPreMem * kSelThreads; i0 < C; i0 += kBatch * kSelThreads) {
+        uint32_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const uint32_t i = i0 + u * kSelThreads + tid;
+          v[u] = i < C ? ck[i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const uint32_t i = i0 + u * kSelThreads + tid;
+          if (i < C) sm_ck[i] = v[u];
+        }
       }
       __syncthreads();
       ck = sm_ck;
-      ci = sm_ci;
     }
-    uint32_t prefix = d1h << 21, mask = 0xFFE00000u;
-    uint32_t krem = krem0;
-#pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
-      const int shift = pass == 0 ? 10 : 0;
-      const int nb = pass == 0 ? 2048 : 1024;
-      for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0u;
-      __syncthreads();
-      for (uint32_t i = tid; i < C; i += kSelThreads) {
-        const uint32_t key = ck[i];
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+    // last radix pass: bits [8:0] of the bin-d1 keys with prefix P2
+    for (uint32_t i0 = 0; i0 < C; i0 += kBatch * kSelThreads) {
+      uint32_t v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t i = i0 + u * kSelThreads + tid;
+        v[u] = i < C ? ck[i] : 0u;
       }
-      __syncthreads();
-      const int per = nb / kSelThreads;
-      const int top = nb - 1 - tid * per;
-      uint32_t mine = 0;
-      for (int i = 0; i < per; ++i) mine += hist[top - i];
-      uint32_t total;
-      uint32_t above = block_excl_scan(mine, sm_w, &total);
-      if (above < krem && krem <= above + mine) {
-        for (int i = 0; i < per; ++i) {
-          const uint32_t cb = hist[top - i];
-          if (krem <= above + cb) {
-            sm_digit = (uint32_t)(top - i);
-            sm_krem = krem - above;
-            break;
-          }
-          above += cb;
-        }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t i = i0 + u * kSelThreads + tid;
+        if (i < C && (v[u] >> 9) == P2) atomicAdd(&hist[v[u] & 511u], 1u);
       }
-      __syncthreads();
-      prefix |= sm_digit << shift;
-      mask |= (uint32_t)(nb - 1) << shift;
-      krem = sm_krem;
-      __syncthreads();
     }
-    T = prefix;
-    const uint32_t take = krem;
-    // bin members in index order: the first `take` equal to T are kept;
-    // count the kept members of every block
-    sm_kept[tid] = 0u;
-    if (tid == 0) sm_jt = 0xFFFFFFFFu;
     __syncthreads();
-    auto keep_member = [&](uint32_t i, uint32_t key, uint32_t eq_rank) {
-      const bool eq = key == T;
-      if (key > T || (eq && eq_rank < take)) {
-        const int32_t j = ci[i];
-        atomicAdd(&sm_kept[(j - g.c_lo) / kBlk], 1u);
-        if (eq && eq_rank == take - 1) sm_jt = (uint32_t)j;
+    {
+      const uint32_t c3[1] = {hist[kSelThreads - 1 - tid]};  // bins >= 512 stay empty
+      pick_bin<1>(c3, krem, sm_w, &sm_digit, &sm_krem);
+    }
+    T = (P2 << 9) | sm_digit;
+    const uint32_t take = sm_krem;
+    // bin-d1 keys in index order: every key > T and the first `take` equal to
+    // T are kept.  Thread t walks the run [t R, t R + R); the kept count of the
+    // block holding the run's keys is flushed whenever the run crosses into
+    // the next block.
+    const uint32_t R = (C + kSelThreads - 1) / kSelThreads;
+    const uint32_t i0 = (uint32_t)tid * R;
+    const uint32_t i1 = i0 + R < C ? i0 + R : C;
+    uint32_t n_eq = 0;
+    for (uint32_t i = i0; i < i1; ++i) n_eq += ck[i] == T ? 1u : 0u;
+    uint32_t tot_eq;
+    uint32_t eq_rank = block_excl_scan(n_eq, sm_w, &tot_eq);
+    if (i0 < i1) {
+      int lo = 0, hi = g.nb - 1;  // block of key i0: the last with sm_off[blk] <= i0
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sm_off[mid] <= i0) lo = mid; else hi = mid - 1;
       }
-    };
-    if (staged) {
-      // kPre consecutive members per thread: one scan ranks the equal keys
-      const uint32_t i0 = (uint32_t)tid * kPre;
-      uint32_t n_eq = 0;
-#pragma unroll
-      for (int u = 0; u < kPre; ++u) n_eq += (i0 + u < C && ck[i0 + u] == T) ? 1u : 0u;
-      uint32_t tot_eq;
-      uint32_t eq_rank = block_excl_scan(n_eq, sm_w, &tot_eq);
-#pragma unroll
-      for (int u = 0; u < kPre; ++u) {
-        const uint32_t i = i0 + u;
-        if (i < C) {
-          const uint32_t key = ck[i];
-          keep_member(i, key, eq_rank);
-          eq_rank += key == T ? 1u : 0u;
+      int blk = lo;
+      uint32_t kept = 0;
+      for (uint32_t i = i0; i < i1; ++i) {
+        while (i >= sm_off[blk + 1]) {  // the run crosses a block border
+          if (kept) atomicAdd(&sm_kept[blk], kept);
+          kept = 0;
+          ++blk;
         }
+        const uint32_t key = ck[i];
+        const bool eq = key == T;
+        if (key > T || (eq && eq_rank < take)) {
+          ++kept;
+          if (eq && eq_rank == take - 1) sm_jt = (uint32_t)ci[i];
+        }
+        eq_rank += eq ? 1u : 0u;
       }
-    } else {
-      uint32_t eq_seen = 0;
-#pragma unroll 1
-      for (uint32_t t0 = 0; t0 < C; t0 += kSelThreads) {
-        const uint32_t i = t0 + tid;
-        const bool valid = i < C;
-        const uint32_t key = valid ? ck[i] : 0u;
-        uint32_t n_eq;
-        const uint32_t eq_rank = eq_seen + block_flag_rank(valid && key == T, sm_w, &n_eq);
-        if (valid) keep_member(i, key, eq_rank);
-        eq_seen += n_eq;
-      }
+      if (kept) atomicAdd(&sm_kept[blk], kept);
     }
     __syncthreads();
     // this block's output offset: sinks, then the kept keys of earlier blocks
@@ -483,10 +556,17 @@ size_t select_ws_bytes(int32_t n_kv_heads, int64_t n) {
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   if (!use_block_path(a.n_kv_heads, a.n)) {
-    hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.n_kv_heads), dim3(kSelThreads), 0, stream, a);
+    const int64_t ncand = a.n - a.n_sink - a.n_recent;
+    if (ncand > kStageFrom)
+      hipLaunchKernelGGL(select_kernel<true>, dim3((unsigned)a.n_kv_heads), dim3(kSelThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(select_kernel<false>, dim3((unsigned)a.n_kv_heads), dim3(kSelThreads), 0, stream, a);
     return hipGetLastError();
   }
   const unsigned grid_b = (unsigned)(a.n_kv_heads * sel_blocks_max(a.n));
+  const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
+  hipError_t e = launch_zero_u32(w.tot1, (int64_t)a.n_kv_heads * (kBins1 + kBins2), stream);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sel_hist1_kernel, dim3(grid_b), dim3(kSelThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_collect_kernel, dim3(grid_b), dim3(kSelThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_write_kernel, dim3(grid_b), dim3(kSelThreads), 0, stream, a);

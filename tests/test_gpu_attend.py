@@ -174,7 +174,8 @@ def test_select_block_path_ties_and_budget_edges(n):
     check_select(s, S, R, 0, k_per_head=ks, k_max=ncand)
 
 
-@pytest.mark.parametrize("hkv,n,K", [(1, 20000, 5000), (2, 65536, 1), (8, 32768, 9762), (63, 17000, 3000)])
+@pytest.mark.parametrize("hkv,n,K", [(1, 20000, 5000), (2, 65536, 1), (8, 32768, 9762), (63, 17000, 3000),
+                                     (1, 4194304, 100000)])
 def test_select_block_path_uniform_k(hkv, n, K):
     banner(f"select block path hkv={hkv} n={n} K={K}")
     rng = np.random.default_rng(hkv * n)
@@ -184,7 +185,9 @@ def test_select_block_path_uniform_k(hkv, n, K):
 
 
 @pytest.mark.parametrize("hkv,n,S,R,K", [(8, 2048, 4, 32, 256), (3, 5000, 4, 64, 1000), (2, 700, 0, 32, 650),
-                                          (4, 100, 4, 8, 0), (2, 100, 4, 8, 500), (1, 32768, 4, 64, 9762)])
+                                          (4, 100, 4, 8, 0), (2, 100, 4, 8, 500), (1, 32768, 4, 64, 9762),
+                                          (8, 16384, 0, 0, 100), (64, 16452, 4, 64, 7000),
+                                          (64, 20000, 4, 64, 5000)])
 def test_select_bit_exact_on_oracle_scores(hkv, n, S, R, K):
     banner(f"select hkv={hkv} n={n} S={S} R={R} K={K}")
     rng = np.random.default_rng(n + K)
