@@ -35,9 +35,10 @@
  *   - Scratch: a caller-provided device workspace of at least
  *     skv_workspace_size() bytes, 256-byte aligned, holding split-K partials
  *     and other per-call intermediates (its first SKV_WS_HEADER_BYTES are
- *     reserved; skv_workspace_init zero-fills them).  Two calls that share
- *     one workspace must not overlap in time (same stream, or ordered by
- *     events); nothing in it needs to survive between calls.
+ *     reserved; skv_workspace_init zero-fills them, and every call leaves
+ *     them zero).  Two calls that share one workspace must not overlap in
+ *     time (same stream, or ordered by events); apart from the zero header,
+ *     nothing in it needs to survive between calls.
  *   - Streams: every call only enqueues work on `stream` (a hipStream_t; NULL
  *     is the null stream) and returns without synchronising.
  *   - Errors: arguments are validated on the host before anything is
@@ -71,7 +72,7 @@ typedef enum {
 
 typedef enum { SKV_F32 = 0, SKV_BF16 = 1 } skv_dtype;
 
-#define SKV_WS_HEADER_BYTES 65536
+#define SKV_WS_HEADER_BYTES 1048576
 
 typedef struct {
   int32_t n_q_heads;      /* Hq (layers x heads may be flattened into heads)     */
@@ -115,7 +116,11 @@ skv_status skv_score(const skv_problem* p, const void* q, int32_t n_obs, const v
  * (-0.0 equals +0.0).  Writes idx[h * idx_stride + i], i < count[h], the sinks
  * and kept candidates in ascending order, and count[h] = #sinks + K_h.
  * k_per_head is a device array or NULL; k_max (host) bounds every K_h and
- * idx_stride >= n_sink + k_max.  Scores must be finite. */
+ * idx_stride >= n_sink + k_max.  Scores must be finite.
+ * Long rows with few kv heads (n > 16384, n_kv_heads < 64) keep running
+ * histogram totals in the workspace header: it must be zero when the call
+ * starts (skv_workspace_init once after allocating the workspace; the call
+ * leaves it zero again). */
 skv_status skv_select(const skv_problem* p, const float* score, int64_t score_stride,
                       int64_t n, int32_t n_sink, int32_t n_recent,
                       const int32_t* k_per_head, int32_t k_uniform, int32_t k_max,

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libsparsekv.so")
 
 SKV_OK, SKV_ERR_INVALID_ARG, SKV_ERR_UNSUPPORTED, SKV_ERR_WORKSPACE, SKV_ERR_HIP = range(5)
 SKV_F32, SKV_BF16 = 0, 1
-SKV_WS_HEADER_BYTES = 65536
+SKV_WS_HEADER_BYTES = 1048576
 _ALIGN = 256
 
 _lib = None
@@ -133,7 +133,8 @@ def skv_workspace_size(p: Problem, n_max: int, rows_max: int = 1) -> int:
 
 class Workspace:
     """Device scratch for libsparsekv calls (torch-allocated, 256-byte aligned,
-    counters zeroed once).  Calls sharing it must be ordered on one stream."""
+    reserved header zeroed once; every call leaves it zero).  Calls sharing it
+    must be ordered on one stream."""
 
     def __init__(self, nbytes: int, device=None, stream=None):
         torch = _torch()

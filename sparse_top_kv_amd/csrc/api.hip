@@ -463,6 +463,7 @@ skv_status skv_select(const skv_problem* p, const float* score, int64_t score_st
   if (sel_ws > 0 && (st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + sel_ws)) != SKV_OK) return st;
   skv::SelectArgs a{};
   a.ws = sel_ws > 0 ? (char*)ws + SKV_WS_HEADER_BYTES : nullptr;
+  a.totals = sel_ws > 0 ? (uint32_t*)ws : nullptr;  // the reserved header
   a.score = score;
   a.score_stride = score_stride;
   a.n = n;

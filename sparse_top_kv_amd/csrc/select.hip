@@ -17,6 +17,7 @@
 #include "skv_common.h"
 #include "skv_kernels.h"
 #include "skv_block.h"
+#include "../../include/sparsekv.h"
 
 namespace skv {
 namespace {
@@ -172,9 +173,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
 // head select would leave most CUs idle).  Candidates are cut into blocks of
 // kBlk.  Radix digits: key bits [31:20] (4096 bins), [19:9] (2048), [8:0]
 // (512).  Integer histogram totals are the only global atomics, so the result
-// is identical run to run.  A clear kernel zeroes the head totals, then:
+// is identical run to run.  The first-level totals live in memory that is
+// zero on entry and is left zero (kernel 3 clears them after their last
+// reader); kernel 1 clears the second-level totals:
 //   1 per block: histogram of the first digit, kept per block and added into
-//                the head's first-level totals
+//                the head's first-level totals; block 0 clears the head's
+//                second-level totals
 //   2 per block: from the head totals, the bin d1 holding the K-th key and the
 //                rank left inside it; copy this block's bin-d1 keys (key,
 //                index) in index order (offset from the other blocks' bin-d1
@@ -186,7 +190,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
 //                -> threshold key T and how many keys equal to T are kept,
 //                lowest index first; the kept bin-d1 keys of every block ->
 //                this block's output offset; write its kept indices.  Block 0
-//                writes the sinks and the count.
+//                writes the sinks and the count and clears the first-level
+//                totals.
 // The per-head steps inside kernels 2 and 3 are recomputed by every block of
 // the head from the same totals (cheaper than a one-workgroup-per-head launch).
 // ---------------------------------------------------------------------------
@@ -221,7 +226,7 @@ __device__ __forceinline__ SelGeom sel_geom(const SelectArgs& a, int h) {
 
 // Scratch layout (per kv head, nbm = blocks for the longest head).
 struct SelWs {
-  uint32_t* tot1;    // [Hkv][4096] head histogram of the first digit
+  uint32_t* tot1;    // [Hkv][4096] head histogram of the first digit (SelectArgs::totals, zero on entry)
   uint32_t* tot2;    // [Hkv][2048] head histogram of the second digit of the bin-d1 keys
   uint32_t* hist1;   // [Hkv][nbm][4096] block histograms of the first digit
   uint32_t* above;   // [Hkv][nbm] keys above bin d1 per block
@@ -234,7 +239,7 @@ struct SelWs {
 
 __host__ __device__ inline int sel_blocks_max(int64_t n) { return (int)((n + kBlk - 1) / kBlk); }
 
-__host__ __device__ inline SelWs sel_ws(void* ws, int hkv, int64_t n) {
+__host__ __device__ inline SelWs sel_ws(void* ws, uint32_t* totals, int hkv, int64_t n) {
   SelWs w;
   w.nbm = sel_blocks_max(n);
   char* p = (char*)ws;
@@ -243,8 +248,8 @@ __host__ __device__ inline SelWs sel_ws(void* ws, int hkv, int64_t n) {
     p += (bytes + 255) / 256 * 256;
     return q;
   };
-  w.tot1 = (uint32_t*)take((size_t)hkv * (kBins1 + kBins2) * 4);  // tot1 and tot2: one clear
-  w.tot2 = w.tot1 + (size_t)hkv * kBins1;
+  w.tot1 = totals;
+  w.tot2 = (uint32_t*)take((size_t)hkv * kBins2 * 4);
   w.hist1 = (uint32_t*)take((size_t)hkv * w.nbm * kBins1 * 4);
   w.above = (uint32_t*)take((size_t)hkv * w.nbm * 4);
   w.moff = (uint32_t*)take((size_t)hkv * (w.nbm + 1) * 4);
@@ -275,6 +280,10 @@ __device__ __forceinline__ void pick_bin(const uint32_t (&c)[PER], uint32_t krem
   uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) mine += c[i];
+  if (threadIdx.x == 0) {  // in range whatever the counts hold
+    *sm_digit = 0u;
+    *sm_krem = 1u;
+  }
   uint32_t total;
   uint32_t above = block_excl_scan(mine, sm_w, &total);
   if (above < krem && krem <= above + mine) {
@@ -292,7 +301,7 @@ __device__ __forceinline__ void pick_bin(const uint32_t (&c)[PER], uint32_t krem
 
 __global__ __launch_bounds__(kSelThreads) void sel_hist1_kernel(const SelectArgs a) {
   __shared__ uint32_t hist[kBins1];
-  const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
+  const SelWs w = sel_ws(a.ws, a.totals, a.n_kv_heads, a.n);
   const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
   const SelGeom g = sel_geom(a, h);
   if (b >= g.nb || !sel_radix(g)) return;
@@ -301,6 +310,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist1_kernel(const SelectArgs
   int64_t j0;
   load_block_scores(a, g, h, b, sv, j0);
   for (int i = tid; i < kBins1; i += kSelThreads) hist[i] = 0u;
+  if (b == 0)
+    for (int i = tid; i < kBins2; i += kSelThreads) w.tot2[(int64_t)h * kBins2 + i] = 0u;
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < kBlkPer; ++u)
@@ -319,7 +330,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect_kernel(const SelectAr
   __shared__ uint32_t hist[kBins2];
   __shared__ uint32_t sm_w[kSelWaves + 1];
   __shared__ uint32_t sm_digit, sm_krem, sm_base;
-  const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
+  const SelWs w = sel_ws(a.ws, a.totals, a.n_kv_heads, a.n);
   const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
   const SelGeom g = sel_geom(a, h);
   if (b >= g.nb || !sel_radix(g)) return;
@@ -389,7 +400,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_write_kernel(const SelectArgs
   __shared__ uint32_t sm_kept[kSelThreads];
   __shared__ uint32_t sm_off[kSelThreads + 1];
   __shared__ uint32_t sm_ck[kStageMem];  // bin-d1 keys when they fit (the usual case)
-  const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
+  const SelWs w = sel_ws(a.ws, a.totals, a.n_kv_heads, a.n);
   const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
   const SelGeom g = sel_geom(a, h);
   if (b > 0 && b >= g.nb) return;
@@ -398,6 +409,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_write_kernel(const SelectArgs
     int32_t* out = a.idx + (int64_t)h * a.idx_stride;
     for (int64_t i = tid; i < g.nsink; i += kSelThreads) out[i] = (int32_t)i;
     if (tid == 0) a.count[h] = (int32_t)(g.nsink + g.K);
+    if (sel_radix(g))  // the previous kernel was the last reader of the first-level totals
+      for (int i = tid; i < kBins1; i += kSelThreads) w.tot1[(int64_t)h * kBins1 + i] = 0u;
   }
   if (b >= g.nb || g.K == 0) return;
   const bool radix = g.K < g.ncand;
@@ -548,9 +561,12 @@ bool use_block_path(int32_t hkv, int64_t n) {
 
 }  // namespace
 
+static_assert((size_t)63 * kBins1 * 4 <= SKV_WS_HEADER_BYTES,
+              "the block path's head totals fit the reserved workspace header");
+
 size_t select_ws_bytes(int32_t n_kv_heads, int64_t n) {
   if (!use_block_path(n_kv_heads, n)) return 0;
-  const SelWs w = sel_ws(nullptr, n_kv_heads, n);
+  const SelWs w = sel_ws(nullptr, nullptr, n_kv_heads, n);
   return (size_t)((char*)(w.cidx + (int64_t)n_kv_heads * n) - (char*)nullptr) + 256;
 }
 
@@ -564,9 +580,6 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const unsigned grid_b = (unsigned)(a.n_kv_heads * sel_blocks_max(a.n));
-  const SelWs w = sel_ws(a.ws, a.n_kv_heads, a.n);
-  hipError_t e = launch_zero_u32(w.tot1, (int64_t)a.n_kv_heads * (kBins1 + kBins2), stream);
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sel_hist1_kernel, dim3(grid_b), dim3(kSelThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_collect_kernel, dim3(grid_b), dim3(kSelThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_write_kernel, dim3(grid_b), dim3(kSelThreads), 0, stream, a);

@@ -123,6 +123,7 @@ struct SelectArgs {
   int32_t* count;
   int32_t n_kv_heads;
   void* ws;                   // scratch of the block-parallel path (select_ws_bytes)
+  uint32_t* totals;           // block path: first-level head totals, zero on entry, left zero
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 // Scratch the block-parallel select needs (0 when the one-workgroup-per-head

@@ -184,6 +184,29 @@ def test_select_block_path_uniform_k(hkv, n, K):
     check_select(s, 4, 64, K)
 
 
+def test_select_block_path_leaves_header_zero():
+    """The block path keeps head totals in the workspace header: two calls in a
+    row on one workspace (different scores and K) both match the oracle, and
+    the header reads zero after each."""
+    banner("select block path header")
+    hkv, n, S, R = 8, 70000, 4, 64
+    ws = select_ws(hkv, n)
+    hdr = ws.tensor[:skv.SKV_WS_HEADER_BYTES]
+    rng = np.random.default_rng(11)
+    for K in (20000, 3000):
+        s = rng.standard_normal((hkv, n)).astype(np.float32)
+        ref_idx, ref_cnt = oracle.select(s, S, R, K)
+        idx = torch.full((hkv, S + K), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros(hkv, dtype=torch.int32, device="cuda")
+        skv.skv_select(dev(s), n, S, R, K, idx, cnt, ws)
+        torch.cuda.synchronize()
+        gi, gc = host(idx), host(cnt)
+        assert np.array_equal(gc, ref_cnt)
+        for h in range(hkv):
+            assert np.array_equal(gi[h, :gc[h]], ref_idx[h, :ref_cnt[h]])
+        assert int(torch.count_nonzero(hdr)) == 0
+
+
 @pytest.mark.parametrize("hkv,n,S,R,K", [(8, 2048, 4, 32, 256), (3, 5000, 4, 64, 1000), (2, 700, 0, 32, 650),
                                           (4, 100, 4, 8, 0), (2, 100, 4, 8, 500), (1, 32768, 4, 64, 9762),
                                           (8, 16384, 0, 0, 100), (64, 16452, 4, 64, 7000),
