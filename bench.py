@@ -30,6 +30,9 @@ gamma=5 verify), the SpecVLM selection on it (top-P 0.5 + uniform fill to
 10 % of the video tokens) and the round over that set, sweeps of the round
 over gamma = 1..13 and over K (measured vs I/O-model break-even acceptance), one-time selection costs, and the byte-count speedup bounds.
 `--sections all` adds the 1024-head SparseMM batched step (17 GB of cache).
+`--sections mfma` and `--sections hbm` are profiling modes (no bench line): the
+Qwen2-7B matrix-core calls, and three eager calls of each streaming kernel at
+32K and 128K, for runs under rocprofv3 counters.
 
 cpu_baseline: the fp64 oracle (test infrastructure) timed on this host on a
 bounded sample of the headline step.
@@ -66,7 +69,8 @@ def parse():
     ap.add_argument("--blocks", type=int, default=5, help="timed blocks (median reported)")
     ap.add_argument("--sections", default="default",
                     help="headline | default | all | mfma (profiling: only the Qwen2-7B matrix-core "
-                         "calls, no bench line)")
+                         "calls, no bench line) | hbm (profiling: three eager calls of each "
+                         "streaming kernel at 32K and 128K, no bench line)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 512 MiB device copy (counter calibration under a profiler)")
@@ -217,6 +221,58 @@ def main():
                              graph=False)
         print(json.dumps({"sections": "mfma", "text_window_score_us": round(sc_us, 1),
                           "verify_us": round(v_us, 2)}), flush=True)
+        return
+
+    if args.sections == "hbm":
+        # profiling mode for HBM counter runs: each call three times, eagerly, in
+        # a fixed order (32K: window score, select, gather, sparse and dense
+        # step; 128K: per-step score, select, sparse and dense step)
+        out_t = {}
+
+        def timed(name, fn, reps=3):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out_t[name] = round(e0.elapsed_time(e1) * 1000.0 / reps, 2)
+
+        w = synth.llama_obs(layer=0)
+        q, qo, k, v = dev(w.q), dev(w.q_obs), dev(w.k), dev(w.v)
+        n, S, R, K = w.n, w.n_sink, w.n_recent, w.k_top
+        hq, hkv, d = w.n_q_heads, w.n_kv_heads, w.head_dim
+        ws = skv.Workspace.for_problem(skv.problem_for(qo, k), 131072, 512)
+        sc = torch.empty((hkv, n), device="cuda")
+        idx = torch.empty((hkv, S + K), dtype=torch.int32, device="cuda")
+        cnt = torch.empty(hkv, dtype=torch.int32, device="cuda")
+        out = torch.empty((hq, d), device="cuda")
+        lse = torch.empty(hq, device="cuda")
+        kc = torch.empty((hkv, S + K + R, d), dtype=torch.bfloat16, device="cuda")
+        vc = torch.empty_like(kc)
+        timed("32k_window_score", lambda: skv.skv_score(qo, k, n, sc, ws))
+        timed("32k_select", lambda: skv.skv_select(sc, n, S, R, K, idx, cnt, ws))
+        timed("32k_gather", lambda: skv.skv_gather(k, v, n, idx, cnt, n - R, kc, vc))
+        timed("32k_sparse_step", lambda: skv.skv_attend_sparse(q, k, v, n, idx, cnt, n - R, out, lse, ws))
+        timed("32k_dense_step", lambda: skv.skv_attend_dense(q, k, v, n, out, lse, ws))
+        del k, v, kc, vc
+        w3 = synth.llama_needle(layer=0)
+        q3, k3, v3 = dev(w3.q), dev(w3.k), dev(w3.v)
+        n3, K3 = w3.n, w3.k_top
+        sc3 = torch.empty((hkv, n3), device="cuda")
+        idx3 = torch.empty((hkv, S + K3), dtype=torch.int32, device="cuda")
+        timed("128k_step_score", lambda: skv.skv_score(q3, k3, n3, sc3, ws))
+        timed("128k_select", lambda: skv.skv_select(sc3, n3, S, R, K3, idx3, cnt, ws))
+        timed("128k_sparse_step", lambda: skv.skv_attend_sparse(q3, k3, v3, n3, idx3, cnt, n3 - R, out, lse, ws))
+        timed("128k_dense_step", lambda: skv.skv_attend_dense(q3, k3, v3, n3, out, lse, ws))
+        if args.calib_copy:  # known traffic for the counters' scale: 512 MiB read, 512 MiB written
+            src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps({"sections": "hbm", "eager_us": out_t}), flush=True)
         return
 
     # ------------------------------------------------------------------
