@@ -172,6 +172,140 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
 
 
 // ---------------------------------------------------------------------------
+// Short rows (at most kSmallMax candidates): one four-wave workgroup per kv
+// head.  Thread t holds the run of candidates [t P, t P + P) as keys in
+// registers, loaded once.  Each radix pass takes three barriers: histogram
+// complete, scan totals, digit chosen (the other of two histogram buffers is
+// cleared in the same step); the compaction is one scan of the (equal, above)
+// counts of every run.  The 1024-thread kernel spends most of a short row's
+// time in its workgroup barriers (2K candidates: 8.6 us).
+// ---------------------------------------------------------------------------
+constexpr int kSmallThreads = 256;
+constexpr int kSmallWaves = kSmallThreads / 64;
+constexpr int kSmallPer = 16;
+constexpr int kSmallMax = kSmallThreads * kSmallPer;
+
+// Exclusive prefix sum of one value per thread over the workgroup; sm_w holds
+// kSmallWaves words that no other call touches before the next barrier.
+__device__ __forceinline__ uint32_t small_excl_scan(uint32_t v, uint32_t* sm_w, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t x = wave_incl_scan(v);
+  if (lane == 63) sm_w[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kSmallWaves; ++w) {
+    const uint32_t c = sm_w[w];
+    before += w < wave ? c : 0u;
+    all += c;
+  }
+  *total = all;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kSmallThreads) void select_small_kernel(const SelectArgs a) {
+  __shared__ uint32_t hist[2][kBins];
+  __shared__ uint32_t sm_w[4][kSmallWaves];
+  __shared__ uint32_t sm_digit[3], sm_krem[3];
+
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x;
+  const float* s = a.score + (int64_t)h * a.score_stride;
+  int32_t* out = a.idx + (int64_t)h * a.idx_stride;
+  const int64_t n = a.n;
+  const int64_t tail = n - a.n_recent > 0 ? n - a.n_recent : 0;
+  const int64_t nsink = a.n_sink < tail ? a.n_sink : tail;
+  const int64_t c_lo = a.n_sink, c_hi = n - a.n_recent;
+  const int ncand = c_lo < c_hi ? (int)(c_hi - c_lo) : 0;  // <= kSmallMax
+  int64_t K = a.k_per_head ? a.k_per_head[h] : a.k_uniform;
+  K = K < 0 ? 0 : K;
+  K = K > ncand ? ncand : K;
+  K = K > a.k_max ? a.k_max : K;  // never write past the index row
+
+  for (int64_t i = tid; i < nsink; i += kSmallThreads) out[i] = (int32_t)i;
+  if (tid == 0) a.count[h] = (int32_t)(nsink + K);
+  if (K == 0) return;
+  if (K == ncand) {
+    for (int64_t i = tid; i < K; i += kSmallThreads) out[nsink + i] = (int32_t)(c_lo + i);
+    return;
+  }
+
+  const int P = (ncand + kSmallThreads - 1) / kSmallThreads;
+  const int i0 = tid * P;
+  const int nv = ncand - i0 < 0 ? 0 : (ncand - i0 > P ? P : ncand - i0);  // keys of this run
+  uint32_t key[kSmallPer];
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u) key[u] = u < nv ? score_key(s[c_lo + i0 + u]) : 0u;
+  for (int b = tid; b < kBins; b += kSmallThreads) hist[0][b] = 0u;
+  __syncthreads();
+
+  // ---- radix passes: digits [31:21], [20:10], [9:0] ----------------------
+  uint32_t prefix = 0, mask = 0;
+  uint32_t krem = (uint32_t)K;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 2 ? 1024 : 2048;
+    uint32_t* H = hist[pass & 1];
+#pragma unroll
+    for (int u = 0; u < kSmallPer; ++u)
+      if (u < nv && (key[u] & mask) == prefix) atomicAdd(&H[(key[u] >> shift) & (uint32_t)(nb - 1)], 1u);
+    __syncthreads();
+    // thread t owns nb / 256 consecutive bins, visited from the top
+    const int per = nb / kSmallThreads;
+    const int top = nb - 1 - tid * per;
+    uint32_t mine = 0;
+    for (int i = 0; i < per; ++i) mine += H[top - i];
+    uint32_t total;
+    uint32_t above = small_excl_scan(mine, sm_w[pass], &total);
+    if (above < krem && krem <= above + mine) {
+      for (int i = 0; i < per; ++i) {
+        const uint32_t cb = H[top - i];
+        if (krem <= above + cb) {
+          sm_digit[pass] = (uint32_t)(top - i);
+          sm_krem[pass] = krem - above;
+          break;
+        }
+        above += cb;
+      }
+    }
+    if (pass < 2)  // the other buffer was last read before the previous pass's last barrier
+      for (int b = tid; b < kBins; b += kSmallThreads) hist[(pass + 1) & 1][b] = 0u;
+    __syncthreads();
+    prefix |= sm_digit[pass] << shift;
+    mask |= (uint32_t)(nb - 1) << shift;
+    krem = sm_krem[pass];
+  }
+  const uint32_t T = prefix;
+  const uint32_t take = krem;  // keys equal to T to keep, lowest index first
+  const uint32_t limit = (uint32_t)(nsink + K);
+
+  // ---- compaction in index order: one scan of (equal, above) per run ------
+  uint32_t n_eq = 0, n_gt = 0;
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u) {
+    n_eq += (u < nv && key[u] == T) ? 1u : 0u;
+    n_gt += (u < nv && key[u] > T) ? 1u : 0u;
+  }
+  uint32_t tot;  // counts <= kSmallMax < 2^16: both in one scan
+  const uint32_t ex = small_excl_scan((n_eq << 16) | n_gt, sm_w[3], &tot);
+  uint32_t eq_rank = ex >> 16;
+  uint32_t pos = (uint32_t)nsink + (ex & 0xFFFFu) + (eq_rank < take ? eq_rank : take);
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u) {
+    if (u < nv) {
+      const bool eq = key[u] == T;
+      if (key[u] > T || (eq && eq_rank < take)) {
+        if (pos < limit) out[pos] = (int32_t)(c_lo + i0 + u);  // never past the row
+        ++pos;
+      }
+      eq_rank += eq ? 1u : 0u;
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
 // Block-parallel path for long caches with few kv heads (a one-workgroup-per-
 // head select would leave most CUs idle).  Candidates are cut into blocks of
 // kBlk.  Radix digits: key bits [31:20] (4096 bins), [19:9] (2048), [8:0]
@@ -576,6 +710,10 @@ size_t select_ws_bytes(int32_t n_kv_heads, int64_t n) {
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   if (!use_block_path(a.n_kv_heads, a.n)) {
     const int64_t ncand = a.n - a.n_sink - a.n_recent;
+    if (ncand <= kSmallMax) {
+      hipLaunchKernelGGL(select_small_kernel, dim3((unsigned)a.n_kv_heads), dim3(kSmallThreads), 0, stream, a);
+      return hipGetLastError();
+    }
     if (ncand > kStageFrom && a.n_kv_heads <= kStageMaxHeads)
       hipLaunchKernelGGL(select_kernel<true>, dim3((unsigned)a.n_kv_heads), dim3(kSelThreads), 0, stream, a);
     else

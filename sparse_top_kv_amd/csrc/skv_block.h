@@ -8,25 +8,29 @@ namespace {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP: shifts by 1, 2, 4
+// and 8 lanes inside each row of 16 (lanes shifted in read zero), then the
+// total of row 0 and of row 2 broadcast into rows 1 and 3 (row_bcast:15), then
+// the total of rows 0-1 into rows 2 and 3 (row_bcast:31).  No LDS round trips.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
 // Exclusive prefix sum of one uint32 per thread over the workgroup; *total
 // receives the sum.  Uses sm_w (kSelWaves + 1 words).
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sm_w, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) sm_w[wave] = x;
   __syncthreads();
   if (wave == 0) {
-    uint32_t t = lane < kSelWaves ? sm_w[lane] : 0u;
-#pragma unroll
-    for (int off = 1; off < kSelWaves; off <<= 1) {
-      const uint32_t y = __shfl_up(t, off, 64);
-      if (lane >= off) t += y;
-    }
+    const uint32_t t = wave_incl_scan(lane < kSelWaves ? sm_w[lane] : 0u);
     if (lane < kSelWaves) sm_w[lane] = t;  // inclusive per-wave prefix
   }
   __syncthreads();

@@ -210,7 +210,8 @@ def test_select_block_path_leaves_header_zero():
 @pytest.mark.parametrize("hkv,n,S,R,K", [(8, 2048, 4, 32, 256), (3, 5000, 4, 64, 1000), (2, 700, 0, 32, 650),
                                           (4, 100, 4, 8, 0), (2, 100, 4, 8, 500), (1, 32768, 4, 64, 9762),
                                           (8, 16384, 0, 0, 100), (64, 16452, 4, 64, 7000),
-                                          (64, 20000, 4, 64, 5000)])
+                                          (64, 20000, 4, 64, 5000), (2, 4164, 4, 64, 1000),
+                                          (2, 4165, 4, 64, 4000), (130, 300, 0, 16, 37)])
 def test_select_bit_exact_on_oracle_scores(hkv, n, S, R, K):
     banner(f"select hkv={hkv} n={n} S={S} R={R} K={K}")
     rng = np.random.default_rng(n + K)
