@@ -446,6 +446,17 @@ def main():
         details["llama128k_topk_speedup_measured"] = round(sweep["131072"]["us"] / ts_us, 3)
         details["llama128k_topk_speedup_byte_bound"] = round(
             rf.dense_step_bytes(hq, hkv, d, n3, "bf16") / ts_bytes, 3)
+        # the three calls of that step timed on their own (same inputs)
+        nst = max(20, args.steps // 4)
+        part = {}
+        part["score_us"], _ = time_steps(
+            lambda i: skv.skv_score(big[i % 2]["q"], big[i % 2]["k"], n3, score3, ws), nst, 5, 3)
+        part["select_us"], _ = time_steps(
+            lambda i: skv.skv_select(score3, n3, S, R, K3, idx3, cnt3, ws), nst, 5, 3)
+        part["attend_sparse_us"], _ = time_steps(
+            lambda i: skv.skv_attend_sparse(big[i % 2]["q"], big[i % 2]["k"], big[i % 2]["v"], n3, idx3, cnt3,
+                                            n3 - R, out, lse, ws), nst, 5, 3)
+        details["llama128k_topk_step_parts_us"] = {k: round(v, 2) for k, v in part.items()}
         del big, score3
         torch.cuda.empty_cache()
         # ------------------------------------------------------------------
