@@ -159,11 +159,14 @@ __global__ __launch_bounds__(kThreads) void score_finalize_kernel(const ScoreSte
   }
   const float* ml = a.part_ml + (int64_t)h * cph * G * 2;
   for (int g = wave; g < G; g += kWaves) {
-    float M = kNegInf;
-    for (int64_t cc = lane; cc < nchunks; cc += 64) M = fmaxf(M, ml[(cc * G + g) * 2]);
+    // the first 64 chunks' statistics in one round of loads, any others after
+    const float2 st0 = lane < nchunks ? *reinterpret_cast<const float2*>(ml + ((int64_t)lane * G + g) * 2)
+                                      : make_float2(kNegInf, 0.0f);
+    float M = st0.x;
+    for (int64_t cc = lane + 64; cc < nchunks; cc += 64) M = fmaxf(M, ml[(cc * G + g) * 2]);
     M = wave_max(M);
-    float L = 0.0f;
-    for (int64_t cc = lane; cc < nchunks; cc += 64) {
+    float L = (st0.x == kNegInf) ? 0.0f : st0.y * fast_exp2(st0.x - M);
+    for (int64_t cc = lane + 64; cc < nchunks; cc += 64) {
       const float mc = ml[(cc * G + g) * 2];
       L += (mc == kNegInf) ? 0.0f : ml[(cc * G + g) * 2 + 1] * fast_exp2(mc - M);
     }
@@ -183,9 +186,14 @@ __global__ __launch_bounds__(kThreads) void score_finalize_kernel(const ScoreSte
     for (int e = 0; e < 8; ++e) s[e] += fast_exp2(v[e] - l2);
   }
   float* out = a.score + (int64_t)h * a.score_stride;
+  if (jb + 8 <= a.n && (reinterpret_cast<uintptr_t>(out + jb) & 15) == 0) {
+    *reinterpret_cast<float4*>(out + jb) = make_float4(s[0], s[1], s[2], s[3]);
+    *reinterpret_cast<float4*>(out + jb + 4) = make_float4(s[4], s[5], s[6], s[7]);
+  } else {
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (jb + e < a.n) out[jb + e] = s[e];
+    for (int e = 0; e < 8; ++e)
+      if (jb + e < a.n) out[jb + e] = s[e];
+  }
 }
 
 // bf16 caches: phase 1 on the matrix cores.  K streams through a per-wave
