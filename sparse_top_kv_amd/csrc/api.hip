@@ -198,7 +198,9 @@ skv_status launch_partials_merge(const skv_problem* p, char* base, const PartLay
 }
 
 ChunkPlan score_step_plan(const skv_problem* p, int64_t n) {
-  if (p->dtype == SKV_BF16) return plan_chunks(n, p->n_kv_heads, skv::score_step_mfma_granule(), 1 << 20);
+  if (p->dtype == SKV_BF16)
+    return plan_chunks(n, p->n_kv_heads, skv::score_step_mfma_granule(),
+                       skv::score_step_mfma_max_chunk(p->n_q_heads / p->n_kv_heads));
   return plan_chunks(n, p->n_kv_heads, 4 * skv::attend_rows_per_iter(p->dtype, p->head_dim),
                      skv::attend_max_chunk());
 }

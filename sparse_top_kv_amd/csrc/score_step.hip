@@ -197,11 +197,15 @@ __global__ __launch_bounds__(kThreads) void score_finalize_kernel(const ScoreSte
 }
 
 // bf16 caches: phase 1 on the matrix cores.  K streams through a per-wave
-// ring of 16-key LDS tiles (direct-to-LDS copies, as in the attention kernel;
-// no V, so each wave keeps S = 4 tiles); q.K^T is one 16x16x32 MFMA per 32
-// channels with the G query heads padded to 16.  Lane (q4, li) holds the
-// logits of keys 4 q4 .. 4 q4 + 3 for head li: it stores them as one 16-byte
-// write and keeps a running (max, sum) of its head.
+// ring of 16-key LDS tiles (direct-to-LDS copies, as in the attention kernel);
+// q.K^T is one 16x16x32 MFMA per 32 channels with the G query heads padded to
+// 16.  Lane (q4, li) holds the logits of keys 4 q4 .. 4 q4 + 3 for head li: it
+// keeps a running (max, sum) of its head and puts them into the workgroup's
+// LDS copy of its chunk's logits, which goes to memory in one coalesced pass
+// after the last tile (interleaving the logit writes with the K stream cost
+// about 7 us of the 55 at 128K).  Chunks hold at most kLgFloats / G keys.
+constexpr int kLgFloats = 16384;  // logits of one chunk, all heads of the group (64 KB)
+
 template <int D, int W, int S>
 __global__ __launch_bounds__(64 * W) void score_mfma_kernel(const ScoreStepArgs a, int G) {
   using TG = TileGeom<D>;
@@ -211,6 +215,9 @@ __global__ __launch_bounds__(64 * W) void score_mfma_kernel(const ScoreStepArgs 
   __shared__ __attribute__((aligned(1024))) char st2[W][TB];
   __shared__ __attribute__((aligned(1024))) char st3[W][TB];
   __shared__ float sm_m[W][16], sm_l[W][16];
+  // chunk logits, head-major; each head's row padded by 4 floats so the heads
+  // of one store sit in different banks
+  __shared__ __attribute__((aligned(16))) float sm_lg[kLgFloats + 4 * 16];
   static_assert(S >= 2 && S <= 4, "ring of two to four stages");
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -249,7 +256,8 @@ __global__ __launch_bounds__(64 * W) void score_mfma_kernel(const ScoreStepArgs 
   const int nsteps = (rows + kStep - 1) / kStep;
   const int nst = wave < nsteps ? (nsteps - 1 - wave) / W + 1 : 0;
   const float c2 = a.scale_log2;
-  float* lrow = a.logits + (int64_t)(h * G + (li < G ? li : 0)) * a.logits_stride;
+  const int lg_stride = a.chunk + 4;  // floats per head row in sm_lg
+  float* lg_row = sm_lg + (li < G ? li : 0) * lg_stride;
 
   auto issue = [&](char (*stg)[TB], int k) {
     const int j = wave + W * k;
@@ -284,12 +292,12 @@ __global__ __launch_bounds__(64 * W) void score_mfma_kernel(const ScoreStepArgs 
     for (int r = 0; r < 4; ++r) sv[r] = cs[r] * c2;
     const bool full = (j + 1) * kStep <= rows;  // wave-uniform
     if (full) {
-      if (li < G) *reinterpret_cast<float4*>(lrow + r0 + rb) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+      if (li < G) *reinterpret_cast<float4*>(lg_row + rb) = make_float4(sv[0], sv[1], sv[2], sv[3]);
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool ok = rb + r < rows;
-        if (ok && li < G) lrow[r0 + rb + r] = sv[r];
+        if (ok && li < G) lg_row[rb + r] = sv[r];
         sv[r] = ok ? sv[r] : kNegInf;
       }
     }
@@ -323,6 +331,17 @@ __global__ __launch_bounds__(64 * W) void score_mfma_kernel(const ScoreStepArgs 
     sm_l[wave][lane] = x;
   }
   __syncthreads();
+  // the chunk's logits to memory: rows of G heads, 16 bytes per thread and step
+  // (the logits rows are padded to a multiple of four keys, so a chunk's last
+  // four-key group is always in bounds)
+  {
+    const int q_per_head = (rows + 3) / 4;
+    for (int e = tid; e < G * q_per_head; e += 64 * W) {
+      const int g = e / q_per_head, r = 4 * (e - g * q_per_head);
+      const float4 v = *reinterpret_cast<const float4*>(sm_lg + g * lg_stride + r);
+      *reinterpret_cast<float4*>(a.logits + (int64_t)(h * G + g) * a.logits_stride + r0 + r) = v;
+    }
+  }
   if (tid < G) {
     const int g = tid;
     float Mw = sm_m[0][g];
@@ -358,7 +377,7 @@ hipError_t launch_finalize_g(int g, const ScoreStepArgs& a, hipStream_t s) {
 }
 
 constexpr int kScoreWaves = 8;
-constexpr int kScoreStages = 4;
+constexpr int kScoreStages = 2;
 
 template <int D>
 hipError_t launch_mfma(int g, const ScoreStepArgs& a, hipStream_t s) {
@@ -397,6 +416,10 @@ hipError_t launch_d(int g, const ScoreStepArgs& a, hipStream_t s) {
 }  // namespace
 
 int score_step_mfma_granule() { return kScoreWaves * kStep; }
+int score_step_mfma_max_chunk(int g) {
+  const int gr = score_step_mfma_granule();
+  return g < 1 ? gr : (kLgFloats / g) / gr * gr;
+}
 
 hipError_t launch_score_step(int dtype, int d, int g, const ScoreStepArgs& a, hipStream_t s) {
   if (dtype == 1 && d == 128) return launch_mfma<128>(g, a, s);

@@ -89,8 +89,10 @@ struct ScoreStepArgs {
   int64_t score_stride;
 };
 hipError_t launch_score_step(int dtype, int d, int g, const ScoreStepArgs& a, hipStream_t stream);
-// bf16 runs phase 1 on the matrix cores: chunks are multiples of this.
+// bf16 runs phase 1 on the matrix cores: chunks are multiples of this and
+// hold at most score_step_mfma_max_chunk(G) keys (their logits stay in LDS).
 int score_step_mfma_granule();
+int score_step_mfma_max_chunk(int g);
 
 // Observation-window score on MFMA (bf16 only): W queries x G heads per kv head.
 struct ScoreObsArgs {
