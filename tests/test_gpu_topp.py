@@ -63,7 +63,8 @@ def test_topp_matches_oracle(pooled, mode, lam, prune):
 
 
 @pytest.mark.parametrize("rows,n,S,R", [(1, 1, 0, 0), (3, 70, 4, 8), (8, 1024, 0, 0), (2, 1025, 1, 1),
-                                        (5, 40000, 4, 512), (2, 10, 6, 6), (1, 300, 400, 0)])
+                                        (5, 40000, 4, 512), (2, 10, 6, 6), (1, 300, 400, 0),
+                                        (2, 32768 + 68, 4, 64), (2, 32769 + 68, 4, 64)])
 def test_topp_shapes_and_ragged_tails(rows, n, S, R):
     banner(f"topp shape rows={rows} n={n} S={S} R={R}")
     s = _attn_like(rows, n, 2)
