@@ -19,7 +19,7 @@
 namespace skv {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
 template <int D, int kBatch>  // kBatch: chunks per thread per round of loads
