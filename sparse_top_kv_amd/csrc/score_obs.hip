@@ -25,7 +25,8 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 256;
-constexpr int kBlockKeys = 64 * kWaves;  // keys per workgroup
+constexpr int kKT = 4;                      // 16-key tiles of K per wave (A operands in registers)
+constexpr int kBlockKeys = 16 * kKT * kWaves;  // keys per workgroup
 
 struct RowInfo {
   bool ok;
@@ -46,10 +47,10 @@ __device__ __forceinline__ RowInfo row_info(const ScoreObsArgs& a, int h, int ro
 
 template <int D>
 __device__ __forceinline__ void load_k_tiles(const ScoreObsArgs& a, int h, int64_t kw0, int q4, int i16,
-                                             bf16x8_t (&kf)[4][D / 32]) {
+                                             bf16x8_t (&kf)[kKT][D / 32]) {
   const char* kb = a.k + (int64_t)h * a.head_stride_b;
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
+  for (int kt = 0; kt < kKT; ++kt) {
     int64_t key = kw0 + kt * 16 + i16;
     key = key < a.n ? key : a.n - 1;
 #pragma unroll
@@ -126,10 +127,10 @@ __device__ __forceinline__ void read_q_tile(const char* chunk, int tt, int q4, i
 }
 
 template <int D>
-__device__ __forceinline__ void s_tiles(const bf16x8_t (&kf)[4][D / 32], const bf16x8_t (&qb)[D / 32],
-                                        floatx4_t (&s)[4]) {
+__device__ __forceinline__ void s_tiles(const bf16x8_t (&kf)[kKT][D / 32], const bf16x8_t (&qb)[D / 32],
+                                        floatx4_t (&s)[kKT]) {
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
+  for (int kt = 0; kt < kKT; ++kt) {
     floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) acc = mfma_bf16(kf[kt][ks], qb[ks], acc);
@@ -146,19 +147,19 @@ __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs 
   const int q4 = lane >> 4, i16 = lane & 15;
   const int h = blockIdx.x / a.n_kblocks;
   const int kb = blockIdx.x - h * a.n_kblocks;
-  const int kw0 = kb * kBlockKeys + wave * 64;  // keys are below 2^31
+  const int kw0 = kb * kBlockKeys + wave * 16 * kKT;  // keys are below 2^31
   const int n = (int)a.n;
   const int R = a.n_obs * a.group;
   const int RT = (R + 15) / 16;
   const int NCH = (RT + kChunk - 1) / kChunk;
   // every window row sees keys <= n - W: no masks for a wave below that
-  const bool all_vis = kw0 + 63 <= n - a.n_obs;
+  const bool all_vis = kw0 + 16 * kKT - 1 <= n - a.n_obs;
   // the workgroups of a kv head walk the query chunks from different starting
   // points, so they do not all fetch the same chunk at the same time
   const int rot = kb % NCH;
   auto cid = [&](int c) { return c + rot < NCH ? c + rot : c + rot - NCH; };
 
-  bf16x8_t kf[4][D / 32];
+  bf16x8_t kf[kKT][D / 32];
   load_k_tiles<D>(a, h, kw0, q4, i16, kf);
   {
     uint4 v[QG::kPPT];
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs 
       if (tt >= nt) break;  // uniform
       bf16x8_t qb[D / 32];
       read_q_tile<D>(qchunk, tt, q4, i16, qb);
-      floatx4_t s[4];
+      floatx4_t s[kKT];
       s_tiles<D>(kf, qb, s);
       // S^T = K Q^T: lane (q4, i16) holds keys 16 kt + 4 q4 + r of query row
       // 16 rt + i16.  The scale (> 0) is applied after the max, inside the
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs 
       if (!all_vis) {
         const int last = (int)row_info(a, h, (ci * kChunk + tt) * 16 + i16, D).last;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < kKT; ++kt) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int key = kw0 + kt * 16 + q4 * 4 + r;
@@ -224,14 +225,14 @@ __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs 
         }
       }
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < kKT; ++kt)
         mw = fmaxf(mw, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
       mw = xor16_max(mw);
       mw = xor32_max(mw);
       const float mu = mw == kNegInf ? 0.0f : mw * c2;
       float lw = 0.0f;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < kKT; ++kt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) lw += fast_exp2(fmaf(s[kt][r], c2, -mu));
       }
@@ -295,13 +296,13 @@ __global__ __launch_bounds__(kThreads) void obs_pass2_kernel(const ScoreObsArgs 
   const int q4 = lane >> 4, i16 = lane & 15;
   const int h = blockIdx.x / a.n_kblocks;
   const int kb = blockIdx.x - h * a.n_kblocks;
-  const int kw0 = kb * kBlockKeys + wave * 64;  // keys are below 2^31
+  const int kw0 = kb * kBlockKeys + wave * 16 * kKT;  // keys are below 2^31
   const int n = (int)a.n;
   const int R = a.n_obs * a.group;
   const int RT = (R + 15) / 16;
   const int NCH = (RT + kChunk - 1) / kChunk;
   // every window row sees keys <= n - W: no masks for a wave below that
-  const bool all_vis = kw0 + 63 <= n - a.n_obs;
+  const bool all_vis = kw0 + 16 * kKT - 1 <= n - a.n_obs;
   const int rot = kb % NCH;  // staggered chunk order, as in pass 1
   auto cid = [&](int c) { return c + rot < NCH ? c + rot : c + rot - NCH; };
   auto load_l2 = [&](int c) -> float {
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void obs_pass2_kernel(const ScoreObsArgs 
     return tid < kL2 ? a.row_lse2[(int64_t)h * R + row] : 0.0f;
   };
 
-  bf16x8_t kf[4][D / 32];
+  bf16x8_t kf[kKT][D / 32];
   load_k_tiles<D>(a, h, kw0, q4, i16, kf);
   {
     uint4 v[QG::kPPT];
@@ -321,9 +322,9 @@ __global__ __launch_bounds__(kThreads) void obs_pass2_kernel(const ScoreObsArgs 
   }
   wait_vm<0>();  // K and the first chunk have landed (see pass 1)
 
-  float acc[4][4];
+  float acc[kKT][4];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
+  for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[kt][r] = 0.0f;
 
@@ -346,20 +347,20 @@ __global__ __launch_bounds__(kThreads) void obs_pass2_kernel(const ScoreObsArgs 
       bf16x8_t qb[D / 32];
       read_q_tile<D>(qchunk, tt, q4, i16, qb);
       const float cur_l2 = l2s[tt * 16 + i16];
-      floatx4_t s[4];
+      floatx4_t s[kKT];
       s_tiles<D>(kf, qb, s);
       const int row = (ci * kChunk + tt) * 16 + i16;
       if (row >= R) continue;
       if (all_vis) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < kKT; ++kt) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[kt][r] += fast_exp2(fmaf(s[kt][r], c2, -cur_l2));
         }
       } else {
         const int last = (int)row_info(a, h, row, D).last;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < kKT; ++kt) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int key = kw0 + kt * 16 + q4 * 4 + r;
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void obs_pass2_kernel(const ScoreObsArgs 
   if (kw0 >= n) return;
   const float inv_w = 1.0f / (float)a.n_obs;
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
+  for (int kt = 0; kt < kKT; ++kt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float tot = group_sum<16>(acc[kt][r]);
