@@ -376,23 +376,34 @@ struct SelWs {
 
 __host__ __device__ inline int sel_blocks_max(int64_t n) { return (int)((n + kBlk - 1) / kBlk); }
 
+// Byte offsets of the scratch arrays (each 256-byte aligned); [7] = total.
+__host__ __device__ inline void sel_offsets(int hkv, int64_t n, size_t (&off)[8]) {
+  const size_t nbm = (size_t)sel_blocks_max(n);
+  const size_t bytes[7] = {(size_t)hkv * kBins2 * 4, (size_t)hkv * nbm * kBins1 * 4, (size_t)hkv * nbm * 4,
+                           (size_t)hkv * (nbm + 1) * 4, (size_t)hkv * 8 * 4, (size_t)hkv * n * 4,
+                           (size_t)hkv * n * 4};
+  size_t at = 0;
+  for (int i = 0; i < 7; ++i) {
+    off[i] = at;
+    at += (bytes[i] + 255) / 256 * 256;
+  }
+  off[7] = at;
+}
+
 __host__ __device__ inline SelWs sel_ws(void* ws, uint32_t* totals, int hkv, int64_t n) {
   SelWs w;
   w.nbm = sel_blocks_max(n);
+  size_t off[8];
+  sel_offsets(hkv, n, off);
   char* p = (char*)ws;
-  auto take = [&](size_t bytes) {
-    char* q = p;
-    p += (bytes + 255) / 256 * 256;
-    return q;
-  };
   w.tot1 = totals;
-  w.tot2 = (uint32_t*)take((size_t)hkv * kBins2 * 4);
-  w.hist1 = (uint32_t*)take((size_t)hkv * w.nbm * kBins1 * 4);
-  w.above = (uint32_t*)take((size_t)hkv * w.nbm * 4);
-  w.moff = (uint32_t*)take((size_t)hkv * (w.nbm + 1) * 4);
-  w.head = (uint32_t*)take((size_t)hkv * 8 * 4);
-  w.ckey = (uint32_t*)take((size_t)hkv * n * 4);
-  w.cidx = (int32_t*)take((size_t)hkv * n * 4);
+  w.tot2 = (uint32_t*)(p + off[0]);
+  w.hist1 = (uint32_t*)(p + off[1]);
+  w.above = (uint32_t*)(p + off[2]);
+  w.moff = (uint32_t*)(p + off[3]);
+  w.head = (uint32_t*)(p + off[4]);
+  w.ckey = (uint32_t*)(p + off[5]);
+  w.cidx = (int32_t*)(p + off[6]);
   return w;
 }
 
@@ -703,8 +714,9 @@ static_assert((size_t)63 * kBins1 * 4 <= SKV_WS_HEADER_BYTES,
 
 size_t select_ws_bytes(int32_t n_kv_heads, int64_t n) {
   if (!use_block_path(n_kv_heads, n)) return 0;
-  const SelWs w = sel_ws(nullptr, nullptr, n_kv_heads, n);
-  return (size_t)((char*)(w.cidx + (int64_t)n_kv_heads * n) - (char*)nullptr) + 256;
+  size_t off[8];
+  sel_offsets(n_kv_heads, n, off);
+  return off[7];
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
