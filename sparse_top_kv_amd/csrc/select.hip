@@ -1,5 +1,4 @@
 // select.hip -- sinks + per-head top-K of the candidate range by radix select.
-#include <limits.h>
 //
 // Method: keep the attention sinks, the run of recent entries and the
 // highest-scoring history entries of each kv head ("Where Activation Sparsity
@@ -7,13 +6,20 @@
 // Context"; argTopK per kv head in "Sparse-to-Dense ..." Sec. 3.2; per-head K
 // from the SparseMM budgets).  Order: score descending, index ascending.
 //
-// One 1024-thread workgroup per kv head.  Scores map to order-preserving
-// 32-bit keys (score_key); the first kStage keys are loaded once into LDS (one
-// round of global loads), the rest, if any, are re-read per pass.  Three
-// counting passes with 2048/2048/1024-bin LDS histograms fix the key T of the
-// K-th entry and how many entries equal to T are taken.  A final pass in index
-// order writes every key > T and the lowest-index `take` keys == T, so the
-// output is ascending without a sort and ties go to the lowest index.
+// Scores map to order-preserving 32-bit keys (score_key); counting passes over
+// digits of the keys fix the key T of the K-th entry and how many entries
+// equal to T are taken; a pass in index order writes every key > T and the
+// lowest-index `take` keys == T, so the output is ascending without a sort and
+// ties go to the lowest index.  Three launch shapes:
+//   - up to 4096 candidates: one 256-thread workgroup per kv head, keys in
+//     registers (select_small_kernel);
+//   - longer rows with many kv heads (or rows past the block path's limit):
+//     one 1024-thread workgroup per kv head (select_kernel), the first 16K
+//     keys staged in LDS when the grid is small;
+//   - long rows with few kv heads: workgroups over 4096-candidate blocks in
+//     three kernels (sel_hist1_kernel, sel_collect_kernel, sel_write_kernel).
+#include <limits.h>
+
 #include "skv_common.h"
 #include "skv_kernels.h"
 #include "skv_block.h"
@@ -26,13 +32,13 @@ constexpr int kBins = 2048;
 
 constexpr int kStage = 16384;                 // keys staged in LDS (64 KB)
 constexpr int kStagePer = kStage / kSelThreads;
-constexpr int kStageFrom = 4096;              // staging pays from this many candidates
-constexpr int kStageMaxHeads = 128;           // ... and while the grid leaves CUs to spare
+constexpr int kStageMaxHeads = 128;           // staging pays while the grid leaves CUs to spare
 
-// STAGE: stage the first kStage candidates in LDS.  Used for longer rows with
-// up to kStageMaxHeads heads; short rows (passes hit the caches) and grids of
-// many heads (every CU busy; measured 188 -> 257 us at 1024 heads x 32K with
-// staging) read global memory per pass.
+// One 1024-thread workgroup per kv head: counting passes over key digits
+// [31:21], [20:10], [9:0] with 2048/2048/1024-bin LDS histograms.  STAGE:
+// stage the first kStage candidates in LDS (calls of up to kStageMaxHeads
+// heads: 64 heads x 16K 31.3 -> 23.9 us); grids of many heads read global
+// memory per pass (every CU busy; 1024 heads x 32K: 188 us, 257 with staging).
 template <bool STAGE>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a) {
   __shared__ uint32_t hist[kBins];
@@ -726,7 +732,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(select_small_kernel, dim3((unsigned)a.n_kv_heads), dim3(kSmallThreads), 0, stream, a);
       return hipGetLastError();
     }
-    if (ncand > kStageFrom && a.n_kv_heads <= kStageMaxHeads)
+    if (a.n_kv_heads <= kStageMaxHeads)
       hipLaunchKernelGGL(select_kernel<true>, dim3((unsigned)a.n_kv_heads), dim3(kSelThreads), 0, stream, a);
     else
       hipLaunchKernelGGL(select_kernel<false>, dim3((unsigned)a.n_kv_heads), dim3(kSelThreads), 0, stream, a);
