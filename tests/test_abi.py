@@ -136,3 +136,14 @@ def test_gather_validation():
     assert g(ohs=29 * 128) == skv.SKV_ERR_INVALID_ARG             # heads overlap: 20 + 10 rows
     assert g(n=0, tail=0) == skv.SKV_ERR_INVALID_ARG
     assert g(idx_stride=0, tail=100) == skv.SKV_ERR_INVALID_ARG   # nothing to copy
+
+
+def test_binding_constants_match_the_header():
+    """The Python binding's copies of the header's constants (workspace header
+    size, status and dtype codes) agree with include/sparsekv.h."""
+    txt = open(HEADER).read()
+    m = re.search(r"#define\s+SKV_WS_HEADER_BYTES\s+(\d+)", txt)
+    assert m and int(m.group(1)) == skv.SKV_WS_HEADER_BYTES
+    for name in ("SKV_OK", "SKV_F32", "SKV_BF16"):
+        mm = re.search(rf"\b{name}\s*=\s*(\d+)", txt)
+        assert mm and int(mm.group(1)) == getattr(skv, name), name
