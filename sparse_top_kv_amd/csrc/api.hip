@@ -215,12 +215,27 @@ size_t score_step_scratch(const skv_problem* p, int64_t n) {
          align_up((size_t)p->n_kv_heads * cp.cph * G * 2 * sizeof(float));
 }
 
+// Window-score row groups: with few (kv head, key block) workgroups the query
+// rows are split so that the grid holds at least 4 x target workgroups (at
+// most one group per staged chunk of rows).
+int obs_row_groups(const skv_problem* p, int64_t nkb, int64_t R) {
+  const int64_t wgs = (int64_t)p->n_kv_heads * nkb;
+  const int64_t want = 4 * (int64_t)target_wgs();
+  if (wgs >= want) return 1;
+  const int64_t nch = (R + skv::score_obs_chunk_rows() - 1) / skv::score_obs_chunk_rows();
+  int64_t rg = (want + wgs - 1) / wgs;
+  rg = rg > nch ? nch : rg;
+  return (int)(rg < 1 ? 1 : rg);
+}
+
 size_t score_obs_scratch(const skv_problem* p, int64_t n, int32_t n_obs) {
   const int G = p->n_q_heads / p->n_kv_heads;
   const int64_t R = (int64_t)n_obs * G;
   const int64_t nkb = (n + skv::score_obs_block_keys() - 1) / skv::score_obs_block_keys();
+  const int rg = obs_row_groups(p, nkb, R);
   return align_up((size_t)p->n_kv_heads * nkb * R * 2 * sizeof(float)) +
-         align_up((size_t)p->n_kv_heads * R * sizeof(float));
+         align_up((size_t)p->n_kv_heads * R * sizeof(float)) +
+         (rg > 1 ? align_up((size_t)rg * p->n_kv_heads * n * sizeof(float)) : 0);
 }
 
 // The verify pass: dense, causal, gamma * G query rows per kv head.
@@ -444,6 +459,8 @@ skv_status skv_score(const skv_problem* p, const void* q, int32_t n_obs, const v
   a.part_ml = (float*)(base + SKV_WS_HEADER_BYTES);
   a.row_lse2 = (float*)(base + SKV_WS_HEADER_BYTES +
                         align_up((size_t)p->n_kv_heads * nkb * R * 2 * sizeof(float)));
+  a.row_groups = obs_row_groups(p, nkb, R);
+  a.part_score = (float*)((char*)a.row_lse2 + align_up((size_t)p->n_kv_heads * R * sizeof(float)));
   a.score = score;
   a.score_stride = score_stride;
   return hip_status(skv::launch_score_obs(p->head_dim, a, (hipStream_t)stream));

@@ -138,6 +138,26 @@ __device__ __forceinline__ void s_tiles(const bf16x8_t (&kf)[kKT][D / 32], const
   }
 }
 
+// Workgroup -> (kv head h, key block kb, row group g) and the range of query
+// chunks [c0, c0 + nch) the group covers.
+struct ObsTile {
+  int h, kb, g, c0, nch;
+};
+__device__ __forceinline__ ObsTile obs_tile(const ScoreObsArgs& a, int NCH) {
+  ObsTile t;
+  const int rg = a.row_groups;
+  const int g = blockIdx.x % rg;
+  t.g = g;
+  const int hk = blockIdx.x / rg;
+  t.h = hk / a.n_kblocks;
+  t.kb = hk - t.h * a.n_kblocks;
+  const int per = (NCH + rg - 1) / rg;
+  t.c0 = g * per;
+  t.nch = NCH - t.c0 < per ? NCH - t.c0 : per;
+  if (t.nch < 0) t.nch = 0;
+  return t;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs a) {
   using QG = QGeom<D>;
@@ -145,19 +165,20 @@ __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs 
   __shared__ float sm_ml[2][kChunk][kWaves][16][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, i16 = lane & 15;
-  const int h = blockIdx.x / a.n_kblocks;
-  const int kb = blockIdx.x - h * a.n_kblocks;
-  const int kw0 = kb * kBlockKeys + wave * 16 * kKT;  // keys are below 2^31
   const int n = (int)a.n;
   const int R = a.n_obs * a.group;
   const int RT = (R + 15) / 16;
-  const int NCH = (RT + kChunk - 1) / kChunk;
+  const int NCH_ALL = (RT + kChunk - 1) / kChunk;
+  const ObsTile tl = obs_tile(a, NCH_ALL);
+  const int h = tl.h, kb = tl.kb, NCH = tl.nch;
+  if (NCH == 0) return;  // a row group past the last chunk: nothing to do
+  const int kw0 = kb * kBlockKeys + wave * 16 * kKT;  // keys are below 2^31
   // every window row sees keys <= n - W: no masks for a wave below that
   const bool all_vis = kw0 + 16 * kKT - 1 <= n - a.n_obs;
   // the workgroups of a kv head walk the query chunks from different starting
   // points, so they do not all fetch the same chunk at the same time
   const int rot = kb % NCH;
-  auto cid = [&](int c) { return c + rot < NCH ? c + rot : c + rot - NCH; };
+  auto cid = [&](int c) { return tl.c0 + (c + rot < NCH ? c + rot : c + rot - NCH); };
 
   bf16x8_t kf[kKT][D / 32];
   load_k_tiles<D>(a, h, kw0, q4, i16, kf);
@@ -294,17 +315,28 @@ __global__ __launch_bounds__(kThreads) void obs_pass2_kernel(const ScoreObsArgs 
   __shared__ float l2c[2][kL2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, i16 = lane & 15;
-  const int h = blockIdx.x / a.n_kblocks;
-  const int kb = blockIdx.x - h * a.n_kblocks;
-  const int kw0 = kb * kBlockKeys + wave * 16 * kKT;  // keys are below 2^31
   const int n = (int)a.n;
   const int R = a.n_obs * a.group;
   const int RT = (R + 15) / 16;
-  const int NCH = (RT + kChunk - 1) / kChunk;
+  const int NCH_ALL = (RT + kChunk - 1) / kChunk;
+  const ObsTile tl = obs_tile(a, NCH_ALL);
+  const int h = tl.h, kb = tl.kb, NCH = tl.nch;
+  const int kw0 = kb * kBlockKeys + wave * 16 * kKT;  // keys are below 2^31
   // every window row sees keys <= n - W: no masks for a wave below that
   const bool all_vis = kw0 + 16 * kKT - 1 <= n - a.n_obs;
-  const int rot = kb % NCH;  // staggered chunk order, as in pass 1
-  auto cid = [&](int c) { return c + rot < NCH ? c + rot : c + rot - NCH; };
+  const int rot = NCH > 0 ? kb % NCH : 0;  // staggered chunk order, as in pass 1
+  auto cid = [&](int c) { return tl.c0 + (c + rot < NCH ? c + rot : c + rot - NCH); };
+  // where this workgroup's key sums go: the score itself, or its row group's
+  // partial row
+  float* dst = a.row_groups == 1 ? a.score + (int64_t)h * a.score_stride
+                                 : a.part_score + ((int64_t)tl.g * a.n_kv_heads + h) * a.n;
+  if (NCH == 0) {  // a row group past the last chunk: zero partial sums
+    if (tid < 16 * kKT * kWaves) {
+      const int key = kb * kBlockKeys + tid;
+      if (key < n) dst[key] = 0.0f;
+    }
+    return;
+  }
   auto load_l2 = [&](int c) -> float {
     int row = c * kL2 + tid;
     row = row < R ? row : R - 1;
@@ -384,14 +416,26 @@ __global__ __launch_bounds__(kThreads) void obs_pass2_kernel(const ScoreObsArgs 
     for (int r = 0; r < 4; ++r) {
       const float tot = group_sum<16>(acc[kt][r]);
       const int key = kw0 + kt * 16 + q4 * 4 + r;
-      if (i16 == 0 && key < n) a.score[(int64_t)h * a.score_stride + key] = tot * inv_w;
+      if (i16 == 0 && key < n) dst[key] = tot * inv_w;
     }
   }
 }
 
+// score = the row groups' partial key sums, added in group order.
+__global__ __launch_bounds__(kThreads) void obs_reduce_kernel(const ScoreObsArgs a) {
+  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // (head, key)
+  if (e >= (int64_t)a.n_kv_heads * a.n) return;
+  const int h = (int)(e / a.n);
+  const int64_t key = e - (int64_t)h * a.n;
+  const int64_t plane = (int64_t)a.n_kv_heads * a.n;
+  float t = a.part_score[e];
+  for (int g = 1; g < a.row_groups; ++g) t += a.part_score[g * plane + e];
+  a.score[(int64_t)h * a.score_stride + key] = t;
+}
+
 template <int D>
 hipError_t launch_d(const ScoreObsArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)a.n_kv_heads * a.n_kblocks));
+  const dim3 grid((unsigned)((int64_t)a.n_kv_heads * a.n_kblocks * a.row_groups));
   hipLaunchKernelGGL(obs_pass1_kernel<D>, grid, dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -402,12 +446,18 @@ hipError_t launch_d(const ScoreObsArgs& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(obs_pass2_kernel<D>, grid, dim3(kThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.row_groups == 1) return e;
+  const int64_t total = (int64_t)a.n_kv_heads * a.n;
+  hipLaunchKernelGGL(obs_reduce_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int score_obs_block_keys() { return kBlockKeys; }
+int score_obs_chunk_rows() { return kChunk * 16; }
 
 hipError_t launch_score_obs(int d, const ScoreObsArgs& a, hipStream_t s) {
   if (d == 128) return launch_d<128>(a, s);

@@ -108,8 +108,15 @@ struct ScoreObsArgs {
   float* row_lse2;          // [Hkv][R]
   float* score;
   int64_t score_stride;
+  // Query rows split into row_groups workgroups per (kv head, key block) when
+  // there are few key blocks; each group's key sums go to part_score
+  // [row_groups][Hkv][n] and a last kernel adds them in group order.
+  int32_t row_groups;
+  float* part_score;
 };
 hipError_t launch_score_obs(int d, const ScoreObsArgs& a, hipStream_t stream);
+// Query rows per staged chunk of the window score (row groups split chunks).
+int score_obs_chunk_rows();
 
 // Sinks + top-K selection by radix select on order-preserving score keys.
 struct SelectArgs {

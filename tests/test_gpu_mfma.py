@@ -65,6 +65,27 @@ def test_obs_score_matches_oracle(hq, hkv, d, W, n):
     np.testing.assert_allclose(g.sum(1), hq // hkv, rtol=1e-4)
 
 
+@pytest.mark.parametrize("hq,hkv,W,n", [(7, 1, 80, 70000), (28, 4, 64, 3000)])
+def test_obs_score_row_groups(hq, hkv, W, n):
+    """Few (kv head, key block) workgroups and many window rows: the rows are
+    split into groups whose key sums are added at the end.  The first case has
+    5 chunks of 128 rows over 4 groups of 2 (the last group holds none)."""
+    banner(f"obs score row groups hq={hq} hkv={hkv} W={W} n={n}")
+    d = 128
+    q = _rand((W, hq, d), 6)
+    k = _rand((hkv, n, d), 7)
+    s64, _ = oracle.score(q, k, n)
+    qt, kt = dev(q), dev(k)
+    score = torch.full((hkv, n + 3), float("nan"), device="cuda")
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n, W)
+    skv.skv_score(qt, kt, n, score, ws)
+    torch.cuda.synchronize()
+    g = host(score)[:, :n]
+    assert np.all(np.isfinite(g))
+    assert np.all(np.abs(g - s64) <= 1e-4 * s64 + 1e-12)
+    np.testing.assert_allclose(g.sum(1), hq // hkv, rtol=1e-4)
+
+
 def test_window_select_end_to_end_near_ties():
     """Window score on the GPU -> select on the GPU; the kept set may differ from
     the oracle's only by swaps of near-tied entries at the threshold."""
