@@ -178,17 +178,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
 
 
 // ---------------------------------------------------------------------------
-// Short rows (at most kSmallMax candidates): one four-wave workgroup per kv
-// head.  Thread t holds the run of candidates [t P, t P + P) as keys in
-// registers, loaded once.  Each radix pass takes three barriers: histogram
-// complete, scan totals, digit chosen (the other of two histogram buffers is
-// cleared in the same step); the compaction is one scan of the (equal, above)
-// counts of every run.  The 1024-thread kernel spends most of a short row's
-// time in its workgroup barriers (2K candidates: 8.6 us).
+// Rows of at most kSmallMax candidates: one workgroup per kv head.  Thread t
+// holds the run of candidates [t P, t P + P), P <= PER, as keys in registers,
+// loaded once.  Each radix pass takes three barriers: histogram complete,
+// scan totals, digit chosen (the other of two histogram buffers is cleared in
+// the same step); the compaction is one scan of the (equal, above) counts of
+// every run.  PER = 4 up to 4096 candidates, 16 beyond (a run of 16 slots
+// costs more per pass than the barriers of 1024 threads: 2K candidates x 8
+// heads 5.3 us with 4 per thread, 7.1 us with 256 threads x 16).
 // ---------------------------------------------------------------------------
-constexpr int kSmallThreads = 256;
+constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / 64;
-constexpr int kSmallPer = 16;
+constexpr int kSmallPerShort = 4;   // keys per thread up to 4096 candidates
+constexpr int kSmallPer = 16;       // ... and up to kSmallMax
 constexpr int kSmallMax = kSmallThreads * kSmallPer;
 
 // Exclusive prefix sum of one value per thread over the workgroup; sm_w holds
@@ -209,6 +211,7 @@ __device__ __forceinline__ uint32_t small_excl_scan(uint32_t v, uint32_t* sm_w, 
   return before + x - v;
 }
 
+template <int PER>
 __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(const SelectArgs a) {
   __shared__ uint32_t hist[2][kBins];
   __shared__ uint32_t sm_w[4][kSmallWaves];
@@ -239,9 +242,9 @@ __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(const Selec
   const int P = (ncand + kSmallThreads - 1) / kSmallThreads;
   const int i0 = tid * P;
   const int nv = ncand - i0 < 0 ? 0 : (ncand - i0 > P ? P : ncand - i0);  // keys of this run
-  uint32_t key[kSmallPer];
+  uint32_t key[PER];
 #pragma unroll
-  for (int u = 0; u < kSmallPer; ++u) key[u] = u < nv ? score_key(s[c_lo + i0 + u]) : 0u;
+  for (int u = 0; u < PER; ++u) key[u] = u < nv ? score_key(s[c_lo + i0 + u]) : 0u;
   for (int b = tid; b < kBins; b += kSmallThreads) hist[0][b] = 0u;
   __syncthreads();
 
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(const Selec
     const int nb = pass == 2 ? 1024 : 2048;
     uint32_t* H = hist[pass & 1];
 #pragma unroll
-    for (int u = 0; u < kSmallPer; ++u)
+    for (int u = 0; u < PER; ++u)
       if (u < nv && (key[u] & mask) == prefix) atomicAdd(&H[(key[u] >> shift) & (uint32_t)(nb - 1)], 1u);
     __syncthreads();
     // thread t owns nb / 256 consecutive bins, visited from the top
@@ -289,7 +292,7 @@ __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(const Selec
   // ---- compaction in index order: one scan of (equal, above) per run ------
   uint32_t n_eq = 0, n_gt = 0;
 #pragma unroll
-  for (int u = 0; u < kSmallPer; ++u) {
+  for (int u = 0; u < PER; ++u) {
     n_eq += (u < nv && key[u] == T) ? 1u : 0u;
     n_gt += (u < nv && key[u] > T) ? 1u : 0u;
   }
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(const Selec
   uint32_t eq_rank = ex >> 16;
   uint32_t pos = (uint32_t)nsink + (ex & 0xFFFFu) + (eq_rank < take ? eq_rank : take);
 #pragma unroll
-  for (int u = 0; u < kSmallPer; ++u) {
+  for (int u = 0; u < PER; ++u) {
     if (u < nv) {
       const bool eq = key[u] == T;
       if (key[u] > T || (eq && eq_rank < take)) {
@@ -728,8 +731,14 @@ size_t select_ws_bytes(int32_t n_kv_heads, int64_t n) {
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   if (!use_block_path(a.n_kv_heads, a.n)) {
     const int64_t ncand = a.n - a.n_sink - a.n_recent;
+    if (ncand <= kSmallThreads * kSmallPerShort) {
+      hipLaunchKernelGGL(select_small_kernel<kSmallPerShort>, dim3((unsigned)a.n_kv_heads), dim3(kSmallThreads),
+                         0, stream, a);
+      return hipGetLastError();
+    }
     if (ncand <= kSmallMax) {
-      hipLaunchKernelGGL(select_small_kernel, dim3((unsigned)a.n_kv_heads), dim3(kSmallThreads), 0, stream, a);
+      hipLaunchKernelGGL(select_small_kernel<kSmallPer>, dim3((unsigned)a.n_kv_heads), dim3(kSmallThreads), 0,
+                         stream, a);
       return hipGetLastError();
     }
     if (a.n_kv_heads <= kStageMaxHeads)
