@@ -80,8 +80,9 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
-              "(the decode step shards by kv head with no exchange; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode "
+              "step shards by kv head with no exchange, so one GPU's throughput is the "
+              "per-GPU figure", file=sys.stderr)
         sys.exit(2)
     import torch
 
