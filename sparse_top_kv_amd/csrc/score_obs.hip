@@ -158,11 +158,14 @@ __device__ __forceinline__ ObsTile obs_tile(const ScoreObsArgs& a, int NCH) {
   return t;
 }
 
-template <int D>
+// NBUF: query-chunk buffers in LDS.  A workgroup that walks one chunk (at
+// most 128 window rows per row group) needs one, which halves the LDS of the
+// kernel and the registers of the prefetch, so more workgroups share a CU.
+template <int D, int NBUF>
 __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs a) {
   using QG = QGeom<D>;
-  __shared__ __attribute__((aligned(16))) char qc[2][QG::kChunkB];
-  __shared__ float sm_ml[2][kChunk][kWaves][16][2];
+  __shared__ __attribute__((aligned(16))) char qc[NBUF][QG::kChunkB];
+  __shared__ float sm_ml[NBUF][kChunk][kWaves][16][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, i16 = lane & 15;
   const int n = (int)a.n;
@@ -170,8 +173,9 @@ __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs 
   const int RT = (R + 15) / 16;
   const int NCH_ALL = (RT + kChunk - 1) / kChunk;
   const ObsTile tl = obs_tile(a, NCH_ALL);
-  const int h = tl.h, kb = tl.kb, NCH = tl.nch;
+  const int h = tl.h, kb = tl.kb, NCH = NBUF == 1 && tl.nch > 1 ? 1 : tl.nch;  // the host picks NBUF
   if (NCH == 0) return;  // a row group past the last chunk: nothing to do
+  auto buf = [](int c) { return NBUF == 1 ? 0 : (c & 1); };
   const int kw0 = kb * kBlockKeys + wave * 16 * kKT;  // keys are below 2^31
   // every window row sees keys <= n - W: no masks for a wave below that
   const bool all_vis = kw0 + 16 * kKT - 1 <= n - a.n_obs;
@@ -199,12 +203,12 @@ __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs 
       const int row = (cc * kChunk + tt) * 16 + rr;
       float M = kNegInf;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[c & 1][tt][w][rr][0]);
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[buf(c)][tt][w][rr][0]);
       float L = 0.0f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float mw2 = sm_ml[c & 1][tt][w][rr][0];
-        L += mw2 == kNegInf ? 0.0f : sm_ml[c & 1][tt][w][rr][1] * fast_exp2(mw2 - M);
+        const float mw2 = sm_ml[buf(c)][tt][w][rr][0];
+        L += mw2 == kNegInf ? 0.0f : sm_ml[buf(c)][tt][w][rr][1] * fast_exp2(mw2 - M);
       }
       if (row < R) {
         float* ml = a.part_ml + (((int64_t)h * a.n_kblocks + kb) * R + row) * 2;
@@ -216,10 +220,10 @@ __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs 
 
   for (int c = 0; c < NCH; ++c) {
     uint4 nxt[QG::kPPT];
-    if (c + 1 < NCH) load_q_chunk<D>(a, h, cid(c + 1), tid, nxt);
+    if (NBUF > 1 && c + 1 < NCH) load_q_chunk<D>(a, h, cid(c + 1), tid, nxt);
     lds_barrier();  // chunk c and the statistics of chunk c - 1 are in LDS
     if (c > 0) combine(c - 1);
-    const char* qchunk = qc[c & 1];
+    const char* qchunk = qc[buf(c)];
     const int ci = cid(c);
     const int nt = RT - ci * kChunk < kChunk ? RT - ci * kChunk : kChunk;
     const float c2 = a.scale_log2;
@@ -260,13 +264,13 @@ __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs 
       lw = xor16_sum(lw);
       lw = xor32_sum(lw);
       if (q4 == 0) {
-        sm_ml[c & 1][tt][wave][i16][0] = mw == kNegInf ? kNegInf : mu;
-        sm_ml[c & 1][tt][wave][i16][1] = lw;
+        sm_ml[buf(c)][tt][wave][i16][0] = mw == kNegInf ? kNegInf : mu;
+        sm_ml[buf(c)][tt][wave][i16][1] = lw;
       }
     }
     // the buffer of chunk c + 1 was last read in iteration c - 1, before the
     // barrier above
-    if (c + 1 < NCH) store_q_chunk<D>(qc[(c + 1) & 1], tid, nxt);
+    if (NBUF > 1 && c + 1 < NCH) store_q_chunk<D>(qc[buf(c + 1)], tid, nxt);
   }
   lds_barrier();
   combine(NCH - 1);
@@ -307,12 +311,12 @@ __global__ __launch_bounds__(kThreads) void obs_lse_kernel(const ScoreObsArgs a,
   if (lane == 0) a.row_lse2[(int64_t)h * R + row] = M + __log2f(L);
 }
 
-template <int D>
+template <int D, int NBUF>
 __global__ __launch_bounds__(kThreads) void obs_pass2_kernel(const ScoreObsArgs a) {
   using QG = QGeom<D>;
   constexpr int kL2 = kChunk * 16;  // row normalisers per chunk
-  __shared__ __attribute__((aligned(16))) char qc[2][QG::kChunkB];
-  __shared__ float l2c[2][kL2];
+  __shared__ __attribute__((aligned(16))) char qc[NBUF][QG::kChunkB];
+  __shared__ float l2c[NBUF][kL2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, i16 = lane & 15;
   const int n = (int)a.n;
@@ -320,7 +324,8 @@ __global__ __launch_bounds__(kThreads) void obs_pass2_kernel(const ScoreObsArgs 
   const int RT = (R + 15) / 16;
   const int NCH_ALL = (RT + kChunk - 1) / kChunk;
   const ObsTile tl = obs_tile(a, NCH_ALL);
-  const int h = tl.h, kb = tl.kb, NCH = tl.nch;
+  const int h = tl.h, kb = tl.kb, NCH = NBUF == 1 && tl.nch > 1 ? 1 : tl.nch;  // the host picks NBUF
+  auto buf = [](int c) { return NBUF == 1 ? 0 : (c & 1); };
   const int kw0 = kb * kBlockKeys + wave * 16 * kKT;  // keys are below 2^31
   // every window row sees keys <= n - W: no masks for a wave below that
   const bool all_vis = kw0 + 16 * kKT - 1 <= n - a.n_obs;
@@ -363,13 +368,13 @@ __global__ __launch_bounds__(kThreads) void obs_pass2_kernel(const ScoreObsArgs 
   for (int c = 0; c < NCH; ++c) {
     uint4 nxt[QG::kPPT];
     float l2n = 0.0f;
-    if (c + 1 < NCH) {
+    if (NBUF > 1 && c + 1 < NCH) {
       load_q_chunk<D>(a, h, cid(c + 1), tid, nxt);
       l2n = load_l2(cid(c + 1));
     }
     lds_barrier();  // chunk c is in LDS
-    const char* qchunk = qc[c & 1];
-    const float* l2s = l2c[c & 1];
+    const char* qchunk = qc[buf(c)];
+    const float* l2s = l2c[buf(c)];
     const int ci = cid(c);
     const int nt = RT - ci * kChunk < kChunk ? RT - ci * kChunk : kChunk;
     const float c2 = a.scale_log2;
@@ -403,9 +408,9 @@ __global__ __launch_bounds__(kThreads) void obs_pass2_kernel(const ScoreObsArgs 
       }
     }
     // the buffers of chunk c + 1 were last read in iteration c - 1
-    if (c + 1 < NCH) {
-      store_q_chunk<D>(qc[(c + 1) & 1], tid, nxt);
-      if (tid < kL2) l2c[(c + 1) & 1][tid] = l2n;
+    if (NBUF > 1 && c + 1 < NCH) {
+      store_q_chunk<D>(qc[buf(c + 1)], tid, nxt);
+      if (tid < kL2) l2c[buf(c + 1)][tid] = l2n;
     }
   }
   if (kw0 >= n) return;
@@ -436,16 +441,24 @@ __global__ __launch_bounds__(kThreads) void obs_reduce_kernel(const ScoreObsArgs
 template <int D>
 hipError_t launch_d(const ScoreObsArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)a.n_kv_heads * a.n_kblocks * a.row_groups));
-  hipLaunchKernelGGL(obs_pass1_kernel<D>, grid, dim3(kThreads), 0, s, a);
+  const int R = a.n_obs * a.group;
+  const int nch_all = ((R + 15) / 16 + kChunk - 1) / kChunk;
+  const bool one = (nch_all + a.row_groups - 1) / a.row_groups <= 1;  // chunks per row group
+  if (one)
+    hipLaunchKernelGGL((obs_pass1_kernel<D, 1>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((obs_pass1_kernel<D, 2>), grid, dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int R = a.n_obs * a.group;
   const int rblocks = (R + kWaves - 1) / kWaves;
   hipLaunchKernelGGL(obs_lse_kernel, dim3((unsigned)(a.n_kv_heads * rblocks)), dim3(kThreads), 0, s, a,
                      rblocks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(obs_pass2_kernel<D>, grid, dim3(kThreads), 0, s, a);
+  if (one)
+    hipLaunchKernelGGL((obs_pass2_kernel<D, 1>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((obs_pass2_kernel<D, 2>), grid, dim3(kThreads), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess || a.row_groups == 1) return e;
   const int64_t total = (int64_t)a.n_kv_heads * a.n;
