@@ -11,8 +11,8 @@
 // equal to T are taken; a pass in index order writes every key > T and the
 // lowest-index `take` keys == T, so the output is ascending without a sort and
 // ties go to the lowest index.  Three launch shapes:
-//   - up to 4096 candidates: one 256-thread workgroup per kv head, keys in
-//     registers (select_small_kernel);
+//   - up to 16K candidates: one 1024-thread workgroup per kv head, keys in
+//     registers, 4 or 16 per thread (select_small_kernel);
 //   - longer rows with many kv heads (or rows past the block path's limit):
 //     one 1024-thread workgroup per kv head (select_kernel), the first 16K
 //     keys staged in LDS when the grid is small;
