@@ -150,6 +150,101 @@ bool problem_ok(const OraProblem* p) {
          (p->dtype == ORA_F32 || p->dtype == ORA_BF16);
 }
 
+// Non-negative integers of any size (base 2^32 digits, least significant
+// first), for the exact mass sums of the SpecVLM selection below.  Only what
+// that rule needs: from an integer-valued double, add, shift left, multiply by
+// a 64-bit integer, compare.
+struct Nat {
+  std::vector<uint32_t> d;
+};
+
+void nat_trim(Nat& a) {
+  while (!a.d.empty() && a.d.back() == 0) a.d.pop_back();
+}
+
+// x >= 0 with no fractional part, exactly.
+Nat nat_from_integer_double(double x) {
+  Nat r;
+  if (x == 0.0) return r;
+  int e = 0;
+  const double f = std::frexp(x, &e);                  // x = f 2^e, f in [0.5, 1)
+  uint64_t m = (uint64_t)std::ldexp(f, 53);            // 53-bit integer, exact
+  int sh = e - 53;                                     // x = m 2^sh
+  if (sh < 0) {                                        // x is an integer: the dropped
+    m >>= -sh;                                         // bits are zeros
+    sh = 0;
+  }
+  r.d = {(uint32_t)m, (uint32_t)(m >> 32)};
+  nat_trim(r);
+  Nat out;
+  out.d.assign((size_t)(sh / 32) + r.d.size() + 1, 0u);
+  const int bs = sh % 32;
+  for (size_t i = 0; i < r.d.size(); ++i) {
+    const uint64_t v = (uint64_t)r.d[i] << bs;
+    out.d[i + sh / 32] |= (uint32_t)v;
+    out.d[i + sh / 32 + 1] |= (uint32_t)(v >> 32);
+  }
+  nat_trim(out);
+  return out;
+}
+
+Nat nat_add(const Nat& a, const Nat& b) {
+  Nat r;
+  const size_t n = std::max(a.d.size(), b.d.size());
+  r.d.assign(n + 1, 0u);
+  uint64_t carry = 0;
+  for (size_t i = 0; i < n; ++i) {
+    const uint64_t t = (uint64_t)(i < a.d.size() ? a.d[i] : 0u) + (i < b.d.size() ? b.d[i] : 0u) + carry;
+    r.d[i] = (uint32_t)t;
+    carry = t >> 32;
+  }
+  r.d[n] = (uint32_t)carry;
+  nat_trim(r);
+  return r;
+}
+
+Nat nat_shl(const Nat& a, int sh) {
+  Nat r;
+  if (a.d.empty()) return r;
+  r.d.assign(a.d.size() + (size_t)(sh / 32) + 1, 0u);
+  const int bs = sh % 32;
+  for (size_t i = 0; i < a.d.size(); ++i) {
+    const uint64_t v = (uint64_t)a.d[i] << bs;
+    r.d[i + sh / 32] |= (uint32_t)v;
+    r.d[i + sh / 32 + 1] |= (uint32_t)(v >> 32);
+  }
+  nat_trim(r);
+  return r;
+}
+
+Nat nat_mul_u64(const Nat& a, uint64_t m) {
+  const uint32_t ml[2] = {(uint32_t)m, (uint32_t)(m >> 32)};
+  Nat r;
+  r.d.assign(a.d.size() + 3, 0u);
+  for (int j = 0; j < 2; ++j) {
+    uint64_t carry = 0;
+    for (size_t i = 0; i < a.d.size(); ++i) {
+      const uint64_t t = (uint64_t)a.d[i] * ml[j] + r.d[i + j] + carry;
+      r.d[i + j] = (uint32_t)t;
+      carry = t >> 32;
+    }
+    for (size_t k = a.d.size() + j; carry; ++k) {
+      const uint64_t t = (uint64_t)r.d[k] + carry;
+      r.d[k] = (uint32_t)t;
+      carry = t >> 32;
+    }
+  }
+  nat_trim(r);
+  return r;
+}
+
+int nat_cmp(const Nat& a, const Nat& b) {
+  if (a.d.size() != b.d.size()) return a.d.size() < b.d.size() ? -1 : 1;
+  for (size_t i = a.d.size(); i-- > 0;)
+    if (a.d[i] != b.d[i]) return a.d[i] < b.d[i] ? -1 : 1;
+  return 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,18 +352,19 @@ int ora_select(const float* score, int64_t score_stride, int32_t Hkv, int64_t n,
 // top-P retention, Stage II spatially uniform reduction).  Candidates, sinks
 // and the recent run are split as in ora_select.  One selection per score row,
 // or, with pooled != 0, one selection on the per-token sum over all rows that
-// every row then receives (the blog averages over layers and heads; the
-// constant factor does not change the selection).
+// every row then receives (the blog averages the verifier's attention over
+// layers and heads; the constant factor is dropped).
 //
 // Readings, in the order the blog gives the steps:
-//   mass     a_j >= 0 is measured exactly as the integer u_j = floor(a_j 2^S)
-//            (pooled: the sum over rows of those integers), with
-//            S = 62 - E - ceil(log2 N), 2^(E-1) <= max a < 2^E and N the number
-//            of terms summed into one total (n_cand, or rows x n_cand); every
-//            total then stays below 2^62 and all sums are exact;
-//   order    u descending, index ascending;
+//   a_j      the candidate's score (fp32, finite, >= 0).  Pooled: the sum over
+//            rows, added in double in ascending row order and rounded to the
+//            nearest fp32 (saturating at the largest finite fp32);
+//   order    a descending, index ascending;
 //   Stage I  c = the smallest c' whose first c' candidates in that order carry
-//            mass >= lambda * (total mass), compared exactly; V_R = those c;
+//            mass sum >= lambda * (sum of every a), in exact arithmetic: every
+//            fp32 a is an integer multiple of 2^-149, so the sums are exact
+//            integers in that unit, and lambda (a double) is the exact
+//            fraction lam_m / 2^lam_sh; V_R = those c candidates;
 //   Stage II B = (1 - r) n_cand rounded to nearest in double (ties away from
 //            zero: r = 0.9 of 100 candidates gives 10); the L = n_cand - c leftover
 //            candidates, in ascending index order, are sampled at ranks
@@ -285,7 +381,6 @@ int ora_select_topp(const float* score, int64_t score_stride, int32_t H, int64_t
       !(lambda >= 0.0 && lambda <= 1.0) || !(prune >= 0.0 && prune <= 1.0) ||
       (fill_mode != 0 && fill_mode != 1))
     return 1;
-  typedef unsigned __int128 u128;
   const int64_t tail = std::max<int64_t>(n - R, 0);
   const int64_t nsink = std::min<int64_t>(S, tail);
   const int64_t c_lo = S, ncand = (S < n - R) ? (n - R) - S : 0;
@@ -296,46 +391,44 @@ int ora_select_topp(const float* score, int64_t score_stride, int32_t H, int64_t
       if (!std::isfinite(x) || x < 0.0f) return 2;
     }
   const int64_t budget = std::llround((1.0 - prune) * (double)ncand);
+  // lambda = lam_m / 2^lam_sh exactly (a double has a 53-bit significand)
+  int lexp = 0;
+  const double lfrac = std::frexp(lambda, &lexp);
+  const uint64_t lam_m = (uint64_t)std::ldexp(lfrac, 53);
+  const int lam_sh = 53 - lexp;
   const int n_sel = pooled ? 1 : H;
   for (int sel = 0; sel < n_sel; ++sel) {
     const int h0 = pooled ? 0 : sel, h1 = pooled ? H : sel + 1;
-    // fixed-point scale from the largest score and the number of summed terms
-    double amax = 0.0;
-    for (int h = h0; h < h1; ++h)
-      for (int64_t j = c_lo; j < c_lo + ncand; ++j) amax = std::max(amax, (double)score[h * score_stride + j]);
-    std::vector<uint64_t> u(ncand, 0);
-    if (amax > 0.0) {
-      int E = 0;
-      std::frexp(amax, &E);
-      const int64_t terms = (int64_t)(h1 - h0) * ncand;
-      int lg = 0;
-      while (((int64_t)1 << lg) < terms) ++lg;
-      const int Sfix = 62 - E - lg;
-      for (int64_t i = 0; i < ncand; ++i)
-        for (int h = h0; h < h1; ++h)
-          u[i] += (uint64_t)std::floor(std::ldexp((double)score[h * score_stride + c_lo + i], Sfix));
+    std::vector<float> a(ncand);
+    for (int64_t i = 0; i < ncand; ++i) {
+      double sum = 0.0;
+      for (int h = h0; h < h1; ++h) sum += (double)score[h * score_stride + c_lo + i];
+      float x = (float)sum;
+      if (std::isinf(x)) x = std::numeric_limits<float>::max();
+      a[i] = x;
     }
-    uint64_t total = 0;
-    for (int64_t i = 0; i < ncand; ++i) total += u[i];
-    // Stage I: sort by mass, keep the shortest prefix reaching lambda of the total
+    // exact masses in units of 2^-149, and their total
+    std::vector<Nat> mass(ncand);
+    Nat total;
+    for (int64_t i = 0; i < ncand; ++i) {
+      mass[i] = nat_from_integer_double(std::ldexp((double)a[i], 149));
+      total = nat_add(total, mass[i]);
+    }
+    // Stage I: sort by score, keep the shortest prefix reaching lambda of the
+    // total: prefix >= lambda * total  <=>  prefix * 2^lam_sh >= lam_m * total
     std::vector<int64_t> order(ncand);
     for (int64_t i = 0; i < ncand; ++i) order[i] = i;
-    std::sort(order.begin(), order.end(), [&](int64_t a, int64_t b) {
-      if (u[a] != u[b]) return u[a] > u[b];
-      return a < b;
+    std::sort(order.begin(), order.end(), [&](int64_t x, int64_t y) {
+      if (a[x] != a[y]) return a[x] > a[y];
+      return x < y;
     });
-    int mexp = 0;
-    const double mfrac = std::frexp(lambda, &mexp);          // lambda = mfrac 2^mexp
-    const uint64_t lam_m = (uint64_t)std::ldexp(mfrac, 53);  // exact: 53-bit mantissa
-    const int lam_sh = 53 - mexp;                            // lambda = lam_m / 2^lam_sh
-    // an integer mass m reaches lambda * total exactly when m >= ceil(lambda * total)
-    const u128 prod = (u128)lam_m * total;
-    uint64_t theta;
-    if (lam_sh >= 128) theta = prod != 0;
-    else theta = (uint64_t)((prod >> lam_sh) + ((prod & (((u128)1 << lam_sh) - 1)) != 0));
+    const Nat rhs = nat_mul_u64(total, lam_m);
     int64_t c = 0;
-    uint64_t acc = 0;
-    while (c < ncand && acc < theta) acc += u[order[c++]];
+    Nat prefix;
+    while (nat_cmp(nat_shl(prefix, lam_sh), rhs) < 0) {
+      prefix = nat_add(prefix, mass[order[c]]);
+      ++c;
+    }
     std::vector<char> in_r(ncand, 0);
     for (int64_t i = 0; i < c; ++i) in_r[order[i]] = 1;
     // Stage II: uniform walk through the leftovers in index order
