@@ -132,11 +132,14 @@ skv_status skv_select(const skv_problem* p, const float* score, int64_t score_st
  * candidates are split as in skv_select.  Per score row h (or, pooled = 1, once
  * on the per-candidate sum over all n_kv_heads rows, the set then written to
  * every row):
- *   mass     u_j = floor(a_j 2^S), exact integers, S = 62 - E - ceil(log2 N)
- *            with 2^(E-1) <= max a < 2^E and N the terms in one total;
+ *   score    a_j = the fp32 score; pooled: the rows' scores added in double in
+ *            ascending row order, rounded to the nearest fp32 (saturating at
+ *            the largest finite fp32);
  *   Stage I  V_R = the shortest prefix of the candidates ordered by
- *            (u descending, index ascending) whose mass is >= lambda * total
- *            (exact comparison; c = |V_R|);
+ *            (a descending, index ascending) whose summed a is >= lambda times
+ *            the sum of every candidate's a, in exact arithmetic (every fp32
+ *            is an integer multiple of 2^-149; lambda is taken as the exact
+ *            value of the double; c = |V_R|);
  *   Stage II B = round((1 - prune_ratio) * #candidates) (double product,
  *            halves away from zero); the L = #candidates - c leftovers, in
  *            index order, are sampled at ranks floor(i L / n_U), i < n_U, with

@@ -271,8 +271,8 @@ size_t verify_scratch(const skv_problem* p, int64_t n, int32_t gamma) {
   return s;
 }
 
-// Pooled top-P selection: one 64-bit fixed-point mass per candidate.
-size_t topp_scratch(int64_t n) { return ((size_t)n * 8 + kAlign - 1) / kAlign * kAlign; }
+// Pooled top-P selection: one fp32 pooled score per candidate.
+size_t topp_scratch(int64_t n) { return ((size_t)n * 4 + kAlign - 1) / kAlign * kAlign; }
 
 }  // namespace
 
@@ -535,7 +535,7 @@ skv_status skv_select_topp(const skv_problem* p, const float* score, int64_t sco
   a.idx_stride = idx_stride;
   a.count = count;
   a.count_r = count_r;
-  a.mass = pooled ? (uint64_t*)((char*)ws + SKV_WS_HEADER_BYTES) : nullptr;
+  a.pooled_row = pooled ? (uint32_t*)((char*)ws + SKV_WS_HEADER_BYTES) : nullptr;
   return hip_status(skv::launch_select_topp(a, (hipStream_t)stream));
 }
 

@@ -3,28 +3,32 @@
 // reduction).
 //
 // One 1024-thread workgroup per selection: a score row (kv head), or, pooled,
-// the per-token sum over all rows (the blog averages the verifier's attention
-// over layers and heads; the constant factor does not change the selection).
+// one row of per-token sums over all rows (the blog averages the verifier's
+// attention over layers and heads; the constant factor is dropped).  Pooled,
+// a token's score is its rows added in double in ascending row order and
+// rounded to the nearest fp32 (saturating at the largest finite fp32).
 //
-// Mass is exact fixed point: u_j = floor(a_j 2^S) for a score a_j >= 0, with
-// S = 62 - E - ceil(log2 N), 2^(E-1) <= max a < 2^E and N the number of terms
-// in one total, so every sum is an exact 64-bit integer below 2^62 and the
-// threshold test cannot depend on the order of additions.
-//
-//   1. max score -> S; total mass U; theta = ceil(lambda U) (128-bit product)
-//   2. radix passes over the 62-bit masses, 8-bit digits from the top, with
-//      per-bin count and mass histograms: the pass finds the bin where the
-//      running mass (largest first) reaches theta.  The last pass fixes the
-//      mass v* of the entry that crosses; `take` entries equal to v* are kept,
-//      lowest index first.  c = |V_R| entries in all.
-//   3. one pass in index order: V_R membership (u > v*, or u == v* within the
+// Stage I is exact.  Candidates are ordered by the fp32 score a (descending,
+// index ascending); c is the smallest count whose prefix mass reaches
+// lambda times the total, compared without rounding.  Every fp32 a >= 0 is
+// M 2^(e' - 150) with e the biased exponent, e' = max(e, 1) and M the 24-bit
+// significand, i.e. an integer multiple M 2^(e' - 1) of the unit 2^-149:
+//   1. histogram over the exponent e (bits 30..23 of a): count and sum of M per
+//      bin, exact in 64 bits (M < 2^24, at most 2^31 candidates);
+//   2. one thread walks the bins from the top in 384-bit integer arithmetic:
+//      total U, theta = ceil(lambda U) (lambda = lam_m / 2^lam_sh exactly), the
+//      bin e1 where the running mass reaches theta, and what that bin still
+//      has to supply, ceil((theta - P) / 2^(e1' - 1)) in units of M;
+//   3. three 8-bit radix passes over M inside bin e1, with per-bin count and
+//      M-sum histograms, find the significand M* of the entry that crosses;
+//      `take` entries equal to it are kept, lowest index first;
+//   4. one pass in index order: V_R membership (a > a*, or a == a* within the
 //      first `take` ties), the leftover rank of every other candidate, the
 //      uniform picks at leftover ranks floor(i L / n_U), and the ascending
-//      output -- three workgroup ballots per 1024 candidates.
-//
-// Digit 0 of a pass is not counted with atomics: it is the group's count and
-// mass minus the other bins (most masses are tiny, so most entries land there
-// in the top digits).
+//      output.
+// Zero scores carry no mass and are left out of every histogram.
+#include <float.h>
+
 #include "skv_block.h"
 #include "skv_common.h"
 #include "skv_kernels.h"
@@ -36,20 +40,87 @@ constexpr int kToppBins = 256;
 
 __device__ __forceinline__ uint32_t pos_bits(float x) { return x > 0.0f ? __float_as_uint(x) : 0u; }
 
-// floor(x 2^S) for x > 0 (0 otherwise), exactly, from the fp32 bits.
-__device__ __forceinline__ uint64_t fixed_mass(float x, int S) {
-  const uint32_t b = pos_bits(x);
-  if (b == 0u) return 0u;
-  const uint32_t be = b >> 23;
-  uint64_t m = b & 0x7fffffu;
-  int ex = -149;
-  if (be) {
-    m |= 0x800000u;
-    ex = (int)be - 150;
+// Score bits of candidate position j of a pooled selection.
+__device__ __forceinline__ uint32_t pooled_bits(const ToppArgs& a, int64_t j) {
+  double s = 0.0;
+  for (int h = 0; h < a.rows; ++h) s = s + (double)a.score[(int64_t)h * a.score_stride + j];
+  float f = (float)s;
+  if (f == __builtin_huge_valf()) f = FLT_MAX;
+  return pos_bits(f);
+}
+
+// 24-bit significand of positive fp32 bits b (no implicit one for subnormals).
+__device__ __forceinline__ uint32_t sig_of(uint32_t b) {
+  return (b & 0x7fffffu) | ((b >> 23) ? 0x800000u : 0u);
+}
+// log2 of the unit of exponent bin e's significands, in units of 2^-149.
+__device__ __forceinline__ int unit_shift(int e) { return (e ? e : 1) - 1; }
+
+// 384-bit unsigned integer (little-endian 64-bit limbs): holds every total
+// (below 2^311) and lambda times it (below 2^365).
+struct Wide {
+  uint64_t w[6];
+};
+
+__device__ __forceinline__ void wide_zero(Wide& x) {
+#pragma unroll
+  for (int i = 0; i < 6; ++i) x.w[i] = 0u;
+}
+
+// x += v 2^sh, 0 <= sh < 320.
+__device__ __forceinline__ void wide_add_shl(Wide& x, uint64_t v, int sh) {
+  const int li = sh >> 6, bo = sh & 63;
+  const uint64_t lo = v << bo, hi = bo ? v >> (64 - bo) : 0u;
+  uint64_t carry = 0;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const uint64_t add = i == li ? lo : (i == li + 1 ? hi : 0u);
+    const uint64_t t = x.w[i] + add;
+    const uint64_t c1 = t < add;
+    const uint64_t t2 = t + carry;
+    const uint64_t c2 = t2 < carry;
+    x.w[i] = t2;
+    carry = c1 | c2;
   }
-  const int sh = ex + S;
-  if (sh >= 0) return m << sh;  // below 2^62 by the choice of S
-  return -sh >= 64 ? 0u : (m >> -sh);
+}
+
+__device__ __forceinline__ int wide_cmp(const Wide& a, const Wide& b) {
+  for (int i = 5; i >= 0; --i)
+    if (a.w[i] != b.w[i]) return a.w[i] < b.w[i] ? -1 : 1;
+  return 0;
+}
+
+// a - b for a >= b.
+__device__ __forceinline__ Wide wide_sub(const Wide& a, const Wide& b) {
+  Wide r;
+  uint64_t borrow = 0;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const uint64_t t = a.w[i] - b.w[i];
+    const uint64_t b1 = a.w[i] < b.w[i];
+    r.w[i] = t - borrow;
+    borrow = b1 | (t < borrow);
+  }
+  return r;
+}
+
+// ceil(x / 2^sh) for 0 <= sh < 384 (the caller knows the result fits in the
+// returned limbs: all of them for theta, the lowest for a bin's need).
+__device__ __forceinline__ Wide wide_shr_ceil(const Wide& x, int sh) {
+  Wide r;
+  wide_zero(r);
+  const int ls = sh >> 6, bs = sh & 63;
+  bool rem = false;
+  for (int i = 0; i < 6; ++i)
+    if (i < ls) rem = rem || x.w[i] != 0u;
+  if (bs && ls < 6) rem = rem || (x.w[ls] << (64 - bs)) != 0u;
+  for (int i = 0; i < 6; ++i) {
+    const int s0 = i + ls;
+    const uint64_t lo = s0 < 6 ? x.w[s0] : 0u, hi = s0 + 1 < 6 ? x.w[s0 + 1] : 0u;
+    r.w[i] = bs ? (lo >> bs) | (hi << (64 - bs)) : lo;
+  }
+  if (rem) wide_add_shl(r, 1u, 0);
+  return r;
 }
 
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
@@ -68,17 +139,137 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u62(uint64_t x) {
   return (uint64_t)s0 + ((uint64_t)s1 << 25) + ((uint64_t)s2 << 50);
 }
 
-__global__ __launch_bounds__(kSelThreads) void topp_kernel(const ToppArgs a) {
-  __shared__ uint32_t h_cnt[kToppBins];
-  __shared__ uint64_t h_mass[kToppBins];
-  __shared__ uint32_t sm_w[kSelWaves + 1];
-  __shared__ uint64_t sm_q[kSelWaves];
-  __shared__ uint32_t sm_c[kSelWaves];
-  __shared__ uint64_t sm_need, sm_gmass, sm_theta;
-  __shared__ uint32_t sm_digit, sm_gcnt, sm_above;
-  __shared__ int sm_S;
+// Shared state of the Stage I passes.
+struct ToppShared {
+  uint32_t h_cnt[kToppBins];
+  uint64_t h_mass[kToppBins];
+  uint64_t sq[kSelWaves];
+  uint32_t sc[kSelWaves];
+  uint64_t need;    // mass still to supply, in units of the current group's significands
+  uint32_t above;   // candidates ordered before the current group
+  uint32_t digit;
+  int e1;           // exponent bin of the crossing entry; -1: nothing is retained
+};
 
+__device__ __forceinline__ void topp_clear_hist(ToppShared& sh) {
+  for (int b = threadIdx.x; b < kToppBins; b += blockDim.x) {
+    sh.h_cnt[b] = 0u;
+    sh.h_mass[b] = 0u;
+  }
+}
+
+// Step 2 (after the exponent histogram): one thread, 384-bit arithmetic.
+__device__ __forceinline__ void topp_walk_exponents(ToppShared& sh, uint64_t lam_m, int lam_sh) {
+  if (threadIdx.x != 0) return;
+  Wide U;
+  wide_zero(U);
+  for (int e = 0; e < kToppBins; ++e)
+    if (sh.h_mass[e]) wide_add_shl(U, sh.h_mass[e], unit_shift(e));
+  // theta = ceil(lam_m U / 2^lam_sh); lam_m < 2^54 keeps the product in 384 bits
+  Wide prod;
+  uint64_t carry = 0;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const unsigned __int128 t = (unsigned __int128)U.w[i] * lam_m + carry;
+    prod.w[i] = (uint64_t)t;
+    carry = (uint64_t)(t >> 64);
+  }
+  Wide theta;
+  if (lam_sh >= 384) {
+    wide_zero(theta);
+    bool nz = false;
+    for (int i = 0; i < 6; ++i) nz = nz || prod.w[i] != 0u;
+    theta.w[0] = nz ? 1u : 0u;
+  } else {
+    theta = wide_shr_ceil(prod, lam_sh);
+  }
+  bool tz = true;
+  for (int i = 0; i < 6; ++i) tz = tz && theta.w[i] == 0u;
+  sh.e1 = -1;
+  sh.need = 0;
+  sh.above = 0;
+  if (tz) return;  // the empty prefix already reaches lambda U
+  Wide P;
+  wide_zero(P);
+  uint32_t above = 0;
+  for (int e = kToppBins - 1; e >= 0; --e) {
+    if (!sh.h_mass[e]) continue;
+    Wide Pn = P;
+    wide_add_shl(Pn, sh.h_mass[e], unit_shift(e));
+    if (wide_cmp(Pn, theta) >= 0) {
+      sh.e1 = e;
+      sh.need = wide_shr_ceil(wide_sub(theta, P), unit_shift(e)).w[0];
+      sh.above = above;
+      return;
+    }
+    P = Pn;
+    above += sh.h_cnt[e];
+  }
+}
+
+// Step 3, the scan of one radix pass over the significands of the current
+// group (histograms filled): thread t < 256 owns bin 255 - t; the bin where
+// the running mass from the top reaches `need` becomes the next digit.
+__device__ __forceinline__ void topp_pick_digit(ToppShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t need = sh.need;  // read before the barrier below: rewritten after it
+  uint64_t q = 0, qx = 0;
+  uint32_t k = 0, kx = 0;
+  if (wave < 4) {
+    const int b = 255 - tid;
+    q = sh.h_mass[b];
+    k = sh.h_cnt[b];
+    const uint64_t qs = wave_incl_scan_u62(q);
+    const uint32_t ks = wave_incl_scan(k);
+    if (lane == 63) {
+      sh.sq[wave] = qs;
+      sh.sc[wave] = ks;
+    }
+    qx = qs - q;
+    kx = ks - k;
+  }
+  __syncthreads();
+  if (wave < 4) {
+    for (int w = 0; w < wave; ++w) {
+      qx += sh.sq[w];
+      kx += sh.sc[w];
+    }
+    if (q > 0 && qx < need && need - qx <= q) {
+      sh.digit = (uint32_t)(255 - tid);
+      sh.need = need - qx;
+      sh.above += kx;
+    }
+  }
+  __syncthreads();
+}
+
+// Candidate score bits held or re-read by a kernel: ExpHist counts every
+// positive value into its exponent bin; SigHist counts the values of exponent
+// bin e1 whose significand matches `prefix` above bit shift + 8, by the
+// significand digit at `shift`.
+__device__ __forceinline__ void topp_add_exp(ToppShared& sh, uint32_t b) {
+  if (b) {
+    const uint32_t e = b >> 23;
+    atomicAdd(&sh.h_cnt[e], 1u);
+    atomicAdd((unsigned long long*)&sh.h_mass[e], (unsigned long long)sig_of(b));
+  }
+}
+__device__ __forceinline__ void topp_add_sig(ToppShared& sh, uint32_t b, int e1, int shift, uint32_t prefix) {
+  const uint32_t m = sig_of(b);
+  if (b && (int)(b >> 23) == e1 && (m >> (shift + 8)) == (prefix >> (shift + 8))) {
+    const uint32_t dg = (m >> shift) & 255u;
+    atomicAdd(&sh.h_cnt[dg], 1u);
+    atomicAdd((unsigned long long*)&sh.h_mass[dg], (unsigned long long)m);
+  }
+}
+
+// Rows of any length: the scores are re-read from memory in every pass (the
+// pooled row is written once to the scratch a.pooled_row and re-read).
+__global__ __launch_bounds__(kSelThreads) void topp_kernel(const ToppArgs a) {
+  __shared__ ToppShared sh;
+  __shared__ uint32_t sm_w[kSelWaves + 1];
+
+  const int tid = threadIdx.x;
   const int h0 = a.pooled ? 0 : blockIdx.x;
   const int h1 = a.pooled ? a.rows : h0 + 1;
   const int64_t n = a.n;
@@ -90,144 +281,43 @@ __global__ __launch_bounds__(kSelThreads) void topp_kernel(const ToppArgs a) {
   for (int h = h0; h < h1; ++h)
     for (int64_t i = tid; i < nsink; i += kSelThreads) a.idx[(int64_t)h * a.idx_stride + i] = (int32_t)i;
 
-  // ---- 1. scale, fixed-point masses, total, threshold ---------------------
-  uint32_t mb = 0;
-  for (int h = h0; h < h1; ++h) {
-    const float* s = a.score + (int64_t)h * a.score_stride;
-    for (int64_t j = c_lo + tid; j < c_hi; j += kSelThreads) mb = max(mb, pos_bits(s[j]));
+  if (a.pooled) {
+    for (int64_t j = c_lo + tid; j < c_hi; j += kSelThreads) a.pooled_row[j - c_lo] = pooled_bits(a, j);
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off, 64));
-  if (lane == 0) sm_w[wave] = mb;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t m = 0;
-    for (int w = 0; w < kSelWaves; ++w) m = max(m, sm_w[w]);
-    const int64_t terms = (int64_t)(h1 - h0) * ncand;
-    const int lg = terms <= 1 ? 0 : 64 - __clzll((unsigned long long)(terms - 1));
-    int E = 0;
-    if (m >> 23) E = (int)(m >> 23) - 126;
-    else if (m) E = (31 - __clz((int)m)) - 148;
-    sm_S = 62 - E - lg;
-  }
-  __syncthreads();
-  const int S = sm_S;
-  auto mass_of = [&](int64_t j) -> uint64_t {  // candidate position j
-    if (a.pooled) return a.mass[j - c_lo];
-    return fixed_mass(a.score[(int64_t)h0 * a.score_stride + j], S);
+  topp_clear_hist(sh);
+  __syncthreads();  // the pooled row written above is read back by other threads
+  auto bits_of = [&](int64_t j) -> uint32_t {  // candidate position j
+    if (a.pooled) return a.pooled_row[j - c_lo];
+    return pos_bits(a.score[(int64_t)h0 * a.score_stride + j]);
   };
-  uint64_t part = 0;
-  for (int64_t j = c_lo + tid; j < c_hi; j += kSelThreads) {
-    uint64_t u;
-    if (a.pooled) {
-      u = 0;
-      for (int h = 0; h < a.rows; ++h) u += fixed_mass(a.score[(int64_t)h * a.score_stride + j], S);
-      a.mass[j - c_lo] = u;
-    } else {
-      u = fixed_mass(a.score[(int64_t)h0 * a.score_stride + j], S);
-    }
-    part += u;
-  }
-  part = wave_sum_u64(part);
-  if (lane == 0) sm_q[wave] = part;
+
+  // ---- 1-2. exponent histogram, then the walk over the exponent bins -------
+  for (int64_t j = c_lo + tid; j < c_hi; j += kSelThreads) topp_add_exp(sh, bits_of(j));
   __syncthreads();
-  if (tid == 0) {
-    uint64_t U = 0;
-    for (int w = 0; w < kSelWaves; ++w) U += sm_q[w];
-    const unsigned __int128 prod = (unsigned __int128)a.lam_m * U;
-    uint64_t theta;
-    if (a.lam_sh >= 128) {
-      theta = prod != 0;
-    } else {
-      const unsigned __int128 low = prod & ((((unsigned __int128)1) << a.lam_sh) - 1);
-      theta = (uint64_t)(prod >> a.lam_sh) + (low != 0);
-    }
-    sm_theta = theta;
-    sm_need = theta;
-    sm_gmass = U;
-    sm_gcnt = (uint32_t)ncand;
-    sm_above = 0;
-  }
-  __syncthreads();  // the pooled masses written above are read back by other threads below
+  topp_walk_exponents(sh, a.lam_m, a.lam_sh);
+  __syncthreads();
 
-  // ---- 2. radix passes on the masses --------------------------------------
-  uint64_t vstar = ~0ull;  // nothing is retained when theta == 0
+  // ---- 3. radix passes over the significands of bin e1 ---------------------
+  const int e1 = sh.e1;
+  uint32_t vbits = 0xFFFFFFFFu;  // nothing is retained when e1 < 0
   uint32_t take = 0, c = 0;
-  if (sm_theta > 0) {
-    // masses are below 2^(62 - lg) per row, times the rows summed when pooled
-    const int64_t terms = (int64_t)(h1 - h0) * ncand;
-    const int lg = terms <= 1 ? 0 : 64 - __clzll((unsigned long long)(terms - 1));
-    const int lgr = h1 - h0 <= 1 ? 0 : 32 - __clz(h1 - h0 - 1);
-    const int kb = 62 - lg + lgr < 62 ? 62 - lg + lgr : 62;
-    const int passes = (kb + 7) / 8;
-    uint64_t prefix = 0;
+  if (e1 >= 0) {
+    uint32_t prefix = 0;
 #pragma unroll 1
-    for (int pass = 0; pass < passes; ++pass) {
-      const int shift = 8 * (passes - 1 - pass);
-      for (int b = tid; b < kToppBins; b += kSelThreads) {
-        h_cnt[b] = 0u;
-        h_mass[b] = 0u;
-      }
+    for (int shift = 16; shift >= 0; shift -= 8) {
+      topp_clear_hist(sh);
       __syncthreads();
-      for (int64_t j = c_lo + tid; j < c_hi; j += kSelThreads) {
-        const uint64_t u = mass_of(j);
-        const bool in_group = pass == 0 || (u >> (shift + 8)) == (prefix >> (shift + 8));
-        const uint32_t dg = (uint32_t)(u >> shift) & 255u;
-        if (in_group && dg != 0u) {
-          atomicAdd(&h_cnt[dg], 1u);
-          atomicAdd((unsigned long long*)&h_mass[dg], (unsigned long long)u);
-        }
-      }
+      for (int64_t j = c_lo + tid; j < c_hi; j += kSelThreads) topp_add_sig(sh, bits_of(j), e1, shift, prefix);
       __syncthreads();
-      // bins from the top: thread t < 256 owns bin 255 - t; bin 0 (t = 255) is
-      // the group minus the others
-      // read before the barrier below: the crossing thread rewrites them after it
-      const uint64_t need = sm_need, gmass = sm_gmass;
-      const uint32_t gcnt = sm_gcnt;
-      uint64_t q = 0, qx = 0;
-      uint32_t k = 0, kx = 0;
-      if (wave < 4) {
-        const int b = 255 - tid;
-        q = b ? h_mass[b] : 0u;
-        k = b ? h_cnt[b] : 0u;
-        const uint64_t qs = wave_incl_scan_u62(q);
-        const uint32_t ks = wave_incl_scan(k);
-        if (lane == 63) {
-          sm_q[wave] = qs;
-          sm_c[wave] = ks;
-        }
-        qx = qs - q;
-        kx = ks - k;
-      }
-      __syncthreads();
-      if (wave < 4) {
-        for (int w = 0; w < wave; ++w) {
-          qx += sm_q[w];
-          kx += sm_c[w];
-        }
-        if (tid == 255) {
-          q = gmass - qx;
-          k = gcnt - kx;
-        }
-        if (q > 0 && qx < need && need - qx <= q) {
-          sm_digit = (uint32_t)(255 - tid);
-          sm_need = need - qx;
-          sm_above += kx;
-          sm_gmass = q;
-          sm_gcnt = k;
-        }
-      }
-      __syncthreads();
-      prefix |= (uint64_t)sm_digit << shift;
-      __syncthreads();
+      topp_pick_digit(sh);
+      prefix |= sh.digit << shift;
     }
-    vstar = prefix;  // > 0: the crossing group carries mass
-    const uint64_t need = sm_need;
-    take = (uint32_t)((need + vstar - 1) / vstar);
-    c = sm_above + take;
+    vbits = ((uint32_t)e1 << 23) | (prefix & 0x7fffffu);
+    take = (uint32_t)((sh.need + prefix - 1) / prefix);  // prefix = M* > 0
+    c = sh.above + take;
   }
 
-  // ---- 3. V_R, uniform picks, ascending output ----------------------------
+  // ---- 4. V_R, uniform picks, ascending output ----------------------------
   const int64_t left = ncand - c;
   int64_t n_u = a.fill_mode == 0 ? a.budget - (int64_t)c : a.budget;
   n_u = n_u < 0 ? 0 : (n_u > left ? left : n_u);
@@ -236,11 +326,11 @@ __global__ __launch_bounds__(kSelThreads) void topp_kernel(const ToppArgs a) {
   for (int64_t t0 = c_lo; t0 < c_hi; t0 += kSelThreads) {
     const int64_t j = t0 + tid;
     const bool valid = j < c_hi;
-    const uint64_t u = valid ? mass_of(j) : 0u;
-    const bool tie = valid && u == vstar;
+    const uint32_t b = valid ? bits_of(j) : 0u;
+    const bool tie = valid && b == vbits;
     uint32_t n_tie, n_left, n_out;
     const uint32_t tie_rank = tie_seen + block_flag_rank(tie, sm_w, &n_tie);
-    const bool in_r = valid && (u > vstar || (tie && tie_rank < take));
+    const bool in_r = valid && e1 >= 0 && (b > vbits || (tie && tie_rank < take));
     const uint32_t lr = left_seen + block_flag_rank(valid && !in_r, sm_w, &n_left);
     bool pick = false;
     if (valid && !in_r && n_u > 0) {
@@ -263,26 +353,18 @@ __global__ __launch_bounds__(kSelThreads) void topp_kernel(const ToppArgs a) {
 }
 
 // Same selection for up to kRunMax candidates (Qwen2-7B video scores, 25,088
-// candidates: 121 -> 55 us per row, 119 -> 77 us pooled), with every mass in
-// registers:
-// thread t holds candidates t, t + 1024, t + 2048, ... (coalesced loads), so
-// the radix passes touch no global memory.  Index-order ranks (ties before a
-// candidate, leftovers before it, outputs before it) come from one ballot per
-// register slot and wave and one workgroup scan over the (slot, wave) counts
-// in slot-major order, instead of three ballots and barriers per 1024
-// candidates; the pick test runs in 32-bit arithmetic (every operand < 2^30).
+// candidates per row) with every score in registers: thread t holds
+// candidates t, t + 1024, t + 2048, ... (coalesced loads), so the passes touch
+// no global memory.  Index-order ranks (ties before a candidate, leftovers
+// before it, outputs before it) come from one ballot per register slot and
+// wave and one workgroup scan over the (slot, wave) counts in slot-major
+// order; the pick test runs in 32-bit arithmetic (every operand < 2^30).
 constexpr int kRunPer = 32;
 constexpr int kRunMax = kSelThreads * kRunPer;
 
 __global__ __launch_bounds__(kSelThreads) void topp_run_kernel(const ToppArgs a) {
-  __shared__ uint32_t h_cnt[kToppBins];
-  __shared__ uint64_t h_mass[kToppBins];
+  __shared__ ToppShared sh;
   __shared__ uint32_t sm_w[kSelWaves + 1];
-  __shared__ uint64_t sm_q[kSelWaves];
-  __shared__ uint32_t sm_c[kSelWaves];
-  __shared__ uint64_t sm_need, sm_gmass, sm_theta;
-  __shared__ uint32_t sm_digit, sm_gcnt, sm_above;
-  __shared__ int sm_S;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h0 = a.pooled ? 0 : blockIdx.x;
@@ -299,152 +381,57 @@ __global__ __launch_bounds__(kSelThreads) void topp_run_kernel(const ToppArgs a)
   for (int h = h0; h < h1; ++h)
     for (int64_t i = tid; i < nsink; i += kSelThreads) a.idx[(int64_t)h * a.idx_stride + i] = (int32_t)i;
 
-  // ---- 1. scale, fixed-point masses, total, threshold ---------------------
-  uint32_t mb = 0;
-  for (int h = h0; h < h1; ++h) {
-    const float* s = a.score + (int64_t)h * a.score_stride + c_lo + tid;
+  uint32_t bits[kRunPer];
 #pragma unroll
-    for (int u = 0; u < kRunPer; ++u)
-      if (valid(u)) mb = max(mb, pos_bits(s[kSelThreads * u]));
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off, 64));
-  if (lane == 0) sm_w[wave] = mb;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t m = 0;
-    for (int w = 0; w < kSelWaves; ++w) m = max(m, sm_w[w]);
-    const int64_t terms = (int64_t)(h1 - h0) * ncand;
-    const int lg = terms <= 1 ? 0 : 64 - __clzll((unsigned long long)(terms - 1));
-    int E = 0;
-    if (m >> 23) E = (int)(m >> 23) - 126;
-    else if (m) E = (31 - __clz((int)m)) - 148;
-    sm_S = 62 - E - lg;
-  }
-  __syncthreads();
-  const int S = sm_S;
-  uint64_t mass[kRunPer];
-#pragma unroll
-  for (int u = 0; u < kRunPer; ++u) mass[u] = 0u;
-  for (int h = h0; h < h1; ++h) {
-    const float* s = a.score + (int64_t)h * a.score_stride + c_lo + tid;
-#pragma unroll
-    for (int u = 0; u < kRunPer; ++u)
-      if (valid(u)) mass[u] += fixed_mass(s[kSelThreads * u], S);
-  }
-  uint64_t part = 0;
-#pragma unroll
-  for (int u = 0; u < kRunPer; ++u) part += mass[u];
-  part = wave_sum_u64(part);
-  if (lane == 0) sm_q[wave] = part;
-  __syncthreads();
-  if (tid == 0) {
-    uint64_t U = 0;
-    for (int w = 0; w < kSelWaves; ++w) U += sm_q[w];
-    const unsigned __int128 prod = (unsigned __int128)a.lam_m * U;
-    uint64_t theta;
-    if (a.lam_sh >= 128) {
-      theta = prod != 0;
-    } else {
-      const unsigned __int128 low = prod & ((((unsigned __int128)1) << a.lam_sh) - 1);
-      theta = (uint64_t)(prod >> a.lam_sh) + (low != 0);
+  for (int u = 0; u < kRunPer; ++u) {
+    bits[u] = 0u;
+    if (valid(u)) {
+      const int64_t j = c_lo + tid + (int64_t)kSelThreads * u;
+      bits[u] = a.pooled ? pooled_bits(a, j) : pos_bits(a.score[(int64_t)h0 * a.score_stride + j]);
     }
-    sm_theta = theta;
-    sm_need = theta;
-    sm_gmass = U;
-    sm_gcnt = (uint32_t)ncand;
-    sm_above = 0;
   }
+  topp_clear_hist(sh);
   __syncthreads();
 
-  // ---- 2. radix passes on the masses (in registers) -------------------------
-  uint64_t vstar = ~0ull;  // nothing is retained when theta == 0
+  // ---- 1-2. exponent histogram, then the walk over the exponent bins -------
+#pragma unroll
+  for (int u = 0; u < kRunPer; ++u) topp_add_exp(sh, bits[u]);  // invalid slots hold 0
+  __syncthreads();
+  topp_walk_exponents(sh, a.lam_m, a.lam_sh);
+  __syncthreads();
+
+  // ---- 3. radix passes over the significands of bin e1 ---------------------
+  const int e1 = sh.e1;
+  uint32_t vbits = 0xFFFFFFFFu;  // nothing is retained when e1 < 0
   uint32_t take = 0, c = 0;
-  if (sm_theta > 0) {
-    const int64_t terms = (int64_t)(h1 - h0) * ncand;
-    const int lg = terms <= 1 ? 0 : 64 - __clzll((unsigned long long)(terms - 1));
-    const int lgr = h1 - h0 <= 1 ? 0 : 32 - __clz(h1 - h0 - 1);
-    const int kb = 62 - lg + lgr < 62 ? 62 - lg + lgr : 62;
-    const int passes = (kb + 7) / 8;
-    uint64_t prefix = 0;
+  if (e1 >= 0) {
+    uint32_t prefix = 0;
 #pragma unroll 1
-    for (int pass = 0; pass < passes; ++pass) {
-      const int shift = 8 * (passes - 1 - pass);
-      for (int b = tid; b < kToppBins; b += kSelThreads) {
-        h_cnt[b] = 0u;
-        h_mass[b] = 0u;
-      }
+    for (int shift = 16; shift >= 0; shift -= 8) {
+      topp_clear_hist(sh);
       __syncthreads();
 #pragma unroll
-      for (int u = 0; u < kRunPer; ++u) {
-        const uint64_t m = mass[u];
-        const bool in_group = pass == 0 || (m >> (shift + 8)) == (prefix >> (shift + 8));
-        const uint32_t dg = (uint32_t)(m >> shift) & 255u;
-        if (valid(u) && in_group && dg != 0u) {
-          atomicAdd(&h_cnt[dg], 1u);
-          atomicAdd((unsigned long long*)&h_mass[dg], (unsigned long long)m);
-        }
-      }
+      for (int u = 0; u < kRunPer; ++u) topp_add_sig(sh, bits[u], e1, shift, prefix);
       __syncthreads();
-      // bins from the top: thread t < 256 owns bin 255 - t; bin 0 (t = 255) is
-      // the group minus the others; read before the barrier below (the
-      // crossing thread rewrites them after it)
-      const uint64_t need = sm_need, gmass = sm_gmass;
-      const uint32_t gcnt = sm_gcnt;
-      uint64_t q = 0, qx = 0;
-      uint32_t k = 0, kx = 0;
-      if (wave < 4) {
-        const int b = 255 - tid;
-        q = b ? h_mass[b] : 0u;
-        k = b ? h_cnt[b] : 0u;
-        const uint64_t qs = wave_incl_scan_u62(q);
-        const uint32_t ks = wave_incl_scan(k);
-        if (lane == 63) {
-          sm_q[wave] = qs;
-          sm_c[wave] = ks;
-        }
-        qx = qs - q;
-        kx = ks - k;
-      }
-      __syncthreads();
-      if (wave < 4) {
-        for (int w = 0; w < wave; ++w) {
-          qx += sm_q[w];
-          kx += sm_c[w];
-        }
-        if (tid == 255) {
-          q = gmass - qx;
-          k = gcnt - kx;
-        }
-        if (q > 0 && qx < need && need - qx <= q) {
-          sm_digit = (uint32_t)(255 - tid);
-          sm_need = need - qx;
-          sm_above += kx;
-          sm_gmass = q;
-          sm_gcnt = k;
-        }
-      }
-      __syncthreads();
-      prefix |= (uint64_t)sm_digit << shift;
-      __syncthreads();
+      topp_pick_digit(sh);
+      prefix |= sh.digit << shift;
     }
-    vstar = prefix;  // > 0: the crossing group carries mass
-    const uint64_t need = sm_need;
-    take = (uint32_t)((need + vstar - 1) / vstar);
-    c = sm_above + take;
+    vbits = ((uint32_t)e1 << 23) | (prefix & 0x7fffffu);
+    take = (uint32_t)((sh.need + prefix - 1) / prefix);  // prefix = M* > 0
+    c = sh.above + take;
   }
 
-  // ---- 3. V_R, uniform picks, ascending output ----------------------------
+  // ---- 4. V_R, uniform picks, ascending output ----------------------------
   // exclusive index-order rank of every slot's flag: one ballot per slot and
   // wave, one scan over the (slot, wave) counts in slot-major order into tab;
   // a slot's rank is then tab[slot][wave] plus its lanes below in the ballot
   __shared__ uint32_t tab[kRunPer * kSelWaves];
-  auto flag_scan = [&](uint32_t bits) -> uint32_t {
+  auto flag_scan = [&](uint32_t fl) -> uint32_t {
     __syncthreads();  // the previous scan's tab is no longer read
 #pragma unroll
     for (int u = 0; u < kRunPer; ++u) {
       if (u < R) {  // uniform
-        const uint64_t bb = __ballot((bits >> u) & 1u);
+        const uint64_t bb = __ballot((fl >> u) & 1u);
         if (lane == 0) tab[u * kSelWaves + wave] = (uint32_t)__popcll(bb);
       }
     }
@@ -456,22 +443,23 @@ __global__ __launch_bounds__(kSelThreads) void topp_run_kernel(const ToppArgs a)
     __syncthreads();
     return total;
   };
-  auto slot_rank = [&](uint32_t bits, int u) -> uint32_t {
-    const uint64_t bb = __ballot((bits >> u) & 1u);
+  auto slot_rank = [&](uint32_t fl, int u) -> uint32_t {
+    const uint64_t bb = __ballot((fl >> u) & 1u);
     return tab[u * kSelWaves + wave] +
            __builtin_amdgcn_mbcnt_hi((uint32_t)(bb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bb, 0u));
   };
   uint32_t tie_bits = 0;
 #pragma unroll
   for (int u = 0; u < kRunPer; ++u)
-    if (valid(u) && mass[u] == vstar) tie_bits |= 1u << u;
+    if (valid(u) && bits[u] == vbits) tie_bits |= 1u << u;
   flag_scan(tie_bits);
   uint32_t in_bits = 0;
 #pragma unroll
   for (int u = 0; u < kRunPer; ++u) {
     if (u < R) {  // uniform: every lane takes part in the ballot
       const uint32_t r = slot_rank(tie_bits, u);
-      if (valid(u) && (mass[u] > vstar || (((tie_bits >> u) & 1u) && r < take))) in_bits |= 1u << u;
+      if (valid(u) && e1 >= 0 && (bits[u] > vbits || (((tie_bits >> u) & 1u) && r < take)))
+        in_bits |= 1u << u;
     }
   }
   uint32_t left_bits = 0;

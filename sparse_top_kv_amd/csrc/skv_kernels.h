@@ -158,7 +158,7 @@ struct ToppArgs {
   int64_t idx_stride;
   int32_t* count;
   int32_t* count_r;         // may be null
-  uint64_t* mass;           // pooled: candidates x 8 bytes of scratch
+  uint32_t* pooled_row;     // pooled, beyond 32K candidates: each candidate's pooled fp32 bits (scratch)
 };
 hipError_t launch_select_topp(const ToppArgs& a, hipStream_t stream);
 

@@ -1,5 +1,6 @@
 """GPU parity of the SpecVLM selection (skv_select_topp) against the oracle:
-index sets and counts bit-exact on identical fp32 scores."""
+index sets and counts bit-exact on identical fp32 scores, including scores
+whose masses span the whole fp32 range (Stage I compares exact sums)."""
 import numpy as np
 import pytest
 import torch
@@ -93,3 +94,37 @@ def test_topp_many_rows_pooled_and_repeatable():
     a = _run(s, 8192, 0, 32, 0.5, 0.9, True, 0)
     b = _run(s, 8192, 0, 32, 0.5, 0.9, True, 0)
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def _wide(rng, shape, zeros=0.1):
+    """Binary exponents over about 2^-149 .. 2^20 in one row (subnormals included)."""
+    e = rng.integers(-150, 21, shape).astype(np.float64)
+    x = rng.random(shape) * np.exp2(e)
+    x[rng.random(shape) < zeros] = 0.0
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("n", [3000, 40000])
+def test_topp_exact_masses_over_the_fp32_range(n):
+    """Register-resident rows (3000) and re-read rows (40000 candidates): the
+    crossing may sit in any exponent bin, and lambda = 1 must keep every
+    positive score, subnormals included."""
+    banner(f"topp wide dynamic range n={n}")
+    rng = np.random.default_rng(n)
+    s = _wide(rng, (3, n))
+    for lam in (1.0, 0.5, 0.37, 1e-300, float(np.nextafter(0.5, 1.0))):
+        for pooled in (False, True):
+            gi, gc, gr = _run(s, n, 2, 16, lam, 0.9, pooled, 0)
+    gi, gc, gr = _run(s, n, 0, 0, 1.0, 1.0, False, 0)
+    for h in range(3):
+        assert np.array_equal(gi[h, :gc[h]], np.flatnonzero(s[h] > 0))
+
+
+def test_topp_threshold_a_tiny_mass_past_a_prefix():
+    banner("topp threshold 2^-91 past a prefix")
+    s = np.zeros((2, 1000), np.float32)
+    s[:, 10] = 1.0
+    s[:, 500] = 1.0
+    s[0, 700] = 2.0 ** -90   # half the total is 1 + 2^-91: both ones are needed
+    _, _, gr = _run(s, 1000, 0, 0, 0.5, 1.0, False, 0)
+    assert gr.tolist() == [2, 1]
