@@ -294,10 +294,14 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
     short4_t ahi[NG], alo[NG];
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
+      // a row still without a reference (-inf) has no visible key in this
+      // tile either (any would have triggered the rescale), so every sv is
+      // -inf and the probabilities are 0
+      const float mref = m[gi] == kNegInf ? 0.0f : m[gi];
       float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[r] = fast_exp2(sv[gi][r] - m[gi]);
+        p[r] = fast_exp2(sv[gi][r] - mref);
         l[gi] += p[r];
       }
       const uint32_t h01 = pack_bf16(p[0], p[1]), h23 = pack_bf16(p[2], p[3]);
@@ -326,7 +330,8 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       const float mn = fmaxf(m[gi], row_max(sv[gi]));
-      const float alpha = fast_exp2(m[gi] - mn);
+      // unchanged reference (also -inf to -inf): nothing to rescale
+      const float alpha = m[gi] == mn ? 1.0f : fast_exp2(m[gi] - mn);
       l[gi] *= alpha;
       m[gi] = mn;
       float ar[4];
@@ -370,17 +375,17 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
   for (int u = 0; u < S - 1; ++u)
     if (u < nst) issue(ring(u), u);
   if (nst > 0) {
-    // reference: the first tile's max per row (0 for a row with no visible
-    // key there).  Only the prologue's copies are in flight here: steps 1 ..
+    // reference: the first tile's max per row; -inf for a row with no
+    // visible key there (causal pass), which the first tile that shows the
+    // row a key replaces through the rescale (softmax is shift-invariant, so
+    // no fixed stand-in value may be used: logits far below it would
+    // underflow).  Only the prologue's copies are in flight here: steps 1 ..
     // min(nst, S - 1) - 1 are newer than step 0.
     wait_newer<S - 2, 2 * NI>(nst - 1 < S - 2 ? nst - 1 : S - 2);
     float sv[NG][4];
     logits(&st0[0][0], 0, sv);
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      const float mx = row_max(sv[gi]);
-      m[gi] = mx == kNegInf ? 0.0f : mx;
-    }
+    for (int gi = 0; gi < NG; ++gi) m[gi] = row_max(sv[gi]);
     for (int k = 0; k < nst;) {
 #pragma unroll
       for (int u = 0; u < S; ++u) {

@@ -47,6 +47,36 @@ def test_verify_matches_oracle(hq, hkv, d, gamma, n):
         assert (od - out[t]).abs().max().item() <= 2e-3
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(28, 4, 128), (32, 8, 128), (8, 8, 64)])
+@pytest.mark.parametrize("gamma,n", [(16, 777), (5, 300), (13, 2000)])
+def test_verify_with_every_logit_far_below_zero(hq, hkv, d, gamma, n):
+    """Softmax is shift-invariant: with every logit near -100 a row whose
+    wave saw no visible key in its first tile must still take its reference
+    from the keys it does see (a stand-in reference of 0 would underflow every
+    probability to zero and return out = 0, lse = -inf)."""
+    banner(f"verify logits near -100 hq={hq} hkv={hkv} d={d} gamma={gamma} n={n}")
+    rng = np.random.default_rng(31)
+    u = rng.standard_normal(d).astype(np.float32)
+    u /= np.linalg.norm(u)
+    kf = 4.0 * u + 0.05 * rng.standard_normal((hkv, n + 2, d)).astype(np.float32)
+    # q . k * d^-0.5 ~= -100 for every key: q = -c u with 4 c d^-0.5 = 100
+    c = 100.0 * np.sqrt(d) / 4.0
+    qf = -c * u + 0.05 * rng.standard_normal((gamma, hq, d)).astype(np.float32)
+    q, k = synth.bf16_bits(qf.astype(np.float32)), synth.bf16_bits(kf.astype(np.float32))
+    v = _rand((hkv, n + 2, d), 32)
+    ref_o, ref_l = oracle.verify(q, k, v, n)
+    assert ref_l.max() < -80.0  # every row's normaliser is far below zero
+    qt, kt, vt = dev(q), dev(k), dev(v)
+    out = torch.full((gamma, hq, d), float("nan"), device="cuda")
+    lse = torch.full((gamma, hq), float("nan"), device="cuda")
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n, gamma)
+    skv.skv_verify(qt, kt, vt, n, out, lse, ws)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(host(lse)))
+    assert np.abs(host(out) - ref_o).max() <= 2e-3
+    assert np.abs(host(lse) - ref_l).max() <= 1e-4
+
+
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (28, 4, 128), (4, 4, 64), (8, 1, 128)])
 @pytest.mark.parametrize("W,n", [(32, 32), (32, 1000), (2, 300), (32, 4097), (20, 257)])
 def test_obs_score_matches_oracle(hq, hkv, d, W, n):
