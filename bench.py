@@ -60,6 +60,36 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# Dense decode baselines of "Where Activation Sparsity and KV-Cache Sparsity
+# Cross in LLM Decoding", "The Attention Baseline": the same attention read
+# through an eager masked implementation (matmul, explicit mask, softmax,
+# matmul) and through one fused attention kernel with no split over the
+# sequence (PyTorch SDPA, flash backend).  Both are PyTorch's own kernels,
+# timed only as baselines.  q [Hq][d] bf16; k, v [Hkv][n_cap][d] bf16 (rows
+# [0, L) are read); returns [Hkv][G][d] in bf16 for query head h * G + g.
+
+def masked_decode(q, k, v, L, scale, mask=None):
+    import torch
+    hkv, d = k.shape[0], k.shape[2]
+    G = q.shape[0] // hkv
+    qg = q.view(hkv, G, d).transpose(1, 2).contiguous()                 # [Hkv][d][G]
+    lg = torch.matmul(k[:, :L], qg).float() * scale                      # [Hkv][L][G]
+    if mask is not None:
+        lg = lg + mask
+    pr = torch.softmax(lg, dim=1).to(q.dtype).transpose(1, 2).contiguous()
+    return torch.matmul(pr, v[:, :L])                                   # [Hkv][G][d]
+
+
+def fused_decode(q, k, v, L, scale):
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    hkv, d = k.shape[0], k.shape[2]
+    G = q.shape[0] // hkv
+    with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+        o = F.scaled_dot_product_attention(q.view(1, hkv, G, d), k[None, :, :L], v[None, :, :L], scale=scale)
+    return o[0]
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,9 +174,6 @@ def main():
         "The Attention Baseline").  The masked and fused paths are PyTorch's
         own (matmul + softmax, and SDPA's flash kernel); they are baselines
         only.  Returns speedups, each path's HBM fraction and the byte bounds."""
-        import torch.nn.functional as F
-        from torch.nn.attention import SDPBackend, sdpa_kernel
-        G = hq // hkv
         scale = 1.0 / math.sqrt(d)
         res = {}
         for nn in (2048, 8192, 32768, 131072):
@@ -160,15 +187,10 @@ def main():
             sink_cnt = torch.full((hkv,), 4, dtype=torch.int32, device="cuda")
 
             def masked(q, k, v, L):
-                qg = q.view(hkv, G, d).transpose(1, 2).contiguous()          # [Hkv][d][G]
-                lg = torch.matmul(k[:, :L], qg).float() * scale + mask[L]    # [Hkv][L][G]
-                pr = torch.softmax(lg, dim=1).to(q.dtype).transpose(1, 2).contiguous()
-                return torch.matmul(pr, v[:, :L])                            # [Hkv][G][d]
+                return masked_decode(q, k, v, L, scale, mask[L])
 
             def fused(q, k, v, L):
-                with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
-                    return F.scaled_dot_product_attention(q.view(1, hkv, G, d), k[None, :, :L],
-                                                          v[None, :, :L], scale=scale)
+                return fused_decode(q, k, v, L, scale)
 
             paths = {
                 "masked": (lambda i: masked(big[i % 2]["q"], big[i % 2]["k"], big[i % 2]["v"], nn),

@@ -374,3 +374,41 @@ def test_attend_sparse_many_heads_ragged_counts(hq, hkv, n, tail, d):
     assert np.abs(o - ref_o).max() <= to
     assert np.abs(l[~empty] - ref_l[~empty]).max(initial=0) <= tl
     assert torch.equal(out, out2)  # the work list is deterministic
+
+
+@pytest.mark.parametrize("kind", ["window", "random"])
+def test_attend_sparse_128k_thirty_percent_long_chunks(kind):
+    """The Llama-3.1-8B shape at 128K context with 30 % of the cache kept
+    (39,322 rows per kv head): chunks of about 1,280 gathered rows, past the
+    512-row range of the smaller shapes, so every workgroup stages a long
+    offset list and every wave walks many tiles.  "window": four sinks plus
+    the recent run (the sink-plus-window baseline of the attention-baseline
+    comparison); "random": a seeded 30 % subset of the history plus a recent
+    run of 64."""
+    banner(f"sparse 128K 30% kind={kind}")
+    hq, hkv, d, n = 32, 8, 128, 131072
+    keep = int(round(0.3 * n))
+    q = _rand((hq, d), 41, "bf16")
+    k = _cache(hkv, n, d, 42, "bf16", cap_extra=0)
+    v = _cache(hkv, n, d, 43, "bf16", cap_extra=0)
+    if kind == "window":
+        tail = n - (keep - 4)
+        idx = np.tile(np.arange(4, dtype=np.int32), (hkv, 1))
+        cnt = np.full(hkv, 4, np.int32)
+    else:
+        tail = n - 64
+        idx, cnt = _random_sets(hkv, tail, keep - 64, 44, max_count=keep - 64)
+    ref_o, ref_l = oracle.attend_sparse(q, k, v, n, idx, cnt, tail)
+    qt, kt, vt = dev(q), dev(k), dev(v)
+    out = torch.full((hq, d), float("nan"), device="cuda")
+    lse = torch.full((hq,), float("nan"), device="cuda")
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n)
+    it, ct = dev(idx), dev(cnt)
+    skv.skv_attend_sparse(qt, kt, vt, n, it, ct, tail, out, lse, ws)
+    out2 = torch.empty_like(out)
+    skv.skv_attend_sparse(qt, kt, vt, n, it, ct, tail, out2, lse, ws)
+    torch.cuda.synchronize()
+    to, tl = TOL["bf16"]
+    assert np.abs(host(out) - ref_o).max() <= to
+    assert np.abs(host(lse) - ref_l).max() <= tl
+    assert torch.equal(out, out2)
