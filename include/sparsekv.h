@@ -171,6 +171,25 @@ skv_status skv_attend_sparse(const skv_problem* p, const void* q, const void* k,
                              float* out, float* lse, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* skv_attend_sparse without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments (minus ws, ws_bytes),
+ * validation, kernels and results as skv_attend_sparse.  Its scratch is a
+ * fixed array of SKV_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * held until the process ends; the first call on a device looks it up and
+ * enqueues a fill kernel on `stream` that clears its header.  A call whose
+ * scratch (SKV_WS_HEADER_BYTES plus the partials of its split-K plan, the
+ * same amount skv_workspace_size reserves for it) exceeds that size returns
+ * SKV_ERR_WORKSPACE and enqueues nothing.  No call allocates or frees
+ * memory.  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (different streams, or different host threads without
+ * ordering) race and give undefined results. */
+#define SKV_NOALLOC_SCRATCH_BYTES (16 * 1048576)
+skv_status skv_attend_sparse_noalloc(const skv_problem* p, const void* q, const void* k,
+                                     const void* v, int64_t n, const int32_t* idx,
+                                     int64_t idx_stride, const int32_t* count,
+                                     int64_t tail_start, float* out, float* lse, void* stream);
+
 /* Dense decode attention ([BX] "The Attention Baseline": the dense step reads
  * the whole cache through the same split-K kernel): q [Hq][d] over keys
  * [0, n).  out [Hq][d], lse [Hq] (may be NULL). */

@@ -3,8 +3,8 @@
 Argument marshalling only: every step runs in the HIP kernels of
 ``libsparsekv.so`` (built from ``csrc/`` by ``sparse_top_kv_amd.build``).  The
 functions carry the C names (``skv_score``, ``skv_select``,
-``skv_attend_sparse``, ``skv_attend_dense``, ``skv_verify``, ``skv_gather``,
-``skv_select_topp``, ``skv_budgets``)
+``skv_attend_sparse``, ``skv_attend_sparse_noalloc``, ``skv_attend_dense``,
+``skv_verify``, ``skv_gather``, ``skv_select_topp``, ``skv_budgets``)
 and take torch tensors on a ROCm device; torch provides device memory and the
 current stream, nothing else.  A missing library raises at the first call.
 
@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libsparsekv.so")
 SKV_OK, SKV_ERR_INVALID_ARG, SKV_ERR_UNSUPPORTED, SKV_ERR_WORKSPACE, SKV_ERR_HIP = range(5)
 SKV_F32, SKV_BF16 = 0, 1
 SKV_WS_HEADER_BYTES = 1048576
+SKV_NOALLOC_SCRATCH_BYTES = 16 * 1048576
 _ALIGN = 256
 
 _lib = None
@@ -63,6 +64,7 @@ def _load():
         lib.skv_score.argtypes = [P, vp, i32, vp, i64, vp, i64, vp, sz, vp]
         lib.skv_select.argtypes = [P, vp, i64, i64, i32, i32, vp, i32, i32, vp, i64, vp, vp, sz, vp]
         lib.skv_attend_sparse.argtypes = [P, vp, vp, vp, i64, vp, i64, vp, i64, vp, vp, vp, sz, vp]
+        lib.skv_attend_sparse_noalloc.argtypes = [P, vp, vp, vp, i64, vp, i64, vp, i64, vp, vp, vp]
         lib.skv_attend_dense.argtypes = [P, vp, vp, vp, i64, vp, vp, vp, sz, vp]
         lib.skv_verify.argtypes = [P, vp, i32, vp, vp, i64, vp, vp, vp, sz, vp]
         dbl = ctypes.c_double
@@ -71,6 +73,7 @@ def _load():
         lib.skv_gather.argtypes = [P, vp, vp, i64, vp, i64, vp, i64, vp, vp, i64, i64, vp, vp]
         lib.skv_budgets.argtypes = [vp, i32, ctypes.c_double, i32, ctypes.c_double, i64, vp, vp]
         for f in ("skv_workspace_init", "skv_score", "skv_select", "skv_attend_sparse",
+                  "skv_attend_sparse_noalloc",
                   "skv_attend_dense", "skv_verify", "skv_gather", "skv_select_topp", "skv_budgets"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
@@ -238,6 +241,21 @@ def skv_attend_sparse(q, k, v, n: int, idx, count, tail_start: int, out, lse, ws
                                    ws.ptr, ws.nbytes, _stream(stream))
     if st != SKV_OK:
         raise SkvError(st, "skv_attend_sparse")
+    return out, lse
+
+
+def skv_attend_sparse_noalloc(q, k, v, n: int, idx, count, tail_start: int, out, lse,
+                              scale: float = 0.0, stream=None):
+    """skv_attend_sparse on the library's fixed per-GPU scratch (no workspace)."""
+    _check_dev(q, k, v, idx, count, out, lse)
+    if k.stride() != v.stride():
+        raise ValueError("K and V must share strides")
+    p = problem_for(q, k, scale)
+    st = _load().skv_attend_sparse_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), n,
+                                           _ptr(idx), _idx_stride(idx), _ptr(count), tail_start,
+                                           _ptr(out), _ptr(lse), _stream(stream))
+    if st != SKV_OK:
+        raise SkvError(st, "skv_attend_sparse_noalloc")
     return out, lse
 
 

@@ -4,6 +4,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/sparsekv.h"
 #include "skv_kernels.h"
 
@@ -274,6 +276,97 @@ size_t verify_scratch(const skv_problem* p, int64_t n, int32_t gamma) {
 // Pooled top-P selection: one fp32 pooled score per candidate.
 size_t topp_scratch(int64_t n) { return ((size_t)n * 4 + kAlign - 1) / kAlign * kAlign; }
 
+// Argument checks of a gathered-rows decode call (nothing is enqueued) and
+// its split-K plan.
+skv_status check_attend_sparse(const skv_problem* p, const void* q, const void* k, const void* v,
+                               int64_t n, const int32_t* idx, int64_t idx_stride,
+                               const int32_t* count, int64_t tail_start, const float* out,
+                               ChunkPlan* cp) {
+  skv_status st = check_problem(p);
+  if (st != SKV_OK) return st;
+  if (n < 1 || !q || !out || !aligned16(q) || !aligned16(out)) return SKV_ERR_INVALID_ARG;
+  if (!count || (!idx && idx_stride > 0) || idx_stride < 0) return SKV_ERR_INVALID_ARG;
+  if (tail_start < 0 || tail_start > n) return SKV_ERR_INVALID_ARG;
+  if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
+  if ((st = check_cache(p, k, n)) != SKV_OK || (st = check_cache(p, v, n)) != SKV_OK) return st;
+  const int64_t idx_rows = idx_stride < tail_start ? idx_stride : tail_start;
+  *cp = attend_plan(p, idx_rows + (n - tail_start), true);
+  return SKV_OK;
+}
+
+// The launches of a checked gathered-rows decode call; `base` is a workspace
+// of at least SKV_WS_HEADER_BYTES + attend_scratch(p, cp) bytes.
+skv_status run_attend_sparse(const skv_problem* p, const ChunkPlan& cp, const void* q,
+                             const void* k, const void* v, int64_t n, const int32_t* idx,
+                             int64_t idx_stride, const int32_t* count, int64_t tail_start,
+                             float* out, float* lse, char* base, hipStream_t stream) {
+  const int G = p->n_q_heads / p->n_kv_heads;
+  const int64_t idx_rows = idx_stride < tail_start ? idx_stride : tail_start;
+  const PartLayout L = part_layout(p, cp.cph, G);
+  AttendArgs a{};
+  a.q = q;
+  a.k = (const char*)k;
+  a.v = (const char*)v;
+  a.head_stride_b = p->kv_head_stride * elem_size(p);
+  a.pos_stride_b = p->kv_pos_stride * elem_size(p);
+  a.n = n;
+  a.idx = idx;
+  a.idx_stride = idx_stride;
+  a.count = count;
+  a.count_max = idx_rows;  // unique entries below tail_start: never more than this
+  a.tail_start = tail_start;
+  a.n_kv_heads = p->n_kv_heads;
+  a.chunk = cp.chunk;
+  a.chunks_per_head = cp.cph;
+  a.scale_log2 = scale_log2(p);
+  a.part_ml = (float*)(base + L.ml);
+  a.part_acc = (float*)(base + L.acc);
+  a.nch = (int32_t*)(base + L.nch);
+  a.group = G;
+  a.n_pos = 1;
+  a.narrow = cp.narrow;
+  if (cp.list) {
+    a.items = (int2*)(base + L.items);
+    a.n_items = (int32_t*)(base + L.n_items);
+    // four-wave workgroups, two per CU, walking the list
+    const int64_t pairs = (int64_t)p->n_kv_heads * cp.cph, cap = 4 * (int64_t)target_wgs();
+    a.list_grid = (int32_t)(pairs < cap ? pairs : cap);
+  }
+  skv_status st = hip_status(launch_attend_any(p, true, a, stream));
+  if (st != SKV_OK) return st;
+  return launch_partials_merge(p, base, L, cp.cph, G, true, out, lse, stream);
+}
+
+// ---- fixed scratch of skv_attend_sparse_noalloc -----------------------------
+// For callers that cannot allocate device memory: one array per GPU that the
+// library holds until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host it names a stand-in, not device memory):
+// its device address is looked up once per device with hipGetSymbolAddress
+// and kept in g_scratch_ptr.
+static __device__ __align__(256) char scratch[SKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch; the first call on a device
+// looks it up and clears its header (a fill kernel on `stream`: calls on one
+// GPU share the array, and the header must read zero on entry).
+skv_status noalloc_scratch(char** out, hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SKV_ERR_HIP;
+    if (skv::launch_zero_u32((uint32_t*)ptr, kCounterSlots, stream) != hipSuccess) return SKV_ERR_HIP;
+    g_scratch_ptr[dev] = (char*)ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -360,52 +453,28 @@ skv_status skv_attend_sparse(const skv_problem* p, const void* q, const void* k,
                              int64_t n, const int32_t* idx, int64_t idx_stride,
                              const int32_t* count, int64_t tail_start, float* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream) {
-  skv_status st = check_problem(p);
+  ChunkPlan cp;
+  skv_status st = check_attend_sparse(p, q, k, v, n, idx, idx_stride, count, tail_start, out, &cp);
   if (st != SKV_OK) return st;
-  if (n < 1 || !q || !out || !aligned16(q) || !aligned16(out)) return SKV_ERR_INVALID_ARG;
-  if (!count || (!idx && idx_stride > 0) || idx_stride < 0) return SKV_ERR_INVALID_ARG;
-  if (tail_start < 0 || tail_start > n) return SKV_ERR_INVALID_ARG;
-  if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
-  if ((st = check_cache(p, k, n)) != SKV_OK || (st = check_cache(p, v, n)) != SKV_OK) return st;
-  int64_t idx_rows = idx_stride < tail_start ? idx_stride : tail_start;
-  const ChunkPlan cp = attend_plan(p, idx_rows + (n - tail_start), true);
   if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + attend_scratch(p, cp))) != SKV_OK)
     return st;
-  const int G = p->n_q_heads / p->n_kv_heads;
-  char* base = (char*)ws;
-  const PartLayout L = part_layout(p, cp.cph, G);
-  AttendArgs a{};
-  a.q = q;
-  a.k = (const char*)k;
-  a.v = (const char*)v;
-  a.head_stride_b = p->kv_head_stride * elem_size(p);
-  a.pos_stride_b = p->kv_pos_stride * elem_size(p);
-  a.n = n;
-  a.idx = idx;
-  a.idx_stride = idx_stride;
-  a.count = count;
-  a.count_max = idx_rows;  // unique entries below tail_start: never more than this
-  a.tail_start = tail_start;
-  a.n_kv_heads = p->n_kv_heads;
-  a.chunk = cp.chunk;
-  a.chunks_per_head = cp.cph;
-  a.scale_log2 = scale_log2(p);
-  a.part_ml = (float*)(base + L.ml);
-  a.part_acc = (float*)(base + L.acc);
-  a.nch = (int32_t*)(base + L.nch);
-  a.group = G;
-  a.n_pos = 1;
-  a.narrow = cp.narrow;
-  if (cp.list) {
-    a.items = (int2*)(base + L.items);
-    a.n_items = (int32_t*)(base + L.n_items);
-    // four-wave workgroups, two per CU, walking the list
-    const int64_t pairs = (int64_t)p->n_kv_heads * cp.cph, cap = 4 * (int64_t)target_wgs();
-    a.list_grid = (int32_t)(pairs < cap ? pairs : cap);
-  }
-  if ((st = hip_status(launch_attend_any(p, true, a, (hipStream_t)stream))) != SKV_OK)
-    return st;
-  return launch_partials_merge(p, base, L, cp.cph, G, true, out, lse, (hipStream_t)stream);
+  return run_attend_sparse(p, cp, q, k, v, n, idx, idx_stride, count, tail_start, out, lse,
+                           (char*)ws, (hipStream_t)stream);
+}
+
+skv_status skv_attend_sparse_noalloc(const skv_problem* p, const void* q, const void* k,
+                                     const void* v, int64_t n, const int32_t* idx,
+                                     int64_t idx_stride, const int32_t* count, int64_t tail_start,
+                                     float* out, float* lse, void* stream) {
+  ChunkPlan cp;
+  skv_status st = check_attend_sparse(p, q, k, v, n, idx, idx_stride, count, tail_start, out, &cp);
+  if (st != SKV_OK) return st;
+  if (SKV_WS_HEADER_BYTES + attend_scratch(p, cp) > (size_t)SKV_NOALLOC_SCRATCH_BYTES)
+    return SKV_ERR_WORKSPACE;
+  char* base = nullptr;
+  if ((st = noalloc_scratch(&base, (hipStream_t)stream)) != SKV_OK) return st;
+  return run_attend_sparse(p, cp, q, k, v, n, idx, idx_stride, count, tail_start, out, lse, base,
+                           (hipStream_t)stream);
 }
 
 skv_status skv_score(const skv_problem* p, const void* q, int32_t n_obs, const void* k, int64_t n,

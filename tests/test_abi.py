@@ -147,3 +147,22 @@ def test_binding_constants_match_the_header():
     for name in ("SKV_OK", "SKV_F32", "SKV_BF16"):
         mm = re.search(rf"\b{name}\s*=\s*(\d+)", txt)
         assert mm and int(mm.group(1)) == getattr(skv, name), name
+
+
+def _noalloc(p, n=1000, q=FAKE, idx_stride=64, tail=900):
+    lib = skv._load()
+    return lib.skv_attend_sparse_noalloc(ctypes.byref(p), _vp(q), _vp(FAKE), _vp(FAKE), n, _vp(FAKE),
+                                         idx_stride, _vp(FAKE), tail, _vp(FAKE), _vp(0), _vp(0))
+
+
+def test_noalloc_entry_point_validates_and_bounds_its_scratch():
+    """skv_attend_sparse_noalloc checks its arguments like skv_attend_sparse
+    and refuses, before touching any device, a call whose split-K partials do
+    not fit its fixed scratch (4096 kv heads x 10,000 rows: about 40 MB)."""
+    assert _noalloc(_p(), q=0) == skv.SKV_ERR_INVALID_ARG
+    assert _noalloc(_p(), tail=1001) == skv.SKV_ERR_INVALID_ARG
+    assert _noalloc(_p(hq=24, hkv=8)) == skv.SKV_ERR_UNSUPPORTED
+    big = skv.problem(4096, 4096, 128, skv.SKV_BF16, 10000 * 128, 128)
+    assert _noalloc(big, n=10000, idx_stride=9968, tail=9968) == skv.SKV_ERR_WORKSPACE
+    # the same call with a caller workspace would need more than the fixed size
+    assert skv.skv_workspace_size(big, 10000) > skv.SKV_NOALLOC_SCRATCH_BYTES
