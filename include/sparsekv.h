@@ -34,9 +34,12 @@
  *     g / G with G = Hq / Hkv.
  *   - Scratch: a caller-provided device workspace of at least
  *     skv_workspace_size() bytes, 256-byte aligned, holding split-K partials
- *     and other per-call intermediates (its first SKV_WS_HEADER_BYTES are
- *     reserved; skv_workspace_init zero-fills them, and every call leaves
- *     them zero).  Two calls that share one workspace must not overlap in
+ *     and other per-call intermediates.  Its first SKV_WS_HEADER_BYTES are
+ *     reserved counters (the long-row selection's per-head histogram
+ *     totals): skv_workspace_init zero-fills them and every call leaves them
+ *     zero.  A call that returns SKV_ERR_HIP may have stopped between its
+ *     kernels and left them non-zero: call skv_workspace_init before reusing
+ *     the workspace.  Two calls that share one workspace must not overlap in
  *     time (same stream, or ordered by events); apart from the zero header,
  *     nothing in it needs to survive between calls.
  *   - Streams: every call only enqueues work on `stream` (a hipStream_t; NULL
