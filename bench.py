@@ -7,12 +7,16 @@ head dim 128, bf16), 30 % of the cache kept (4 sinks + 64 recent + 9762
 entries per kv head chosen once by the 32-query observation-window score).
 The same step over the whole cache (dense split-K) runs beside it.
 
-Timing: W untimed warm-up steps, then K steps captured once into a HIP graph
-and replayed between two HIP events on the launch stream, with a device
-synchronise on both sides (median of several blocks); each step reads a
-different one of L "layers" (distinct caches, about 1 GB at 32K) so the 256 MB
-Infinity Cache cannot serve the working set.  Inputs are resident in HBM
-before the timed region.  A decode-attention step is two kernels: the split-K
+Timing ("Locating the Crossing" protocol of the ByteCross page: five blocks,
+each in a fresh process, averaged, with a 95 % interval): the headline sparse
+and dense steps are timed in `--blocks` child processes that the parent starts
+one after another before it makes any GPU call.  In each child, W untimed
+warm-up steps run, then K steps are captured once into a HIP graph and replayed
+between two HIP events on the launch stream, with a device synchronise on both
+sides; each step reads a different one of L "layers" (distinct caches, about
+1 GB at 32K) so the 256 MB Infinity Cache cannot serve the working set.
+`value` is the mean over the blocks (median and the t-interval beside it).
+Inputs are resident in HBM before the timed region.  A decode-attention step is two kernels: the split-K
 partial kernel (the dominant one) and the small log-sum-exp merge; the
 roofline figure divides the algorithmic bytes by the whole step time, so the
 merge counts against it.  Eager (one host launch per call) times are reported
@@ -29,7 +33,8 @@ Sparse-to-Dense round of the Qwen2-7B video workload (5 sparse drafts + one
 gamma=5 verify), the SpecVLM selection on it (top-P 0.5 + uniform fill to
 10 % of the video tokens) and the round over that set, sweeps of the round
 over gamma = 1..13 and over K (measured vs I/O-model break-even acceptance), one-time selection costs, and the byte-count speedup bounds.
-`--sections all` adds the 1024-head SparseMM batched step (17 GB of cache).
+The 1024-head SparseMM batched step (17 GB of cache) is part of the default
+sections.
 `--sections mfma` and `--sections hbm` are profiling modes (no bench line): the
 Qwen2-7B matrix-core calls, and three eager calls of each streaming kernel at
 32K and 128K, for runs under rocprofv3 counters.
@@ -104,7 +109,36 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 512 MiB device copy (counter calibration under a profiler)")
+    ap.add_argument("--child-block", action="store_true",
+                    help="internal: time one block of the headline steps and print it as JSON")
     return ap.parse_args()
+
+
+def run_blocks(args):
+    """Time the headline steps in args.blocks fresh child processes, one after
+    another (this process has made no GPU call yet).  Returns the children's
+    JSON results."""
+    import subprocess
+    res = []
+    for b in range(args.blocks):
+        log(f"fresh-process block {b + 1}/{args.blocks}")
+        cmd = [sys.executable, os.path.abspath(__file__), "--child-block", "--steps", str(args.steps),
+               "--warmup", str(args.warmup), "--layers", str(args.layers)]
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        if r.returncode != 0:
+            sys.stderr.write(r.stderr[-4000:])
+            raise SystemExit(f"block {b + 1} failed with status {r.returncode}")
+        res.append(json.loads(r.stdout.strip().splitlines()[-1]))
+    return res
+
+
+def interval95(xs):
+    """(mean, half-width of the two-sided 95 % Student-t interval of the mean)."""
+    from scipy import stats
+    x = np.asarray(xs, np.float64)
+    if len(x) < 2:
+        return float(x.mean()), None
+    return float(x.mean()), float(stats.t.ppf(0.975, len(x) - 1) * x.std(ddof=1) / math.sqrt(len(x)))
 
 
 def main():
@@ -114,6 +148,9 @@ def main():
               "step shards by kv head with no exchange, so one GPU's throughput is the "
               "per-GPU figure", file=sys.stderr)
         sys.exit(2)
+    blocks = None
+    if not args.child_block and args.sections in ("headline", "default", "all"):
+        blocks = run_blocks(args)  # before this process touches the GPU
     import torch
 
     import sparse_top_kv_amd as skv
@@ -336,9 +373,15 @@ def main():
         lay = layers[i % L]
         skv.skv_attend_dense(lay["q"], lay["k"], lay["v"], n, lay["out"], lay["lse"], ws)
 
-    log("timing the 32K sparse and dense steps")
-    sp_us, sp_blocks = time_steps(sparse_step, args.steps, args.warmup, args.blocks)
-    de_us, de_blocks = time_steps(dense_step, args.steps, args.warmup, args.blocks)
+    if args.child_block:
+        sp1, _ = time_steps(sparse_step, args.steps, args.warmup, 1)
+        de1, _ = time_steps(dense_step, args.steps, args.warmup, 1)
+        print(json.dumps({"sparse_us": sp1, "dense_us": de1}), flush=True)
+        return
+    sp_blocks = sorted(b["sparse_us"] for b in blocks)
+    de_blocks = sorted(b["dense_us"] for b in blocks)
+    sp_us, sp_ci = interval95(sp_blocks)
+    de_us, de_ci = interval95(de_blocks)
     sp_eager, _ = time_steps(sparse_step, args.steps, 2, 1, graph=False)
     de_eager, _ = time_steps(dense_step, args.steps, 2, 1, graph=False)
     # the same steps on one layer only: its cache stays in the 256 MB Infinity
@@ -353,9 +396,12 @@ def main():
     sp_bytes = rf.sparse_step_bytes(hq, hkv, d, rows, S + K, "bf16")
     de_bytes = rf.dense_step_bytes(hq, hkv, d, n, "bf16")
     details["llama32k_sparse_us"] = round(sp_us, 3)
+    details["llama32k_sparse_ci95_us"] = None if sp_ci is None else [round(sp_us - sp_ci, 3), round(sp_us + sp_ci, 3)]
+    details["llama32k_sparse_median_us"] = round(float(np.median(sp_blocks)), 3)
     details["llama32k_sparse_blocks_us"] = [round(x, 3) for x in sp_blocks]
-    details["llama32k_sparse_block_range_us"] = [round(sp_blocks[0], 3), round(sp_blocks[-1], 3)]
     details["llama32k_dense_us"] = round(de_us, 3)
+    details["llama32k_dense_ci95_us"] = None if de_ci is None else [round(de_us - de_ci, 3), round(de_us + de_ci, 3)]
+    details["llama32k_dense_median_us"] = round(float(np.median(de_blocks)), 3)
     details["llama32k_dense_blocks_us"] = [round(x, 3) for x in de_blocks]
     details["llama32k_dense_hbm_frac"] = round(rf.roofline_fraction(de_bytes, de_us * 1e-6), 4)
     details["llama32k_sparse_hbm_frac"] = round(rf.roofline_fraction(sp_bytes, sp_us * 1e-6), 4)
@@ -653,7 +699,7 @@ def main():
         del kv4
         torch.cuda.empty_cache()
 
-    if args.sections == "all":
+    if args.sections in ("default", "all"):
         log("generating the 1024-head SparseMM workload (17 GB)")
         w5 = synth.sparsemm_heads()
         n5, H5, R5 = w5.n, w5.n_q_heads, w5.n_recent
@@ -752,7 +798,9 @@ def main():
             "workload": "Llama-3.1-8B-shape single-sequence decode attention, 32K context, top-K sparse "
                         "step over 30% of the cache (4 sinks + 64 recent + 9762 by 32-query window score)",
             "q_heads": hq, "kv_heads": hkv, "head_dim": d, "context": n, "kept_rows_per_kv_head": rows,
-            "layers_rotated": L, "timing": f"median of {args.blocks} blocks x {args.steps} steps",
+            "layers_rotated": L,
+            "timing": f"mean of {args.blocks} blocks x {args.steps} graph-replayed steps, each block in a "
+                      "fresh process; 95 % t-interval in details",
         },
         "roofline": {
             "bound": "hbm",
