@@ -15,7 +15,7 @@
 // significand, i.e. an integer multiple M 2^(e' - 1) of the unit 2^-149:
 //   1. histogram over the exponent e (bits 30..23 of a): count and sum of M per
 //      bin, exact in 64 bits (M < 2^24, at most 2^31 candidates);
-//   2. one thread walks the bins from the top in 384-bit integer arithmetic:
+//   2. one wave scans the bins from the top in 384-bit integer arithmetic:
 //      total U, theta = ceil(lambda U) (lambda = lam_m / 2^lam_sh exactly), the
 //      bin e1 where the running mass reaches theta, and what that bin still
 //      has to supply, ceil((theta - P) / 2^(e1' - 1)) in units of M;
@@ -139,9 +139,13 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u62(uint64_t x) {
   return (uint64_t)s0 + ((uint64_t)s1 << 25) + ((uint64_t)s2 << 50);
 }
 
+constexpr int kSub = 16;  // private copies of every histogram bin
+
 // Shared state of the Stage I passes.
 struct ToppShared {
-  uint32_t h_cnt[kToppBins];
+  uint32_t s_cnt[kToppBins * kSub];   // pass histograms, kSub copies per bin
+  uint64_t s_mass[kToppBins * kSub];
+  uint32_t h_cnt[kToppBins];          // their sums per bin
   uint64_t h_mass[kToppBins];
   uint64_t sq[kSelWaves];
   uint32_t sc[kSelWaves];
@@ -152,20 +156,41 @@ struct ToppShared {
 };
 
 __device__ __forceinline__ void topp_clear_hist(ToppShared& sh) {
+  for (int i = threadIdx.x; i < kToppBins * kSub; i += blockDim.x) {
+    sh.s_cnt[i] = 0u;
+    sh.s_mass[i] = 0u;
+  }
+}
+// After a histogram pass (and a barrier): the per-bin sums of the copies.
+__device__ __forceinline__ void topp_sum_sub(ToppShared& sh) {
   for (int b = threadIdx.x; b < kToppBins; b += blockDim.x) {
-    sh.h_cnt[b] = 0u;
-    sh.h_mass[b] = 0u;
+    uint32_t c = 0;
+    uint64_t m = 0;
+#pragma unroll
+    for (int k = 0; k < kSub; ++k) {
+      c += sh.s_cnt[b * kSub + k];
+      m += sh.s_mass[b * kSub + k];
+    }
+    sh.h_cnt[b] = c;
+    sh.h_mass[b] = m;
   }
 }
 
-// Step 2 (after the exponent histogram): one thread, 384-bit arithmetic.
-__device__ __forceinline__ void topp_walk_exponents(ToppShared& sh, uint64_t lam_m, int lam_sh) {
-  if (threadIdx.x != 0) return;
-  Wide U;
-  wide_zero(U);
-  for (int e = 0; e < kToppBins; ++e)
-    if (sh.h_mass[e]) wide_add_shl(U, sh.h_mass[e], unit_shift(e));
-  // theta = ceil(lam_m U / 2^lam_sh); lam_m < 2^54 keeps the product in 384 bits
+__device__ __forceinline__ Wide wide_add(const Wide& a, const Wide& b) {
+  Wide r;
+  uint64_t carry = 0;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const uint64_t t = a.w[i] + b.w[i];
+    const uint64_t c1 = t < a.w[i];
+    r.w[i] = t + carry;
+    carry = c1 | (r.w[i] < carry);
+  }
+  return r;
+}
+
+// ceil(lam_m U / 2^lam_sh); lam_m < 2^54 keeps the product in 384 bits.
+__device__ __forceinline__ Wide topp_theta(const Wide& U, uint64_t lam_m, int lam_sh) {
   Wide prod;
   uint64_t carry = 0;
 #pragma unroll
@@ -174,28 +199,68 @@ __device__ __forceinline__ void topp_walk_exponents(ToppShared& sh, uint64_t lam
     prod.w[i] = (uint64_t)t;
     carry = (uint64_t)(t >> 64);
   }
+  if (lam_sh < 384) return wide_shr_ceil(prod, lam_sh);
   Wide theta;
-  if (lam_sh >= 384) {
-    wide_zero(theta);
-    bool nz = false;
-    for (int i = 0; i < 6; ++i) nz = nz || prod.w[i] != 0u;
-    theta.w[0] = nz ? 1u : 0u;
-  } else {
-    theta = wide_shr_ceil(prod, lam_sh);
+  wide_zero(theta);
+  bool nz = false;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) nz = nz || prod.w[i] != 0u;
+  theta.w[0] = nz ? 1u : 0u;
+  return theta;
+}
+
+// Step 2 (after the exponent histogram), on wave 0: lane i owns exponent
+// bins 255 - 4 i - k, k = 0..3, so lane order is descending exponent.  Each
+// lane adds its bins' masses exactly (384 bits), a six-step shuffle scan
+// gives every lane the mass of all bins above and including its own, every
+// lane forms theta from the total, and the one lane whose range crosses
+// theta walks its four bins.
+__device__ __forceinline__ void topp_walk_exponents(ToppShared& sh, uint64_t lam_m, int lam_sh) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  Wide mine;
+  wide_zero(mine);
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = 255 - 4 * lane - k;
+    const uint64_t m = sh.h_mass[e];
+    if (m) wide_add_shl(mine, m, unit_shift(e));
+    cnt += sh.h_cnt[e];
   }
+  Wide incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    Wide o;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) o.w[i] = __shfl_up(incl.w[i], off, 64);
+    if (lane >= off) incl = wide_add(incl, o);
+  }
+  const uint32_t cincl = wave_incl_scan(cnt);
+  Wide U;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) U.w[i] = __shfl(incl.w[i], 63, 64);
+  const Wide theta = topp_theta(U, lam_m, lam_sh);
   bool tz = true;
+#pragma unroll
   for (int i = 0; i < 6; ++i) tz = tz && theta.w[i] == 0u;
-  sh.e1 = -1;
-  sh.need = 0;
-  sh.above = 0;
-  if (tz) return;  // the empty prefix already reaches lambda U
-  Wide P;
-  wide_zero(P);
-  uint32_t above = 0;
-  for (int e = kToppBins - 1; e >= 0; --e) {
-    if (!sh.h_mass[e]) continue;
+  if (tz) {  // the empty prefix already reaches lambda U: nothing is retained
+    if (lane == 0) {
+      sh.e1 = -1;
+      sh.need = 0;
+      sh.above = 0;
+    }
+    return;
+  }
+  Wide P = wide_sub(incl, mine);  // mass of every bin above this lane's
+  if (!(wide_cmp(P, theta) < 0 && wide_cmp(theta, incl) <= 0)) return;
+  uint32_t above = cincl - cnt;
+  for (int k = 0; k < 4; ++k) {
+    const int e = 255 - 4 * lane - k;
+    const uint64_t m = sh.h_mass[e];
+    if (!m) continue;
     Wide Pn = P;
-    wide_add_shl(Pn, sh.h_mass[e], unit_shift(e));
+    wide_add_shl(Pn, m, unit_shift(e));
     if (wide_cmp(Pn, theta) >= 0) {
       sh.e1 = e;
       sh.need = wide_shr_ceil(wide_sub(theta, P), unit_shift(e)).w[0];
@@ -243,24 +308,27 @@ __device__ __forceinline__ void topp_pick_digit(ToppShared& sh) {
   __syncthreads();
 }
 
-// Candidate score bits held or re-read by a kernel: ExpHist counts every
-// positive value into its exponent bin; SigHist counts the values of exponent
-// bin e1 whose significand matches `prefix` above bit shift + 8, by the
-// significand digit at `shift`.
-__device__ __forceinline__ void topp_add_exp(ToppShared& sh, uint32_t b) {
-  if (b) {
-    const uint32_t e = b >> 23;
-    atomicAdd(&sh.h_cnt[e], 1u);
-    atomicAdd((unsigned long long*)&sh.h_mass[e], (unsigned long long)sig_of(b));
-  }
+// Histogram updates.  Scores cluster in a few exponent (and leading-
+// significand) bins, and LDS atomics on one address serialise, so every bin
+// has kSub private copies (lane bits 0-1 and wave bits 0-1 pick one), stored
+// side by side so a bin's copies sit in distinct banks; topp_sum_sub adds
+// them up after the pass (integer sums: the result is exact and ordered).
+__device__ __forceinline__ int topp_sub() { return (threadIdx.x & 3) | (((threadIdx.x >> 6) & 3) << 2); }
+__device__ __forceinline__ void topp_add(ToppShared& sh, uint32_t bin, uint32_t sig) {
+  const int i = (int)bin * kSub + topp_sub();
+  atomicAdd(&sh.s_cnt[i], 1u);
+  atomicAdd((unsigned long long*)&sh.s_mass[i], (unsigned long long)sig);
 }
+// Exponent histogram: every positive value into its exponent bin.
+__device__ __forceinline__ void topp_add_exp(ToppShared& sh, uint32_t b) {
+  if (b) topp_add(sh, b >> 23, sig_of(b));
+}
+// Significand histogram of exponent bin e1: the values whose significand
+// matches `prefix` above bit shift + 8, by the significand digit at `shift`.
 __device__ __forceinline__ void topp_add_sig(ToppShared& sh, uint32_t b, int e1, int shift, uint32_t prefix) {
   const uint32_t m = sig_of(b);
-  if (b && (int)(b >> 23) == e1 && (m >> (shift + 8)) == (prefix >> (shift + 8))) {
-    const uint32_t dg = (m >> shift) & 255u;
-    atomicAdd(&sh.h_cnt[dg], 1u);
-    atomicAdd((unsigned long long*)&sh.h_mass[dg], (unsigned long long)m);
-  }
+  if (b && (int)(b >> 23) == e1 && (m >> (shift + 8)) == (prefix >> (shift + 8)))
+    topp_add(sh, (m >> shift) & 255u, m);
 }
 
 // Rows of any length: the scores are re-read from memory in every pass (the
@@ -294,6 +362,8 @@ __global__ __launch_bounds__(kSelThreads) void topp_kernel(const ToppArgs a) {
   // ---- 1-2. exponent histogram, then the walk over the exponent bins -------
   for (int64_t j = c_lo + tid; j < c_hi; j += kSelThreads) topp_add_exp(sh, bits_of(j));
   __syncthreads();
+  topp_sum_sub(sh);
+  __syncthreads();
   topp_walk_exponents(sh, a.lam_m, a.lam_sh);
   __syncthreads();
 
@@ -308,6 +378,8 @@ __global__ __launch_bounds__(kSelThreads) void topp_kernel(const ToppArgs a) {
       topp_clear_hist(sh);
       __syncthreads();
       for (int64_t j = c_lo + tid; j < c_hi; j += kSelThreads) topp_add_sig(sh, bits_of(j), e1, shift, prefix);
+      __syncthreads();
+      topp_sum_sub(sh);
       __syncthreads();
       topp_pick_digit(sh);
       prefix |= sh.digit << shift;
@@ -397,6 +469,8 @@ __global__ __launch_bounds__(kSelThreads) void topp_run_kernel(const ToppArgs a)
 #pragma unroll
   for (int u = 0; u < kRunPer; ++u) topp_add_exp(sh, bits[u]);  // invalid slots hold 0
   __syncthreads();
+  topp_sum_sub(sh);
+  __syncthreads();
   topp_walk_exponents(sh, a.lam_m, a.lam_sh);
   __syncthreads();
 
@@ -412,6 +486,8 @@ __global__ __launch_bounds__(kSelThreads) void topp_run_kernel(const ToppArgs a)
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < kRunPer; ++u) topp_add_sig(sh, bits[u], e1, shift, prefix);
+      __syncthreads();
+      topp_sum_sub(sh);
       __syncthreads();
       topp_pick_digit(sh);
       prefix |= sh.digit << shift;
