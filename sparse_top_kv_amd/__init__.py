@@ -4,7 +4,7 @@ Argument marshalling only: every step runs in the HIP kernels of
 ``libsparsekv.so`` (built from ``csrc/`` by ``sparse_top_kv_amd.build``).  The
 functions carry the C names (``skv_score``, ``skv_select``,
 ``skv_attend_sparse``, ``skv_attend_sparse_noalloc``, ``skv_attend_dense``,
-``skv_verify``, ``skv_gather``, ``skv_select_topp``, ``skv_budgets``)
+``skv_verify``, ``skv_topk_step``, ``skv_gather``, ``skv_select_topp``, ``skv_budgets``)
 and take torch tensors on a ROCm device; torch provides device memory and the
 current stream, nothing else.  A missing library raises at the first call.
 
@@ -27,6 +27,7 @@ SKV_OK, SKV_ERR_INVALID_ARG, SKV_ERR_UNSUPPORTED, SKV_ERR_WORKSPACE, SKV_ERR_HIP
 SKV_F32, SKV_BF16 = 0, 1
 SKV_WS_HEADER_BYTES = 1048576
 SKV_NOALLOC_SCRATCH_BYTES = 16 * 1048576
+SKV_TOPK_ERROR_OFFSET = SKV_WS_HEADER_BYTES - 64 * 128 - 128
 _ALIGN = 256
 
 _lib = None
@@ -66,6 +67,8 @@ def _load():
         lib.skv_attend_sparse.argtypes = [P, vp, vp, vp, i64, vp, i64, vp, i64, vp, vp, vp, sz, vp]
         lib.skv_attend_sparse_noalloc.argtypes = [P, vp, vp, vp, i64, vp, i64, vp, i64, vp, vp, vp]
         lib.skv_attend_dense.argtypes = [P, vp, vp, vp, i64, vp, vp, vp, sz, vp]
+        lib.skv_topk_step.argtypes = [P, vp, vp, vp, i64, i32, i32, i32, vp, i64, vp, i64, vp, vp, vp,
+                                      vp, sz, vp]
         lib.skv_verify.argtypes = [P, vp, i32, vp, vp, i64, vp, vp, vp, sz, vp]
         dbl = ctypes.c_double
         lib.skv_select_topp.argtypes = [P, vp, i64, i64, i32, i32, dbl, dbl, i32, i32, vp, i64, vp,
@@ -73,7 +76,7 @@ def _load():
         lib.skv_gather.argtypes = [P, vp, vp, i64, vp, i64, vp, i64, vp, vp, i64, i64, vp, vp]
         lib.skv_budgets.argtypes = [vp, i32, ctypes.c_double, i32, ctypes.c_double, i64, vp, vp]
         for f in ("skv_workspace_init", "skv_score", "skv_select", "skv_attend_sparse",
-                  "skv_attend_sparse_noalloc",
+                  "skv_attend_sparse_noalloc", "skv_topk_step",
                   "skv_attend_dense", "skv_verify", "skv_gather", "skv_select_topp", "skv_budgets"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
@@ -256,6 +259,28 @@ def skv_attend_sparse_noalloc(q, k, v, n: int, idx, count, tail_start: int, out,
                                            _ptr(out), _ptr(lse), _stream(stream))
     if st != SKV_OK:
         raise SkvError(st, "skv_attend_sparse_noalloc")
+    return out, lse
+
+
+def skv_topk_step(q, k, v, n: int, n_sink: int, n_recent: int, k_top: int, score, idx, count, out,
+                  lse, ws: Workspace, scale: float = 0.0, stream=None):
+    """Per-step top-K decode step: score of the decode query q [Hq][d], sinks + top-K +
+    recent run, attention over that set (score, idx, count, out, lse written)."""
+    torch = _torch()
+    _check_dev(q, k, v, score, idx, count, out, lse)
+    if k.stride() != v.stride():
+        raise ValueError("K and V must share strides")
+    if score.dtype != torch.float32 or score.stride(1) != 1:
+        raise ValueError("score must be fp32 [Hkv][>=n]")
+    for t in (idx, count):
+        if t.dtype != torch.int32:
+            raise TypeError("idx and count are int32")
+    p = problem_for(q, k, scale)
+    st = _load().skv_topk_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), n, n_sink, n_recent, k_top,
+                               _ptr(score), score.stride(0), _ptr(idx), _idx_stride(idx), _ptr(count),
+                               _ptr(out), _ptr(lse), ws.ptr, ws.nbytes, _stream(stream))
+    if st != SKV_OK:
+        raise SkvError(st, "skv_topk_step")
     return out, lse
 
 

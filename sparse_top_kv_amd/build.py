@@ -12,7 +12,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparsekv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.hip", "attend.hip", "attend_mfma.hip", "score_step.hip", "score_obs.hip", "select.hip",
-           "merge.hip", "util.hip", "gather.hip", "select_topp.hip"]
+           "merge.hip", "util.hip", "gather.hip", "select_topp.hip", "topk_step.hip"]
 # -amdgpu-mfma-vgpr-form: MFMA accumulators stay in VGPRs (no AGPR copies
 # around the vector work on them).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -39,7 +39,7 @@ def build(sources=None, jobs: int | None = None) -> str:
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB

@@ -21,6 +21,17 @@ using skv::AttendArgs;
 
 constexpr size_t kAlign = 256;
 constexpr int64_t kCounterSlots = SKV_WS_HEADER_BYTES / 4;
+// The header's last 8 KB: per-kv-head counters of skv_topk_step (one 128-byte
+// line each, up to 64 kv heads: arrivals and the chunk ticket), and just below
+// them its error word.  The long-row select uses at most 63 x 16 KB from the
+// start of the header.
+constexpr size_t kTopkCtrOffset = SKV_WS_HEADER_BYTES - 64 * 128;
+constexpr size_t kTopkErrOffset = kTopkCtrOffset - 128;
+constexpr int kTopkMaxKvHeads = 64;
+static_assert(kTopkErrOffset == SKV_TOPK_ERROR_OFFSET, "documented error word");
+static_assert((size_t)63 * 4096 * 4 <= kTopkErrOffset, "select totals and step counters are disjoint");
+// Generous bound on the CUs of one device (sizes the step's scratch).
+constexpr int kMaxCUs = 1024;
 constexpr int kVerifyMaxGamma = 16;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -367,6 +378,54 @@ skv_status noalloc_scratch(char** out, hipStream_t stream) {
   return SKV_OK;
 }
 
+// ---- skv_topk_step planning -------------------------------------------------
+std::mutex g_cu_mu;
+int g_cus[kMaxDevices];
+
+int device_cus() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  std::lock_guard<std::mutex> lock(g_cu_mu);
+  if (!g_cus[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    g_cus[dev] = v;
+  }
+  return g_cus[dev];
+}
+
+struct TopkPlan {
+  bool fused = false;
+  int chunk = 0, P = 0;
+};
+
+// One workgroup per CU: P = CUs / Hkv chunks per kv head, chunks a multiple of
+// the granule and small enough for the group's logits to stay in LDS.
+TopkPlan topk_plan(const skv_problem* p, int64_t n, int cus) {
+  TopkPlan t;
+  const int G = p->n_q_heads / p->n_kv_heads;
+  if (p->dtype != SKV_BF16 || p->n_kv_heads > kTopkMaxKvHeads || cus < p->n_kv_heads) return t;
+  const int pmax = cus / p->n_kv_heads, gr = skv::topk_step_granule();
+  int64_t chunk = (n + pmax - 1) / pmax;
+  chunk = (chunk + gr - 1) / gr * gr;
+  if (chunk > skv::topk_step_max_chunk(G, p->head_dim)) return t;
+  t.fused = true;
+  t.chunk = (int)chunk;
+  t.P = (int)((n + chunk - 1) / chunk);
+  return t;
+}
+
+// Scratch of the fused step for any device: P <= kMaxCUs / Hkv and P <= n / granule.
+size_t topk_scratch_bound(const skv_problem* p, int64_t n_max) {
+  if (p->dtype != SKV_BF16 || p->n_kv_heads > kTopkMaxKvHeads) return 0;
+  const int G = p->n_q_heads / p->n_kv_heads;
+  int64_t P = kMaxCUs / p->n_kv_heads;
+  const int64_t pn = (n_max + skv::topk_step_granule() - 1) / skv::topk_step_granule();
+  P = P < pn ? P : pn;
+  P = P < 1 ? 1 : P;
+  return skv::topk_step_scratch(p->n_kv_heads, (int)P, G, p->head_dim);
+}
+
 }  // namespace
 
 extern "C" {
@@ -394,6 +453,8 @@ size_t skv_workspace_size(const skv_problem* p, int64_t n_max, int32_t rows_max)
   t = skv::select_ws_bytes(p->n_kv_heads, n_max);
   s = s > t ? s : t;
   t = topp_scratch(n_max);
+  s = s > t ? s : t;
+  t = topk_scratch_bound(p, n_max);
   s = s > t ? s : t;
   if (p->dtype == SKV_BF16) {
     const int32_t w = rows_max < n_max ? rows_max : (int32_t)n_max;
@@ -657,6 +718,60 @@ skv_status skv_verify(const skv_problem* p, const void* q, int32_t gamma, const 
       return st;
   }
   return SKV_OK;
+}
+
+skv_status skv_topk_step(const skv_problem* p, const void* q, const void* k, const void* v,
+                         int64_t n, int32_t n_sink, int32_t n_recent, int32_t k_top, float* score,
+                         int64_t score_stride, int32_t* idx, int64_t idx_stride, int32_t* count,
+                         float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  skv_status st = check_problem(p);
+  if (st != SKV_OK) return st;
+  if (n < 1 || !q || !out || !aligned16(q) || !aligned16(out) || !score || score_stride < n || !count)
+    return SKV_ERR_INVALID_ARG;
+  if (n_sink < 0 || n_recent < 0 || k_top < 0) return SKV_ERR_INVALID_ARG;
+  if (idx_stride < (int64_t)n_sink + k_top || (idx_stride > 0 && !idx)) return SKV_ERR_INVALID_ARG;
+  if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
+  if ((st = check_cache(p, k, n)) != SKV_OK || (st = check_cache(p, v, n)) != SKV_OK) return st;
+  const int64_t tail = n - n_recent > 0 ? n - n_recent : 0;
+  const TopkPlan tp = topk_plan(p, n, device_cus());
+  if (tp.fused) {
+    const int G = p->n_q_heads / p->n_kv_heads;
+    const size_t need = SKV_WS_HEADER_BYTES + skv::topk_step_scratch(p->n_kv_heads, tp.P, G, p->head_dim);
+    if ((st = check_ws(ws, ws_bytes, need)) != SKV_OK) return st;
+    skv::TopkArgs a{};
+    a.q = q;
+    a.k = (const char*)k;
+    a.v = (const char*)v;
+    a.head_stride_b = p->kv_head_stride * 2;
+    a.pos_stride_b = p->kv_pos_stride * 2;
+    a.n = n;
+    a.n_sink = n_sink;
+    a.n_recent = n_recent;
+    a.k_top = k_top;
+    a.n_kv_heads = p->n_kv_heads;
+    a.chunk = tp.chunk;
+    a.chunks_per_head = tp.P;
+    a.scale_log2 = scale_log2(p);
+    a.score = score;
+    a.score_stride = score_stride;
+    a.idx = idx;
+    a.idx_stride = idx_stride;
+    a.count = count;
+    a.out = out;
+    a.lse = lse;
+    a.ctr = (uint32_t*)((char*)ws + kTopkCtrOffset);
+    a.err = (uint32_t*)((char*)ws + kTopkErrOffset);
+    const hipError_t e = skv::launch_topk_step(p->head_dim, G, a, (char*)ws + SKV_WS_HEADER_BYTES,
+                                               (hipStream_t)stream);
+    if (e == hipSuccess) return SKV_OK;
+    // not launched: clear the error and take the three-call path
+    (void)hipGetLastError();
+  }
+  if ((st = skv_score(p, q, 1, k, n, score, score_stride, ws, ws_bytes, stream)) != SKV_OK) return st;
+  if ((st = skv_select(p, score, score_stride, n, n_sink, n_recent, nullptr, k_top, k_top, idx,
+                       idx_stride, count, ws, ws_bytes, stream)) != SKV_OK)
+    return st;
+  return skv_attend_sparse(p, q, k, v, n, idx, idx_stride, count, tail, out, lse, ws, ws_bytes, stream);
 }
 
 skv_status skv_gather(const skv_problem* p, const void* k, const void* v, int64_t n,

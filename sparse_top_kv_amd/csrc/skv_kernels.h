@@ -162,6 +162,39 @@ struct ToppArgs {
 };
 hipError_t launch_select_topp(const ToppArgs& a, hipStream_t stream);
 
+// The per-step top-K decode step in one launch (skv_topk_step): score of one
+// decode query, sinks + top-K + recent run, attention over the kept set.
+// bf16 caches; one workgroup per (kv head, chunk); a kv head's workgroups
+// take their chunks in start order from the head's ticket and meet at bounded
+// spin barriers (progress needs (P - 1) Hkv + 1 workgroups resident at once).
+struct TopkArgs {
+  const void* q;            // [Hq][d]
+  const char* k;
+  const char* v;
+  int64_t head_stride_b, pos_stride_b;
+  int64_t n;
+  int32_t n_sink, n_recent;
+  int64_t k_top;            // candidates kept by score (clamped to the candidate count)
+  int32_t n_kv_heads;
+  int32_t chunk;            // keys per workgroup, a multiple of topk_step_granule()
+  int32_t chunks_per_head;  // P
+  float scale_log2;
+  float* score;             // [Hkv][score_stride], may be null
+  int64_t score_stride;
+  int32_t* idx;             // [Hkv][idx_stride]: sinks, then the top-K, ascending
+  int64_t idx_stride;
+  int32_t* count;           // [Hkv]
+  float* out;               // [Hq][d]
+  float* lse;               // [Hq], may be null
+  uint32_t* ctr;            // per kv head 32 words: arrivals (word 0), ticket (word 16); zero on entry, left zero
+  uint32_t* err;            // set to 1 if a barrier spin ran out
+  int32_t pub_cap, pub_rank;  // set by launch_topk_step
+};
+hipError_t launch_topk_step(int d, int g, const TopkArgs& a, void* scratch, hipStream_t stream);
+int topk_step_max_chunk(int g, int d);
+int topk_step_granule();
+size_t topk_step_scratch(int hkv, int p, int g, int d);
+
 // Compaction of a kept set (skv_gather).
 struct GatherArgs {
   const char* k;

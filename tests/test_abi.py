@@ -166,3 +166,33 @@ def test_noalloc_entry_point_validates_and_bounds_its_scratch():
     assert _noalloc(big, n=10000, idx_stride=9968, tail=9968) == skv.SKV_ERR_WORKSPACE
     # the same call with a caller workspace would need more than the fixed size
     assert skv.skv_workspace_size(big, 10000) > skv.SKV_NOALLOC_SCRATCH_BYTES
+
+
+def _topk(p, n=1000, q=FAKE, score=FAKE, score_stride=1000, S=4, R=64, K=256, idx_stride=260, count=FAKE):
+    lib = skv._load()
+    return lib.skv_topk_step(ctypes.byref(p), _vp(q), _vp(FAKE), _vp(FAKE), ctypes.c_int64(n), S, R, K,
+                             _vp(score), ctypes.c_int64(score_stride), _vp(FAKE), ctypes.c_int64(idx_stride),
+                             _vp(count), _vp(FAKE), _vp(0), _vp(FAKE), ctypes.c_size_t(1 << 30), _vp(0))
+
+
+def test_topk_step_validation():
+    """skv_topk_step rejects, before any device call, what the three calls it
+    stands for would reject: a missing score row (required), a score stride
+    below n, an index row too short for the sinks and K, negative counts."""
+    assert _topk(_p(), score=0) == skv.SKV_ERR_INVALID_ARG
+    assert _topk(_p(), score_stride=999) == skv.SKV_ERR_INVALID_ARG
+    assert _topk(_p(), idx_stride=259) == skv.SKV_ERR_INVALID_ARG
+    assert _topk(_p(), K=-1) == skv.SKV_ERR_INVALID_ARG
+    assert _topk(_p(), S=-1) == skv.SKV_ERR_INVALID_ARG
+    assert _topk(_p(), count=0) == skv.SKV_ERR_INVALID_ARG
+    assert _topk(_p(), n=0) == skv.SKV_ERR_INVALID_ARG
+    assert _topk(_p(), q=FAKE + 4) == skv.SKV_ERR_INVALID_ARG
+    assert _topk(_p(hq=24, hkv=8)) == skv.SKV_ERR_UNSUPPORTED
+
+
+def test_topk_error_word_offset_matches_the_header():
+    txt = open(HEADER).read()
+    m = re.search(r"#define\s+SKV_TOPK_ERROR_OFFSET\s+\(SKV_WS_HEADER_BYTES\s*-\s*(\d+)\s*\*\s*(\d+)\s*-\s*(\d+)\)", txt)
+    assert m, "SKV_TOPK_ERROR_OFFSET"
+    off = skv.SKV_WS_HEADER_BYTES - int(m.group(1)) * int(m.group(2)) - int(m.group(3))
+    assert off == skv.SKV_TOPK_ERROR_OFFSET
