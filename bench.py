@@ -35,9 +35,11 @@ gamma=5 verify), the SpecVLM selection on it (top-P 0.5 + uniform fill to
 over gamma = 1..13 and over K (measured vs I/O-model break-even acceptance), one-time selection costs, and the byte-count speedup bounds.
 The 1024-head SparseMM batched step (17 GB of cache) is part of the default
 sections.
-`--sections mfma` and `--sections hbm` are profiling modes (no bench line): the
-Qwen2-7B matrix-core calls, and three eager calls of each streaming kernel at
-32K and 128K, for runs under rocprofv3 counters.
+`--sections mfma`, `--sections hbm` and `--sections valu` are profiling modes
+(no bench line): the Qwen2-7B matrix-core calls; three eager calls of each
+streaming kernel at 32K and 128K; the 32K dense step through the matrix-core
+kernel (bf16) and the vector-ALU kernel (fp32 caches); for runs under
+rocprofv3 counters.
 
 cpu_baseline: the fp64 oracle (test infrastructure) timed on this host on a
 bounded sample of the headline step.
@@ -105,7 +107,8 @@ def parse():
     ap.add_argument("--sections", default="default",
                     help="headline | default | all | mfma (profiling: only the Qwen2-7B matrix-core "
                          "calls, no bench line) | hbm (profiling: three eager calls of each "
-                         "streaming kernel at 32K and 128K, no bench line)")
+                         "streaming kernel at 32K and 128K, no bench line) | valu (profiling: the 32K "
+                         "dense step through the matrix-core and the vector-ALU kernels, no bench line)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 512 MiB device copy (counter calibration under a profiler)")
@@ -283,6 +286,25 @@ def main():
                           "verify_us": round(v_us, 2)}), flush=True)
         return
 
+    if args.sections == "valu":
+        # profiling mode for the matrix-core choice: the 32K dense decode step of
+        # the Llama-3.1-8B shape through the matrix-core kernel (bf16 caches)
+        # and, on the same shape with fp32 caches, through the vector-ALU kernel
+        w = synth.llama_obs(layer=0)
+        n = w.n
+        q, k, v = dev(w.q), dev(w.k), dev(w.v)
+        res = {}
+        for name, (qq, kk, vv) in (("bf16_mfma", (q, k, v)),
+                                   ("fp32_valu", (q.float(), k.float(), v.float()))):
+            wsv = skv.Workspace.for_problem(skv.problem_for(qq, kk), n)
+            o = torch.empty((w.n_q_heads, w.head_dim), device="cuda")
+            ls = torch.empty(w.n_q_heads, device="cuda")
+            us, _ = time_steps(lambda i: skv.skv_attend_dense(qq, kk, vv, n, o, ls, wsv), 20, 2, 1, graph=False)
+            res[name] = {"eager_us": round(us, 2), "keys": w.n_kv_heads * n}
+            del wsv
+        print(json.dumps({"sections": "valu", **res}), flush=True)
+        return
+
     if args.sections == "hbm":
         # profiling mode for HBM counter runs: each call three times, eagerly, in
         # a fixed order (32K: window score, select, gather, sparse and dense
@@ -326,6 +348,7 @@ def main():
         timed("128k_select", lambda: skv.skv_select(sc3, n3, S, R, K3, idx3, cnt, ws))
         timed("128k_sparse_step", lambda: skv.skv_attend_sparse(q3, k3, v3, n3, idx3, cnt, n3 - R, out, lse, ws))
         timed("128k_dense_step", lambda: skv.skv_attend_dense(q3, k3, v3, n3, out, lse, ws))
+        timed("128k_topk_step", lambda: skv.skv_topk_step(q3, k3, v3, n3, S, R, K3, sc3, idx3, cnt, out, lse, ws))
         if args.calib_copy:  # known traffic for the counters' scale: 512 MiB read, 512 MiB written
             src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
             dst = torch.empty_like(src)
