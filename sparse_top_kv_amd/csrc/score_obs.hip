@@ -139,18 +139,28 @@ __device__ __forceinline__ void s_tiles(const bf16x8_t (&kf)[kKT][D / 32], const
 }
 
 // Workgroup -> (kv head h, key block kb, row group g) and the range of query
-// chunks [c0, c0 + nch) the group covers.
+// chunks [c0, c0 + nch) the group covers.  Workgroups are dealt to the eight
+// XCDs in turn (block b to XCD b mod 8), and each XCD has its own L2: the row
+// groups of one (kv head, key block) tile take blocks b, b + 8, b + 16, ...,
+// so they run on one XCD and the tile's keys come from HBM once and from that
+// L2 for the other groups.  The grid is padded to whole tiles per XCD; a
+// workgroup past the last tile is not live.
+constexpr int kXcds = 8;
 struct ObsTile {
   int h, kb, g, c0, nch;
+  bool live;
 };
 __device__ __forceinline__ ObsTile obs_tile(const ScoreObsArgs& a, int NCH) {
   ObsTile t;
   const int rg = a.row_groups;
-  const int g = blockIdx.x % rg;
+  const int xcd = (int)(blockIdx.x % kXcds), local = (int)(blockIdx.x / kXcds);
+  const int tl = local / rg;
+  const int g = local - tl * rg;
   t.g = g;
-  const int hk = blockIdx.x / rg;
-  t.h = hk / a.n_kblocks;
-  t.kb = hk - t.h * a.n_kblocks;
+  const int hk = tl * kXcds + xcd;
+  t.live = hk < a.n_kv_heads * a.n_kblocks;
+  t.h = t.live ? hk / a.n_kblocks : 0;
+  t.kb = t.live ? hk - t.h * a.n_kblocks : 0;
   const int per = (NCH + rg - 1) / rg;
   t.c0 = g * per;
   t.nch = NCH - t.c0 < per ? NCH - t.c0 : per;
@@ -174,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void obs_pass1_kernel(const ScoreObsArgs 
   const int NCH_ALL = (RT + kChunk - 1) / kChunk;
   const ObsTile tl = obs_tile(a, NCH_ALL);
   const int h = tl.h, kb = tl.kb, NCH = NBUF == 1 && tl.nch > 1 ? 1 : tl.nch;  // the host picks NBUF
-  if (NCH == 0) return;  // a row group past the last chunk: nothing to do
+  if (!tl.live || NCH == 0) return;  // padding, or a row group past the last chunk: nothing to do
   auto buf = [](int c) { return NBUF == 1 ? 0 : (c & 1); };
   const int kw0 = kb * kBlockKeys + wave * 16 * kKT;  // keys are below 2^31
   // every window row sees keys <= n - W: no masks for a wave below that
@@ -324,6 +334,7 @@ __global__ __launch_bounds__(kThreads) void obs_pass2_kernel(const ScoreObsArgs 
   const int RT = (R + 15) / 16;
   const int NCH_ALL = (RT + kChunk - 1) / kChunk;
   const ObsTile tl = obs_tile(a, NCH_ALL);
+  if (!tl.live) return;  // padding of the grid
   const int h = tl.h, kb = tl.kb, NCH = NBUF == 1 && tl.nch > 1 ? 1 : tl.nch;  // the host picks NBUF
   auto buf = [](int c) { return NBUF == 1 ? 0 : (c & 1); };
   const int kw0 = kb * kBlockKeys + wave * 16 * kKT;  // keys are below 2^31
@@ -440,7 +451,8 @@ __global__ __launch_bounds__(kThreads) void obs_reduce_kernel(const ScoreObsArgs
 
 template <int D>
 hipError_t launch_d(const ScoreObsArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)a.n_kv_heads * a.n_kblocks * a.row_groups));
+  const int64_t tiles = (int64_t)a.n_kv_heads * a.n_kblocks;
+  const dim3 grid((unsigned)((tiles + kXcds - 1) / kXcds * kXcds * a.row_groups));
   const int R = a.n_obs * a.group;
   const int nch_all = ((R + 15) / 16 + kChunk - 1) / kChunk;
   const bool one = (nch_all + a.row_groups - 1) / a.row_groups <= 1;  // chunks per row group
