@@ -116,3 +116,34 @@ def test_many_head_work_list_in_a_graph():
     out = torch.empty((hq, d), device="cuda")
     lse = torch.empty(hq, device="cuda")
     _replay_matches(lambda: skv.skv_attend_sparse(q, k, v, n, it, ct, tail, out, lse, ws), [out, lse])
+
+
+def test_one_call_topk_step_in_a_graph():
+    """skv_topk_step keeps its per-head arrival counters and chunk tickets in
+    the workspace header and resets them at each step's last arrival: two
+    steps per replay (one through the published-key exchange, one through the
+    global radix levels, which many tied keys force) replay bit for bit."""
+    banner("graph: two one-call top-K steps per replay")
+    hq, hkv, d, n, S, R, K = 32, 8, 128, 40000, 4, 64, 3000
+    q, k, v = _rand((hq, d), 4), _rand((hkv, n, d), 5), _rand((hkv, n, d), 6)
+    kt = _rand((hkv, 1, d), 7).repeat(1, n, 1).contiguous()  # every key equal: ties
+    ws = skv.Workspace.for_problem(skv.problem_for(q, k), n)
+    score = torch.empty((hkv, n), device="cuda")
+    idx = torch.empty((hkv, S + K), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(hkv, dtype=torch.int32, device="cuda")
+    out = torch.empty((hq, d), device="cuda")
+    lse = torch.empty(hq, device="cuda")
+    score2 = torch.empty_like(score)
+    idx2 = torch.empty_like(idx)
+    cnt2 = torch.empty_like(cnt)
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+
+    def run():
+        skv.skv_topk_step(q, k, v, n, S, R, K, score, idx, cnt, out, lse, ws)
+        skv.skv_topk_step(q, kt, v, n, S, R, K, score2, idx2, cnt2, out2, lse2, ws)
+
+    _replay_matches(run, [score, idx, cnt, out, lse, score2, idx2, cnt2, out2, lse2])
+    err = int(ws.tensor[skv.SKV_TOPK_ERROR_OFFSET:skv.SKV_TOPK_ERROR_OFFSET + 4].view(torch.int32).item())
+    assert err == 0
+    assert torch.equal(idx2[:, S:].cpu(), torch.arange(S, S + K, dtype=torch.int32).repeat(hkv, 1))
