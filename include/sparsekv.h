@@ -221,19 +221,19 @@ skv_status skv_verify(const skv_problem* p, const void* q, int32_t gamma, const 
  * idx / count, out [Hq][d] and lse [Hq] (may be NULL).  With bf16 caches, at
  * most 64 kv heads and a cache short enough that each kv head's keys split
  * over CUs / Hkv workgroups keep their logits in LDS (128K context at G = 4
- * on 256 CUs), it runs as one launch whose workgroups take their work in
+ * on 256 CUs), it runs as one kernel whose workgroups take their work in
  * start order and meet at per-kv-head barriers (see the kernel's
- * description); otherwise it runs the three calls.  Scores equal
+ * description), followed by the split-K merge kernel; otherwise it runs the
+ * three calls.  Scores equal
  * skv_score's bit for bit; the selection is skv_select's on those scores;
  * the attention is exact over the same set (its summation order differs
  * from skv_attend_sparse's).  The workspace (skv_workspace_size) also holds
  * the step's counters in the reserved header (zero after
- * skv_workspace_init, left zero by every step); a word at byte
- * SKV_TOPK_ERROR_OFFSET of the workspace is set non-zero if a workgroup of
- * the one-launch form ever waited too long for the others of its kv head
- * (only when other work holds the device's CUs); the step's results are
- * then unspecified and the workspace must be initialised again before the
- * next step.  Two steps on one workspace must not overlap in time. */
+ * skv_workspace_init, cleared again at the end of every step); a word at
+ * byte SKV_TOPK_ERROR_OFFSET of the workspace is set non-zero if a workgroup
+ * of the one-launch form ever waited too long for the others of its kv head
+ * (only when other work holds the device's CUs); that step's results are
+ * then unspecified.  Two steps on one workspace must not overlap in time. */
 #define SKV_TOPK_ERROR_OFFSET (SKV_WS_HEADER_BYTES - 64 * 128 - 128)
 skv_status skv_topk_step(const skv_problem* p, const void* q, const void* k, const void* v,
                          int64_t n, int32_t n_sink, int32_t n_recent, int32_t k_top,

@@ -31,6 +31,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a) {
   __shared__ float sm_red[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (a.clear_ctr && blockIdx.x == 0)  // the one-call step's counters, for its next call
+    for (int i = tid; i < a.clear_heads; i += kThreads) {
+      a.clear_ctr[32 * i] = 0u;
+      a.clear_ctr[32 * i + 16] = 0u;
+    }
   const int Rh = a.rows_per_head;
   const int h = blockIdx.x / Rh;
   const int r = blockIdx.x - h * Rh;

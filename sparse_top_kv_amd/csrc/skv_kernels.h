@@ -54,6 +54,8 @@ struct MergeArgs {
   int32_t n_kv_heads, cph, rows_per_head, group;
   float* out;
   float* lse;               // may be null
+  uint32_t* clear_ctr;      // may be null: words 32 h and 32 h + 16, h < clear_heads, set to zero
+  int32_t clear_heads;
 };
 hipError_t launch_merge(int d, const MergeArgs& a, hipStream_t stream);
 // Rows per wave iteration of the attend kernel (the chunk must be a multiple
@@ -186,7 +188,7 @@ struct TopkArgs {
   int32_t* count;           // [Hkv]
   float* out;               // [Hq][d]
   float* lse;               // [Hq], may be null
-  uint32_t* ctr;            // per kv head 32 words: arrivals (word 0), ticket (word 16); zero on entry, left zero
+  uint32_t* ctr;            // per kv head 32 words: arrivals (word 0), ticket (word 16); zero on entry, cleared by the merge
   uint32_t* err;            // set to 1 if a barrier spin ran out
   int32_t pub_cap, pub_rank;  // set by launch_topk_step
 };

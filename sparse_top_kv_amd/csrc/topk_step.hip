@@ -29,12 +29,13 @@
 //   E  this chunk's kept indices into idx (ascending); the attention
 //      partial (max, sum, acc) over the chunk's kept rows -- sinks, the
 //      selected candidates, the recent run -- from the logits in LDS and
-//      V rows gathered by index; the head's last arriving workgroup merges
-//      the P partials into out and lse.
+//      V rows gathered by index, written in the split-K merge kernel's
+//      format; that kernel (a second launch) merges the P partials into out
+//      and lse and clears the step's counters.
 // "sync" is a barrier of the P workgroups of one kv head: a device-scope
 // arrival counter (its own 128-byte line in the workspace header, zero on
 // entry) that only counts up during the step (barrier k waits for k P
-// arrivals); the final arrival resets it.  Everything one workgroup hands to
+// arrivals); the merge launch resets it.  Everything one workgroup hands to
 // another is written with device-scope stores, completed (s_waitcnt) before
 // the arrival, and read with device-scope loads after it.
 //
@@ -44,9 +45,10 @@
 // workgroups of a head number at most P - 1 while its chunks are not all
 // drawn, so a device that holds (P - 1) Hkv + 1 workgroups at once (P <=
 // CUs / Hkv, one workgroup per CU) never stalls, with no cooperative launch.
-// The head's last arrival resets its counters.  Spins are still bounded: one
-// that runs out (other work holding the CUs far longer than a step) sets the
-// header's error word, and that step's results are unspecified.
+// The merge launch that follows resets the counters.  Spins are still
+// bounded: one that runs out (other work holding the CUs far longer than a
+// step) sets the header's error word, and that step's results are
+// unspecified.
 #include "skv_block.h"
 #include "skv_common.h"
 #include "skv_kernels.h"
@@ -167,26 +169,27 @@ struct TopkWs {
   uint32_t* tot2;   // [Hkv][2048]
   uint32_t* tot3;   // [Hkv][512]
   uint32_t* cnts;   // [Hkv][P][2] keys above T and equal to T
-  float* part;      // [Hkv][P][G][2 + D] attention partial (max, sum, acc)
+  float* part_ml;   // [Hkv][P][G][2] attention partial (max, sum), the merge kernel's format
+  float* part_acc;  // [Hkv][P][G][D] attention partial (acc)
   uint32_t* pub;    // [Hkv][P][pub_cap] each chunk's published keys
   uint32_t* edge;   // [Hkv][P][2] lower edge of the keys a chunk published; an upper bound of T
 };
 
-// Byte offsets of the scratch arrays (each 256-byte aligned); [8] = total.
-inline void topk_offsets(int hkv, int p, int g, int d, size_t (&off)[9]) {
-  const size_t bytes[8] = {(size_t)hkv * p * g * 2 * 4, (size_t)hkv * kBins1 * 4, (size_t)hkv * kBins2 * 4,
-                           (size_t)hkv * kBins3 * 4, (size_t)hkv * p * 2 * 4, (size_t)hkv * p * g * (2 + d) * 4,
-                           (size_t)hkv * kPubKeys * 4, (size_t)hkv * p * 2 * 4};
+// Byte offsets of the scratch arrays (each 256-byte aligned); [9] = total.
+inline void topk_offsets(int hkv, int p, int g, int d, size_t (&off)[10]) {
+  const size_t bytes[9] = {(size_t)hkv * p * g * 2 * 4, (size_t)hkv * kBins1 * 4, (size_t)hkv * kBins2 * 4,
+                           (size_t)hkv * kBins3 * 4, (size_t)hkv * p * 2 * 4, (size_t)hkv * p * g * 2 * 4,
+                           (size_t)hkv * kPubKeys * 4, (size_t)hkv * p * 2 * 4, (size_t)hkv * p * g * d * 4};
   size_t at = 0;
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 9; ++i) {
     off[i] = at;
     at += (bytes[i] + 255) / 256 * 256;
   }
-  off[8] = at;
+  off[9] = at;
 }
 
 inline TopkWs topk_ws_layout(const TopkArgs& a, void* scratch, int g, int d) {
-  size_t off[9];
+  size_t off[10];
   topk_offsets(a.n_kv_heads, a.chunks_per_head, g, d, off);
   char* b = (char*)scratch;
   TopkWs w;
@@ -195,9 +198,10 @@ inline TopkWs topk_ws_layout(const TopkArgs& a, void* scratch, int g, int d) {
   w.tot2 = (uint32_t*)(b + off[2]);
   w.tot3 = (uint32_t*)(b + off[3]);
   w.cnts = (uint32_t*)(b + off[4]);
-  w.part = (float*)(b + off[5]);
+  w.part_ml = (float*)(b + off[5]);
   w.pub = (uint32_t*)(b + off[6]);
   w.edge = (uint32_t*)(b + off[7]);
+  w.part_acc = (float*)(b + off[8]);
   return w;
 }
 
@@ -334,9 +338,9 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
   __shared__ __attribute__((aligned(1024))) char ring[2][kW][TB];
   __shared__ __attribute__((aligned(16))) float sm_lg[kLgFloats + 4 * 16];
   __shared__ float sm_m[kW][16], sm_l[kW][16];
-  __shared__ float sm_lse2[G], sm_M[G], sm_L[G];
+  __shared__ float sm_lse2[G];
   __shared__ uint32_t sm_w[kW + 1], sm_w2[2 * kW];
-  __shared__ uint32_t sm_digit, sm_krem, sm_base, sm_last, sm_item;
+  __shared__ uint32_t sm_digit, sm_krem, sm_base, sm_item;
   static_assert(2 * kW * TB >= kBins1 * 4, "the histograms fit the ring");
   // privatised copies (lane % kCopies) of the 2048-bin LDS histograms: as many
   // (a power of two, at most 8) as leave room in the ring for kRankMax keys
@@ -574,7 +578,6 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
   uint32_t T = K == 0 ? 0xFFFFFFFFu : 0u, take = 0, sel_before = 0, my_take = 0;
   uint32_t pre_gt = 0, pre_eq = 0;  // published keys of earlier chunks above / equal to T (this thread's)
   bool pub_path = false;
-  int nsync = 1;
   if (!radix) {
     if (K > 0) {  // every candidate: those of the chunks before this one
       const int64_t lo = r0 < c_lo ? c_lo : (r0 > c_hi ? c_hi : r0);
@@ -614,7 +617,6 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
       st_dev(w.edge + ((int64_t)h * P + c) * 2 + 1, ub);
     }
     head_sync(ctr, 2u * P, a.err);
-    nsync = 2;
     // the head's published keys: thread t holds words 4 (t + kT i) .. 4 (t + kT i) + 3
     const uint32_t nkeys = (uint32_t)(P * mcap);
     const BufRsrc rpub = make_rsrc(w.pub + (int64_t)h * P * mcap, nkeys * 4);
@@ -792,7 +794,6 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
         st_dev(w.cnts + ((int64_t)h * P + c) * 2 + 1, tot >> 16);
       }
       head_sync(ctr, 6u * P, a.err);
-      nsync = 6;
       // chunks before this one: selected keys and keys equal to T
       uint32_t sb = 0, eq_before = 0;
       for (int c0 = 0; c0 < c; c0 += kT) {
@@ -976,7 +977,8 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
       if (lane == 0) sm_m[wave][g] = mg[g];
     }
     __syncthreads();
-    float* pt = w.part + ((int64_t)h * P + c) * G * (2 + D);
+    float* pml = w.part_ml + ((int64_t)h * P + c) * G * 2;
+    float* pac = w.part_acc + ((int64_t)h * P + c) * G * D;
     for (int e = tid; e < G * (D + 1); e += kT) {
       const int g = e / (D + 1), x = e - g * (D + 1);
       float M = kNegInf;
@@ -988,93 +990,12 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
         const float mv = sm_m[v][g];
         s += mv == kNegInf ? 0.0f : red[(v * G + g) * (D + 1) + x] * fast_exp2(mv - M);
       }
-      if (x < D) st_dev(pt + g * (2 + D) + 2 + x, s);
+      if (x < D) pac[g * D + x] = s;
       else {
-        st_dev(pt + g * (2 + D), M);
-        st_dev(pt + g * (2 + D) + 1, s);
+        pml[g * 2] = M;
+        pml[g * 2 + 1] = s;
       }
     }
-  }
-  // final arrival: the head's last workgroup merges and resets the counter
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm_last = before == (uint32_t)(nsync + 1) * P - 1u;
-    if (sm_last) {  // every workgroup of the head has arrived: reset for the next step
-      st_dev(ctr, 0u);
-      st_dev(ctr + 16, 0u);
-    }
-  }
-  __syncthreads();
-  if (!sm_last) return;
-  // out[h G + g] = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M), M = max m_c.
-  // The chunks' (max, sum) pairs go to LDS (the logits are no longer needed),
-  // each query head's weights 2^(m_c - M) replace the maxima, then thread
-  // (g, x) adds channel x of the chunks' accumulators in chunk order.
-  const float* pt = w.part + (int64_t)h * P * G * (2 + D);
-  const BufRsrc rp = make_rsrc(pt, (uint32_t)((int64_t)P * G * (2 + D) * 4));
-  constexpr int kB = 32;  // accumulator loads in flight
-  // the first batch of this thread's first channel travels with the (max, sum) loads
-  float pre[kB];
-  if (tid < G * D) {
-    const int g = tid / D, x = tid - g * D;
-#pragma unroll
-    for (int u = 0; u < kB; ++u) {
-      const int cc = u < P ? u : P - 1;
-      pre[u] = buf_load_dev(rp, (uint32_t)((((int64_t)cc * G + g) * (2 + D) + 2 + x) * 4));
-    }
-  }
-  float* wt = sm_lg;            // [P][G]
-  float* lc = sm_lg + P * G;    // [P][G]
-  for (int e = tid; e < P * G; e += kT) {
-    wt[e] = ld_dev(pt + (int64_t)e * (2 + D));
-    lc[e] = ld_dev(pt + (int64_t)e * (2 + D) + 1);
-  }
-  __syncthreads();
-  for (int g = wave; g < G; g += kW) {
-    float M = kNegInf;
-    for (int cc = lane; cc < P; cc += 64) M = fmaxf(M, wt[cc * G + g]);
-    M = wave_max(M);
-    float L = 0.0f;
-    for (int cc = lane; cc < P; cc += 64) {
-      const float mc = wt[cc * G + g];
-      const float wg = mc == kNegInf ? 0.0f : fast_exp2(mc - M);
-      L = fmaf(lc[cc * G + g], wg, L);
-      wt[cc * G + g] = wg;
-    }
-    L = wave_sum(L);
-    if (lane == 0) {
-      sm_M[g] = M;
-      sm_L[g] = L;
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < G * D; e += kT) {
-    const int g = e / D, x = e - g * D;
-    float A = 0.0f;
-    int c_from = 0;
-    if (e == tid) {
-#pragma unroll
-      for (int u = 0; u < kB; ++u)
-        if (u < P) A = fmaf(pre[u], wt[u * G + g], A);
-      c_from = kB;
-    }
-    for (int c0 = c_from; c0 < P; c0 += kB) {
-      float v[kB];
-#pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        const int cc = c0 + u < P ? c0 + u : P - 1;
-        v[u] = buf_load_dev(rp, (uint32_t)((((int64_t)cc * G + g) * (2 + D) + 2 + x) * 4));
-      }
-#pragma unroll
-      for (int u = 0; u < kB; ++u)
-        if (c0 + u < P) A = fmaf(v[u], wt[(c0 + u) * G + g], A);
-    }
-    const float L = sm_L[g];
-    const int64_t o = (int64_t)h * G + g;
-    a.out[o * D + x] = L > 0.0f ? A / L : 0.0f;
-    if (x == 0 && a.lse) a.lse[o] = L > 0.0f ? (sm_M[g] + log2f(L)) * kLn2 : kNegInf;
   }
 }
 
@@ -1091,7 +1012,23 @@ hipError_t launch_dg(const TopkArgs& a, void* scratch, hipStream_t s) {
   b.pub_rank = (int32_t)(rank < b.pub_cap * 3 / 4 ? rank : b.pub_cap * 3 / 4);
   TopkWs w = topk_ws_layout(b, scratch, G, D);
   hipLaunchKernelGGL((topk_step_kernel<D, G>), dim3((unsigned)(a.n_kv_heads * P)), dim3(kT), 0, s, b, w);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the P partials of each kv head merged by the split-K merge kernel, which
+  // also clears the step's counters for its next call
+  MergeArgs m{};
+  m.part_ml = w.part_ml;
+  m.part_acc = w.part_acc;
+  m.nch = nullptr;
+  m.n_kv_heads = a.n_kv_heads;
+  m.cph = P;
+  m.rows_per_head = G;
+  m.group = G;
+  m.out = a.out;
+  m.lse = a.lse;
+  m.clear_ctr = a.ctr;
+  m.clear_heads = a.n_kv_heads;
+  return launch_merge(D, m, s);
 }
 
 template <int D>
@@ -1123,9 +1060,9 @@ int topk_step_max_chunk(int g, int d) { return d == 128 ? max_chunk_d<128>(g) : 
 int topk_step_granule() { return kGranule; }
 
 size_t topk_step_scratch(int hkv, int p, int g, int d) {
-  size_t off[9];
+  size_t off[10];
   topk_offsets(hkv, p, g, d, off);
-  return off[8];
+  return off[9];
 }
 
 hipError_t launch_topk_step(int d, int g, const TopkArgs& a, void* scratch, hipStream_t s) {
