@@ -88,12 +88,29 @@ def _check(q, k, v, n, S, R, K, dtype, tag):
     (32, 8, 128, 3000, 4, 64, 2932),     # every candidate
     (32, 8, 128, 3000, 4, 64, 5000),     # K past the candidate count
     (16, 2, 128, 777, 6, 9, 300),        # few kv heads, one short chunk each
+    (16, 8, 128, 30000, 4, 64, 2000),    # groups of two
+    (8, 8, 128, 60000, 2, 16, 3000),     # MHA at head dim 128: 32 keys per thread
+    (32, 8, 64, 50000, 4, 64, 4096),     # head dim 64, groups of four
 ])
 def test_topk_step_matches_oracle(hq, hkv, d, n, S, R, K):
     q = _rand((hq, d), n + 1, "bf16")
     k = _rand((hkv, n + 2, d), n + 2, "bf16")
     v = _rand((hkv, n + 2, d), n + 3, "bf16")
     _check(q, k, v, n, S, R, K, "bf16", "one launch")
+
+
+def test_topk_step_without_lse():
+    """lse may be NULL; out is unchanged by leaving it out."""
+    hq, hkv, d, n, S, R, K = 32, 8, 128, 9000, 4, 64, 700
+    q = dev(_rand((hq, d), 31, "bf16"))
+    k = dev(_rand((hkv, n, d), 32, "bf16"))
+    v = dev(_rand((hkv, n, d), 33, "bf16"))
+    ws = skv.Workspace.for_problem(skv.problem_for(q, k), n)
+    score, idx, cnt, out, lse = _run_step(q, k, v, n, S, R, K, ws)
+    out2 = torch.full_like(out, float("nan"))
+    skv.skv_topk_step(q, k, v, n, S, R, K, score, idx, cnt, out2, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
 
 
 def test_topk_step_exact_ties_keep_the_lowest_indices():
