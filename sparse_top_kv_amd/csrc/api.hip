@@ -415,6 +415,40 @@ TopkPlan topk_plan(const skv_problem* p, int64_t n, int cus) {
   return t;
 }
 
+// The selection alone in one launch (long rows with few kv heads): chunks of
+// at most topk_select_max_chunk() scores, P = ceil(n / chunk) <= CUs / Hkv,
+// and K small enough against the chunks that each chunk's publishing rank
+// (2 ceil(K / P) + 16) fits the published-key budget: larger K, whose keys
+// rarely fit and then take the six-barrier radix levels, stays with the
+// three-kernel select.
+struct SelPlan {
+  bool one = false;
+  int chunk = 0, P = 0;
+};
+SelPlan select_plan(int32_t hkv, int64_t n, int64_t k_max, int cus) {
+  SelPlan t;
+  if (n <= 16384 || hkv >= kTopkMaxKvHeads || cus < hkv) return t;
+  const int pmax = cus / hkv, gr = skv::topk_step_granule();
+  int64_t chunk = (n + pmax - 1) / pmax;
+  chunk = (chunk + gr - 1) / gr * gr;
+  if (chunk > skv::topk_select_max_chunk()) return t;
+  const int64_t P = (n + chunk - 1) / chunk;
+  const int64_t cap = (skv::topk_publish_budget() / P) & ~3;
+  if (2 * ((k_max + P - 1) / P) + 16 > cap * 3 / 4) return t;
+  t.one = true;
+  t.chunk = (int)chunk;
+  t.P = (int)P;
+  return t;
+}
+size_t select_one_scratch_bound(int32_t hkv, int64_t n_max) {
+  if (n_max <= 16384 || hkv >= kTopkMaxKvHeads) return 0;
+  int64_t P = kMaxCUs / hkv;
+  const int64_t pn = (n_max + skv::topk_step_granule() - 1) / skv::topk_step_granule();
+  P = P < pn ? P : pn;
+  P = P < 1 ? 1 : P;
+  return skv::topk_select_scratch(hkv, (int)P);
+}
+
 // Scratch of the fused step for any device: P <= kMaxCUs / Hkv and P <= n / granule.
 size_t topk_scratch_bound(const skv_problem* p, int64_t n_max) {
   if (p->dtype != SKV_BF16 || p->n_kv_heads > kTopkMaxKvHeads) return 0;
@@ -451,6 +485,8 @@ size_t skv_workspace_size(const skv_problem* p, int64_t n_max, int32_t rows_max)
   t = score_step_scratch(p, n_max);
   s = s > t ? s : t;
   t = skv::select_ws_bytes(p->n_kv_heads, n_max);
+  s = s > t ? s : t;
+  t = select_one_scratch_bound(p->n_kv_heads, n_max);
   s = s > t ? s : t;
   t = topp_scratch(n_max);
   s = s > t ? s : t;
@@ -608,6 +644,28 @@ skv_status skv_select(const skv_problem* p, const float* score, int64_t score_st
     return SKV_ERR_INVALID_ARG;
   if (idx_stride < (int64_t)n_sink + k_max || (idx_stride > 0 && !idx)) return SKV_ERR_INVALID_ARG;
   if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
+  const SelPlan sp = select_plan(p->n_kv_heads, n, k_per_head ? k_max : k_uniform, device_cus());
+  if (sp.one) {  // long rows, few kv heads: one launch
+    const size_t need = SKV_WS_HEADER_BYTES + skv::topk_select_scratch(p->n_kv_heads, sp.P);
+    if ((st = check_ws(ws, ws_bytes, need)) != SKV_OK) return st;
+    skv::TopkArgs a{};
+    a.score = const_cast<float*>(score);  // read only
+    a.score_stride = score_stride;
+    a.n = n;
+    a.n_sink = n_sink;
+    a.n_recent = n_recent;
+    a.k_top = k_uniform;
+    a.k_per_head = k_per_head;
+    a.n_kv_heads = p->n_kv_heads;
+    a.chunk = sp.chunk;
+    a.chunks_per_head = sp.P;
+    a.idx = idx;
+    a.idx_stride = idx_stride;
+    a.count = count;
+    a.ctr = (uint32_t*)((char*)ws + kTopkCtrOffset);
+    a.err = (uint32_t*)((char*)ws + kTopkErrOffset);
+    return hip_status(skv::launch_topk_select(a, (char*)ws + SKV_WS_HEADER_BYTES, (hipStream_t)stream));
+  }
   const size_t sel_ws = skv::select_ws_bytes(p->n_kv_heads, n);
   if (sel_ws > 0 && (st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + sel_ws)) != SKV_OK) return st;
   skv::SelectArgs a{};

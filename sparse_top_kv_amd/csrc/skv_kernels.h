@@ -190,12 +190,21 @@ struct TopkArgs {
   float* lse;               // [Hq], may be null
   uint32_t* ctr;            // per kv head 32 words: arrivals (word 0), ticket (word 16); zero on entry, cleared by the merge
   uint32_t* err;            // set to 1 if a barrier spin ran out
-  int32_t pub_cap, pub_rank;  // set by launch_topk_step
+  int32_t pub_cap;          // set by the launch
+  const int32_t* k_per_head;  // [Hkv] or null (selection alone; the step keeps k_top)
 };
 hipError_t launch_topk_step(int d, int g, const TopkArgs& a, void* scratch, hipStream_t stream);
 int topk_step_max_chunk(int g, int d);
 int topk_step_granule();
 size_t topk_step_scratch(int hkv, int p, int g, int d);
+// The same kernel doing the selection alone (skv_select, long rows with few kv
+// heads): `score` is read, q/k/v/out unused; chunks of at most
+// topk_select_max_chunk() scores; no merge launch (the last arrival clears
+// the counters).
+hipError_t launch_topk_select(const TopkArgs& a, void* scratch, hipStream_t stream);
+int topk_select_max_chunk();
+int topk_publish_budget();  // keys a kv head's chunks may publish in all
+size_t topk_select_scratch(int hkv, int p);
 
 // Compaction of a kept set (skv_gather).
 struct GatherArgs {

@@ -64,6 +64,7 @@ constexpr int kLgFloats = 16384;      // logits of one chunk, all query heads of
 constexpr int kGranule = kW * kStep;  // chunk granule (one tile per wave)
 constexpr uint32_t kSpinMax = 1u << 20;
 constexpr int kBins1 = 4096, kBins2 = 2048, kBins3 = 512;
+constexpr int kSelKpt = 8;            // keys per thread of the selection alone (chunks of 4096)
 constexpr int kPubKeys = 16384;       // keys a kv head's chunks publish, at most
 constexpr int kPubW = kPubKeys / kT / 4;  // 16-byte words of them per thread
 constexpr int kRankMax = 512;         // keys of the threshold's bin ranked directly
@@ -324,19 +325,22 @@ __device__ __forceinline__ float buf_load_dev(BufRsrc r, uint32_t voff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 16));  // sc1
 }
 
-template <int D, int G>
+// SEL: the selection alone over a given score row (skv_select on long rows
+// with few kv heads): no K stream, no attention; the same exchange and
+// threshold search, with keys of any sign.
+template <int D, int G, bool SEL>
 __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const TopkWs w) {
   using TG = TileGeom<D>;
   using CK = Chunk<D, G>;
   constexpr int NI = TG::kNI, TB = TG::kTB, PPR = TG::kPPR, KS = TG::kKS;
-  constexpr int KPT = CK::kPer;
+  constexpr int KPT = SEL ? kSelKpt : CK::kPer;
   constexpr int LPR = D / 8;  // lanes per V row (16 bytes each)
   constexpr int RSL = kT / LPR;  // V rows in flight per workgroup step
   static_assert(KPT <= 32, "candidate flags fit one word per thread");
 
   // K ring (two stages per wave), later the histograms and the kept list
   __shared__ __attribute__((aligned(1024))) char ring[2][kW][TB];
-  __shared__ __attribute__((aligned(16))) float sm_lg[kLgFloats + 4 * 16];
+  __shared__ __attribute__((aligned(16))) float sm_lg[SEL ? 4 : kLgFloats + 4 * 16];
   __shared__ float sm_m[kW][16], sm_l[kW][16];
   __shared__ float sm_lse2[G];
   __shared__ uint32_t sm_w[kW + 1], sm_w2[2 * kW];
@@ -347,6 +351,15 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
   constexpr int kFit = (2 * kW * TB / 4 - kRankMax - 64) / 2048;
   constexpr int kCopies = kFit >= 8 ? 8 : (kFit >= 4 ? 4 : (kFit >= 2 ? 2 : 1));
   static_assert(kFit >= 1, "a histogram and the ranked keys fit the ring");
+  // the chunk's local histogram of key bits 31..20: scores are probabilities
+  // in the step (keys >= 2^31: bins 2048..4095), of either sign in SEL
+  constexpr int kHB = SEL ? 4096 : 2048;
+  constexpr int kFitB = (2 * kW * TB / 4) / kHB;
+  constexpr int kCopiesB = SEL ? (kFitB >= 4 ? 4 : (kFitB >= 2 ? 2 : 1)) : kCopies;
+  auto hbin = [](uint32_t k) -> uint32_t { return SEL ? k >> 20 : (k >> 20) & 2047u; };
+  // barriers of the head so far when C starts: one (the logits' statistics)
+  // in the step, none in SEL
+  constexpr uint32_t kSb = SEL ? 0u : 1u;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -367,12 +380,12 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
   const int lg_stride = a.chunk + 4;  // floats per head row in sm_lg
 
   // ---- A: logits of this chunk -------------------------------------------
-  if (c == 0) {  // the head's radix totals start at zero (first added after sync 1)
+  if (c == 0) {  // the head's radix totals start at zero (first added after a barrier)
     for (int i = tid; i < kBins1; i += kT) st_dev(w.tot1 + (int64_t)h * kBins1 + i, 0u);
     for (int i = tid; i < kBins2; i += kT) st_dev(w.tot2 + (int64_t)h * kBins2 + i, 0u);
     for (int i = tid; i < kBins3; i += kT) st_dev(w.tot3 + (int64_t)h * kBins3 + i, 0u);
   }
-  {
+  if constexpr (!SEL) {
     bf16x8_t qb[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -469,10 +482,10 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
       st_dev(st + 1, L);
     }
   }
-  head_sync(ctr, (uint32_t)P, a.err);
+  if constexpr (!SEL) head_sync(ctr, (uint32_t)P, a.err);
 
   // ---- B: scores, level-1 histogram ----------------------------------------
-  for (int g = wave; g < G; g += kW) {
+  for (int g = wave; g < (SEL ? 0 : G); g += kW) {
     // the same reduction as the per-step score kernel's finalize
     const float* st = w.stats + (int64_t)h * P * G * 2;
     const bool in0 = lane < P;
@@ -495,10 +508,13 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
   const int64_t tail = n - a.n_recent > 0 ? n - a.n_recent : 0;
   const int64_t nsink = a.n_sink < tail ? a.n_sink : tail;
   const int64_t ncand = c_lo < c_hi ? c_hi - c_lo : 0;
-  const int64_t K = a.k_top < ncand ? a.k_top : ncand;
+  int64_t kh = a.k_top;
+  if constexpr (SEL)
+    if (a.k_per_head) kh = a.k_per_head[h] < 0 ? 0 : a.k_per_head[h];  // clamped to [0, #candidates]
+  const int64_t K = kh < ncand ? kh : ncand;
   const bool radix = K > 0 && K < ncand;  // uniform: otherwise the selection goes by index
-  if (radix) {  // the candidate half of the 12-bit bins (2048..4095)
-    for (int i = tid; i < kCopies * 2048 / 4; i += kT) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (radix) {
+    for (int i = tid; i < kCopiesB * kHB / 4; i += kT) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
   }
   const int rb0 = KPT * tid;
@@ -510,7 +526,32 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
     float sc[KPT];
 #pragma unroll
     for (int u = 0; u < KPT; ++u) sc[u] = 0.0f;
-    if (interior) {
+    if constexpr (SEL) {  // the given scores: 16-byte loads where the row allows them
+      const float* srow = a.score + (int64_t)h * a.score_stride + r0 + rb0;
+      if (((uintptr_t)a.score & 15u) == 0 && (a.score_stride & 3) == 0 && rb0 + KPT <= rows) {
+#pragma unroll
+        for (int v = 0; v < KPT / 4; ++v) {
+          const float4 x = reinterpret_cast<const float4*>(srow)[v];
+          sc[4 * v] = x.x;
+          sc[4 * v + 1] = x.y;
+          sc[4 * v + 2] = x.z;
+          sc[4 * v + 3] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u)
+          if (rb0 + u < rows) sc[u] = srow[u];
+      }
+      if (interior) {
+        cand = KPT >= 32 ? 0xFFFFFFFFu : (1u << KPT) - 1u;
+      } else {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+          const int64_t j = r0 + rb0 + u;
+          cand |= (rb0 + u < rows && j >= c_lo && j < c_hi ? 1u : 0u) << u;
+        }
+      }
+    } else if (interior) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float l2 = sm_lse2[g];
@@ -544,7 +585,7 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
         cand |= (rb0 + u < rows && j >= c_lo && j < c_hi ? 1u : 0u) << u;
       }
     }
-    if (a.score) {  // 16-byte stores where the row allows them
+    if (!SEL && a.score) {  // 16-byte stores where the row allows them
       float* srow = a.score + (int64_t)h * a.score_stride + r0 + rb0;
       bool vec = false;
       if constexpr (KPT % 4 == 0)
@@ -564,11 +605,11 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
     if (radix) {
       if (interior) {
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) atomicAdd(&hist[(lane % kCopies) * 2048 + ((key[u] >> 20) & 2047u)], 1u);
+        for (int u = 0; u < KPT; ++u) atomicAdd(&hist[(lane % kCopiesB) * kHB + hbin(key[u])], 1u);
       } else {
 #pragma unroll
         for (int u = 0; u < KPT; ++u)
-          if ((cand >> u) & 1u) atomicAdd(&hist[(lane % kCopies) * 2048 + ((key[u] >> 20) & 2047u)], 1u);
+          if ((cand >> u) & 1u) atomicAdd(&hist[(lane % kCopiesB) * kHB + hbin(key[u])], 1u);
       }
     }
   }
@@ -578,6 +619,7 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
   uint32_t T = K == 0 ? 0xFFFFFFFFu : 0u, take = 0, sel_before = 0, my_take = 0;
   uint32_t pre_gt = 0, pre_eq = 0;  // published keys of earlier chunks above / equal to T (this thread's)
   bool pub_path = false;
+  uint32_t nb = kSb;  // barriers of the head passed so far
   if (!radix) {
     if (K > 0) {  // every candidate: those of the chunks before this one
       const int64_t lo = r0 < c_lo ? c_lo : (r0 > c_hi ? c_hi : r0);
@@ -596,9 +638,15 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
     // bins of local rank pub_rank (the publishing edge) and ceil(K / P): some
     // chunk holds that many of the top K, so T lies below the upper edge of
     // the latter's bin in some chunk
-    pick2_lds<2048, kCopies>(hist, (uint32_t)a.pub_rank, (uint32_t)((K + P - 1) / P), sm_w, &sm_digit, &sm_krem);
-    const uint32_t dl = sm_digit ? sm_digit + 2047u : 0u;  // 0: fewer candidates, all published
-    const uint32_t ub = sm_krem == 0u ? 0u : (sm_krem >= 2048u ? 0xFFFFFFFFu : (sm_krem + 2048u) << 20);
+    const int64_t share = (K + P - 1) / P;
+    const int64_t rank = 2 * share + 16 < (int64_t)(mcap * 3 / 4) ? 2 * share + 16 : (int64_t)(mcap * 3 / 4);
+    pick2_lds<kHB, kCopiesB>(hist, (uint32_t)(rank > 0 ? rank : 1), (uint32_t)share, sm_w, &sm_digit, &sm_krem);
+    // 12-bit bins of the two ranks (their index + 1 from the pick, 0 when the
+    // chunk has fewer candidates): the publishing edge dl (0: publish all)
+    // and the upper edge ub of the second bin
+    constexpr uint32_t kOff = SEL ? 0u : 2048u;
+    const uint32_t dl = sm_digit ? sm_digit - 1u + kOff : 0u;
+    const uint32_t ub = sm_krem == 0u ? 0u : (sm_krem + kOff >= 4096u ? 0xFFFFFFFFu : (sm_krem + kOff) << 20);
     uint32_t np = 0;
 #pragma unroll
     for (int u = 0; u < KPT; ++u) np += (((cand >> u) & 1u) && (key[u] >> 20) >= dl) ? 1u : 0u;
@@ -616,7 +664,8 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
       st_dev(w.edge + ((int64_t)h * P + c) * 2, fits ? (dl << 20) : 0xFFFFFFFFu);
       st_dev(w.edge + ((int64_t)h * P + c) * 2 + 1, ub);
     }
-    head_sync(ctr, 2u * P, a.err);
+    head_sync(ctr, (kSb + 1u) * P, a.err);
+    nb = kSb + 1u;
     // the head's published keys: thread t holds words 4 (t + kT i) .. 4 (t + kT i) + 3
     const uint32_t nkeys = (uint32_t)(P * mcap);
     const BufRsrc rpub = make_rsrc(w.pub + (int64_t)h * P * mcap, nkeys * 4);
@@ -634,7 +683,8 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
     uint32_t edge_max, up;  // T < up (up >= 2^31 + 2^20)
     wg_max2_u32(em, um, sm_w2, &edge_max, &up);
     // only keys >= lo can be T (the search fails when fewer than K are)
-    const uint32_t lo = edge_max > 0x80000000u ? edge_max : 0x80000000u;
+    // (above the zero padding; step scores are probabilities, keys >= 2^31)
+    const uint32_t lo = edge_max > (SEL ? 1u : 0x80000000u) ? edge_max : (SEL ? 1u : 0x80000000u);
     bool valid = edge_max != 0xFFFFFFFFu && lo < up;
     if (valid) {
       // 2048 bins of width 2^sh over [lo, up) (keys above in the last one,
@@ -750,7 +800,7 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
         const uint32_t x = hist[i];
         if (x) atomicAdd(w.tot1 + (int64_t)h * kBins1 + i, x);
       }
-      head_sync(ctr, 3u * P, a.err);
+      head_sync(ctr, (kSb + 2u) * P, a.err);
       pick_bin<kBins1>(w.tot1 + (int64_t)h * kBins1, (uint32_t)K, sm_w, &sm_digit, &sm_krem);
       const uint32_t d1 = sm_digit, krem1 = sm_krem;
       for (int i = tid; i < kBins2; i += kT) hist[i] = 0u;
@@ -763,7 +813,7 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
         const uint32_t x = hist[i];
         if (x) atomicAdd(w.tot2 + (int64_t)h * kBins2 + i, x);
       }
-      head_sync(ctr, 4u * P, a.err);
+      head_sync(ctr, (kSb + 3u) * P, a.err);
       pick_bin<kBins2>(w.tot2 + (int64_t)h * kBins2, krem1, sm_w, &sm_digit, &sm_krem);
       const uint32_t q2 = (d1 << 11) | sm_digit, krem2 = sm_krem;
       for (int i = tid; i < kBins3; i += kT) hist[i] = 0u;
@@ -776,7 +826,7 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
         const uint32_t x = hist[i];
         if (x) atomicAdd(w.tot3 + (int64_t)h * kBins3 + i, x);
       }
-      head_sync(ctr, 5u * P, a.err);
+      head_sync(ctr, (kSb + 4u) * P, a.err);
       pick_bin<kBins3>(w.tot3 + (int64_t)h * kBins3, krem2, sm_w, &sm_digit, &sm_krem);
       T = (q2 << 9) | sm_digit;
       take = sm_krem;
@@ -793,7 +843,8 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
         st_dev(w.cnts + ((int64_t)h * P + c) * 2, tot & 0xFFFFu);
         st_dev(w.cnts + ((int64_t)h * P + c) * 2 + 1, tot >> 16);
       }
-      head_sync(ctr, 6u * P, a.err);
+      head_sync(ctr, (kSb + 5u) * P, a.err);
+      nb = kSb + 5u;
       // chunks before this one: selected keys and keys equal to T
       uint32_t sb = 0, eq_before = 0;
       for (int c0 = 0; c0 < c; c0 += kT) {
@@ -877,6 +928,29 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
       const bool forced = !interior && rb0 + u < rows && (j < nsink || j >= tail);
       selm |= (s_ ? 1u : 0u) << u;
       keepm |= (s_ || forced ? 1u : 0u) << u;
+    }
+    if constexpr (SEL) {  // the selection alone: indices, count, and the counters' reset
+      (void)k_at;
+      (void)nkeep;
+      int32_t* orow = a.idx + (int64_t)h * a.idx_stride;
+      for (uint32_t m = selm; m; m &= m - 1u) {
+        if (s_at < (uint64_t)a.idx_stride) orow[s_at] = (int32_t)(r0 + rb0 + __builtin_ctz(m));
+        ++s_at;
+      }
+      if (c == 0) {
+        for (int64_t i = tid; i < nsink; i += kT) orow[i] = (int32_t)i;
+        if (tid == 0) a.count[h] = (int32_t)(nsink + K);
+      }
+      // the head's last arrival (after its last barrier) clears its counters
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t fin = (nb + 1u) * (uint32_t)P;
+        if (__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == fin - 1u) {
+          st_dev(ctr, 0u);
+          st_dev(ctr + 16, 0u);
+        }
+      }
+      return;
     }
     uint32_t* kept = hist;  // the chunk's kept rows (the ring is free again)
     for (uint32_t m = keepm; m; m &= m - 1u) kept[k_at++] = (uint32_t)(rb0 + __builtin_ctz(m));
@@ -1003,15 +1077,12 @@ template <int D, int G>
 hipError_t launch_dg(const TopkArgs& a, void* scratch, hipStream_t s) {
   if (a.chunks_per_head > kMaxP || a.chunks_per_head < 1) return hipErrorInvalidValue;
   TopkArgs b = a;
-  // each chunk publishes up to pub_cap keys, from its bin of local rank
-  // pub_rank up: twice a chunk's even share of the top K, and some
+  // each chunk publishes up to pub_cap keys
   const int P = a.chunks_per_head;
   b.pub_cap = (kPubKeys / P) & ~3;
-  const int64_t share = (a.k_top + P - 1) / P;
-  const int64_t rank = 2 * share + 16;
-  b.pub_rank = (int32_t)(rank < b.pub_cap * 3 / 4 ? rank : b.pub_cap * 3 / 4);
+  b.k_per_head = nullptr;
   TopkWs w = topk_ws_layout(b, scratch, G, D);
-  hipLaunchKernelGGL((topk_step_kernel<D, G>), dim3((unsigned)(a.n_kv_heads * P)), dim3(kT), 0, s, b, w);
+  hipLaunchKernelGGL((topk_step_kernel<D, G, false>), dim3((unsigned)(a.n_kv_heads * P)), dim3(kT), 0, s, b, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the P partials of each kv head merged by the split-K merge kernel, which
@@ -1064,6 +1135,19 @@ size_t topk_step_scratch(int hkv, int p, int g, int d) {
   topk_offsets(hkv, p, g, d, off);
   return off[9];
 }
+
+hipError_t launch_topk_select(const TopkArgs& a, void* scratch, hipStream_t s) {
+  if (a.chunks_per_head > kMaxP || a.chunks_per_head < 1 || a.chunk > kSelKpt * kT) return hipErrorInvalidValue;
+  TopkArgs b = a;
+  const int P = a.chunks_per_head;
+  b.pub_cap = (kPubKeys / P) & ~3;
+  TopkWs w = topk_ws_layout(b, scratch, 1, 128);
+  hipLaunchKernelGGL((topk_step_kernel<128, 1, true>), dim3((unsigned)(a.n_kv_heads * P)), dim3(kT), 0, s, b, w);
+  return hipGetLastError();
+}
+int topk_select_max_chunk() { return kSelKpt * kT; }
+int topk_publish_budget() { return kPubKeys; }
+size_t topk_select_scratch(int hkv, int p) { return topk_step_scratch(hkv, p, 1, 128); }
 
 hipError_t launch_topk_step(int d, int g, const TopkArgs& a, void* scratch, hipStream_t s) {
   if (d == 128) return launch_d<128>(g, a, scratch, s);

@@ -184,6 +184,30 @@ def test_select_block_path_uniform_k(hkv, n, K):
     check_select(s, 4, 64, K)
 
 
+@pytest.mark.parametrize("n", [131072, 131072 + 37, 40000])
+def test_select_one_launch_ties_signs_and_ragged_k(n):
+    """Long rows with few kv heads and K small against the row (here at most
+    4096 of up to 131K) take the one-launch select: per-head K at 0, 1, and
+    up to 4096, on scores with long exact tie runs, an all-equal row, +-0, a
+    tie run across a chunk border, negative scores and a row whose top keys
+    all sit in one chunk (which the published keys cannot cover: the radix
+    levels decide)."""
+    banner(f"select one launch n={n}")
+    hkv, S, R = 8, 4, 64
+    rng = np.random.default_rng(n + 1)
+    s = rng.exponential(1.0, (hkv, n)).astype(np.float32)
+    s[1] = np.round(s[1] * 4) / 4              # few distinct values: long tie runs
+    s[2] = 0.5                                 # all equal: lowest indices win
+    s[3, ::2] = -0.0
+    s[3, 1::2] = 0.0
+    s[4, 4000:4200] = 1e6                      # a tie run across a chunk border
+    s[5] = -s[5]                               # negative scores
+    s[6, 9000:13000] += 100.0                  # the top K of head 6 in one place
+    ks = [0, 1, 4096, 2000, 17, 4095, 300, 1024]
+    check_select(s, S, R, 0, k_per_head=ks, k_max=4096)
+    check_select(s, S, R, 4096)
+
+
 def test_select_block_path_leaves_header_zero():
     """The block path keeps head totals in the workspace header: two calls in a
     row on one workspace (different scores and K) both match the oracle, and
