@@ -206,14 +206,6 @@ inline TopkWs topk_ws_layout(const TopkArgs& a, void* scratch, int g, int d) {
   return w;
 }
 
-__device__ __forceinline__ void st_dev(uint2* p, uint2 v) {
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint2 ld_dev(const uint2* p) {
-  return __builtin_bit_cast(uint2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT));
-}
 
 // The bin of rank krem (1 = the largest key) in an LDS histogram of NB bins
 // held as NC copies [NC][NB] to be summed (thread t holds bins NB - 1 - PER t
@@ -320,9 +312,6 @@ __device__ __forceinline__ void wg_max2_u32(uint32_t a, uint32_t b, uint32_t* sm
 
 __device__ __forceinline__ uint4 buf_load16_dev(BufRsrc r, uint32_t voff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 16));  // sc1
-}
-__device__ __forceinline__ float buf_load_dev(BufRsrc r, uint32_t voff) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 16));  // sc1
 }
 
 // SEL: the selection alone over a given score row (skv_select on long rows
