@@ -508,7 +508,17 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
   }
   const int rb0 = KPT * tid;
   uint32_t key[KPT];
-  uint32_t cand = 0;  // bit u: row rb0 + u is a candidate
+  // bit u: row rb0 + u lies in [lo, hi) and in the chunk (chunk-relative bounds)
+  auto run_mask = [&](int64_t lo, int64_t hi) -> uint32_t {
+    hi = hi > rows ? rows : hi;
+    lo = lo < rb0 ? 0 : (lo > rb0 + KPT ? KPT : lo - rb0);
+    hi = hi < rb0 ? 0 : (hi > rb0 + KPT ? KPT : hi - rb0);
+    auto below = [](int64_t x) -> uint32_t { return x >= 32 ? 0xFFFFFFFFu : (1u << x) - 1u; };
+    return hi > lo ? below(hi) & ~below(lo) : 0u;
+  };
+  // candidates of this thread: its rows inside the chunk and inside [c_lo, c_hi)
+  const int64_t cl0 = (c_lo > r0 ? c_lo : r0) - r0, ch0 = (c_hi < r0 + rows ? c_hi : r0 + rows) - r0;
+  const uint32_t cand = run_mask(cl0, ch0);
   // every thread holds KPT rows and all are candidates (no sink, no recent row)
   const bool interior = rows == KPT * kT && r0 >= c_lo && r0 + rows <= c_hi;
   {
@@ -531,16 +541,10 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
         for (int u = 0; u < KPT; ++u)
           if (rb0 + u < rows) sc[u] = srow[u];
       }
-      if (interior) {
-        cand = KPT >= 32 ? 0xFFFFFFFFu : (1u << KPT) - 1u;
-      } else {
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-          const int64_t j = r0 + rb0 + u;
-          cand |= (rb0 + u < rows && j >= c_lo && j < c_hi ? 1u : 0u) << u;
-        }
-      }
-    } else if (interior) {
+    } else if (rb0 < rows) {
+      // every thread with rows reads all KPT logits: rows past the chunk's
+      // end read words of the LDS buffer that nothing wrote (still inside
+      // it) and are masked out by the candidate flags and the stores below
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float l2 = sm_lse2[g];
@@ -558,20 +562,6 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
 #pragma unroll
           for (int u = 0; u < KPT; ++u) sc[u] += fast_exp2(lr[u] - l2);
         }
-      }
-      cand = KPT >= 32 ? 0xFFFFFFFFu : (1u << KPT) - 1u;
-    } else {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float l2 = sm_lse2[g];
-#pragma unroll
-        for (int u = 0; u < KPT; ++u)
-          if (rb0 + u < rows) sc[u] += fast_exp2(sm_lg[g * lg_stride + rb0 + u] - l2);
-      }
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        const int64_t j = r0 + rb0 + u;
-        cand |= (rb0 + u < rows && j >= c_lo && j < c_hi ? 1u : 0u) << u;
       }
     }
     if (!SEL && a.score) {  // 16-byte stores where the row allows them
@@ -861,14 +851,15 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
     // chunk's selection, its kept rows there plus the forced rows (sinks,
     // recent run) before it.  The same exchange sums the published keys of
     // earlier chunks (the selection before this chunk).
-    uint32_t n_gt = 0, n_eq = 0, n_f = 0;
+    // the forced rows of this thread: sinks and the recent run
+    const uint32_t forcedm = interior ? 0u : (run_mask(-r0, nsink - r0) | run_mask(tail - r0, rows));
+    uint32_t n_gt = 0, n_eq = 0;
+    const uint32_t n_f = (uint32_t)__builtin_popcount(forcedm);
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
       const bool cu = (cand >> u) & 1u;
-      const int64_t j = r0 + rb0 + u;
       n_gt += (cu && key[u] > T) ? 1u : 0u;
       n_eq += (cu && key[u] == T) ? 1u : 0u;
-      n_f += (!interior && rb0 + u < rows && (j < nsink || j >= tail)) ? 1u : 0u;
     }
     uint32_t ex_gf, ex_eq, tot_gf, tot_eq, tot_pre;
     {
@@ -913,11 +904,9 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
       const bool eq = cu && key[u] == T;
       const bool s_ = cu && (key[u] > T || (eq && eq_rank < my_take));
       eq_rank += eq ? 1u : 0u;
-      const int64_t j = r0 + rb0 + u;
-      const bool forced = !interior && rb0 + u < rows && (j < nsink || j >= tail);
       selm |= (s_ ? 1u : 0u) << u;
-      keepm |= (s_ || forced ? 1u : 0u) << u;
     }
+    keepm = selm | forcedm;
     if constexpr (SEL) {  // the selection alone: indices, count, and the counters' reset
       (void)k_at;
       (void)nkeep;
@@ -949,7 +938,7 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
     // x; m is the wave's running maximum (rescaled when a batch raises it).
     const int slot = tid / LPR, piece = tid - slot * LPR;
     const char* vb = a.v + (int64_t)h * a.head_stride_b + piece * 16;
-    constexpr int kU = 4;
+    constexpr int kU = G <= 4 ? 8 : 4;  // rows per slot in flight
     uint4 vr[kU];
     uint32_t rr[kU];
 #pragma unroll
