@@ -502,10 +502,10 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
     if (a.k_per_head) kh = a.k_per_head[h] < 0 ? 0 : a.k_per_head[h];  // clamped to [0, #candidates]
   const int64_t K = kh < ncand ? kh : ncand;
   const bool radix = K > 0 && K < ncand;  // uniform: otherwise the selection goes by index
-  if (radix) {
+  // (this barrier also publishes sm_lse2 to every wave)
+  if (radix)
     for (int i = tid; i < kCopiesB * kHB / 4; i += kT) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
-  }
+  if (radix || !SEL) __syncthreads();
   const int rb0 = KPT * tid;
   uint32_t key[KPT];
   // bit u: row rb0 + u lies in [lo, hi) and in the chunk (chunk-relative bounds)

@@ -91,6 +91,10 @@ def _check(q, k, v, n, S, R, K, dtype, tag):
     (16, 8, 128, 30000, 4, 64, 2000),    # groups of two
     (8, 8, 128, 60000, 2, 16, 3000),     # MHA at head dim 128: 32 keys per thread
     (32, 8, 64, 50000, 4, 64, 4096),     # head dim 64, groups of four
+    # no threshold search (K = 0, K = every candidate) on full chunks: every
+    # wave reads the lse of every query head
+    (32, 8, 128, 131072, 4, 64, 0),
+    (32, 8, 128, 70000, 4, 64, 70000),
 ])
 def test_topk_step_matches_oracle(hq, hkv, d, n, S, R, K):
     q = _rand((hq, d), n + 1, "bf16")
