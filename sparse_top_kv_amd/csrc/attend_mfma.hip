@@ -64,7 +64,8 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
   __shared__ __attribute__((aligned(1024))) char st2[W][2 * TB];
   __shared__ __attribute__((aligned(1024))) char st3[W][2 * TB];
   __shared__ __attribute__((aligned(16))) uint32_t sm_off[SPARSE ? kSparseMaxChunk : 1];
-  __shared__ float sm_m[S][W][16], sm_l[S][W][16];
+  __shared__ float sm_m[S][W][16];
+  __shared__ __attribute__((aligned(16))) float sm_l[S][W][16];
   static_assert(S >= 2 && S <= 4, "ring of two to four stages");
   static_assert(16 * D * 4 <= 2 * TB, "a wave's 16-row partial fits its first stage");
   static_assert(!(SPARSE && CAUSAL), "the causal pass is dense");
@@ -449,19 +450,24 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
       }
     }
     __syncthreads();
+    // item (u, row quad q, column dd), columns fastest: each wave's quad is
+    // one 16-byte LDS read, and a wave's stores are whole row segments
+    for (int e = tid; e < GPR * 4 * D; e += kT) {
+      const int dd = e % D, q = (e / D) % 4, u = e / (4 * D);
+      const int gi = g0 + u, r0q = 16 * gi + 4 * q;  // first row of the quad
+      if (gi < NG && r0q < R) {
+        const int at = dd * 16 + 4 * (q ^ ((dd >> 1) & 3));
+        float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int u = 0; u < GPR; ++u) {
-      const int gi = g0 + u;
-      if (gi < NG && 16 * gi < R) {
-        const int rg = R - 16 * gi < 16 ? R - 16 * gi : 16;  // rows of this group
-        for (int e = tid; e < rg * D; e += kT) {
-          const int rr = e % rg, dd = e / rg;  // rows fastest: conflict-free reads
-          const int at = dd * 16 + 4 * ((rr >> 2) ^ ((dd >> 1) & 3)) + (rr & 3);
-          float A = 0.0f;
+        for (int w = 0; w < W; ++w) {
+          const floatx4_t x = *reinterpret_cast<const floatx4_t*>(reinterpret_cast<const float*>(&ring(u)[w][0]) + at);
+          const floatx4_t wt = *reinterpret_cast<const floatx4_t*>(&sm_l[u][w][4 * q]);
 #pragma unroll
-          for (int w = 0; w < W; ++w) A += reinterpret_cast<const float*>(&ring(u)[w][0])[at] * sm_l[u][w][rr];
-          a.part_acc[(slot * R + 16 * gi + rr) * D + dd] = A;
+          for (int i = 0; i < 4; ++i) A[i] += x[i] * wt[i];
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r0q + i < R) a.part_acc[(slot * R + r0q + i) * D + dd] = A[i];
       }
     }
     __syncthreads();
