@@ -290,9 +290,10 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
     mx = xor16_max(mx);
     return xor32_max(mx);
   };
-  // probabilities against the reference, into the sums and the P.V MFMAs
-  auto accumulate = [&](const char* base, const float (&sv)[NG][4]) {
-    short4_t ahi[NG], alo[NG];
+  // probabilities against the reference, into the sums, as bf16 hi + lo
+  // (the A operands of P.V), and the tile's V columns (the B operands)
+  auto probs = [&](const char* base, const float (&sv)[NG][4], short4_t (&ahi)[NG], short4_t (&alo)[NG],
+                   short4_t (&vb)[NT]) {
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       // a row still without a reference (-inf) has no visible key in this
@@ -311,9 +312,11 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
       ahi[gi] = __builtin_bit_cast(short4_t, make_uint2(h01, h23));
       alo[gi] = __builtin_bit_cast(short4_t, make_uint2(l01, l23));
     }
-    short4_t vb[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) vb[n] = lds_read_tr16(base + voff[n]);
+  };
+  // P.V of one tile on 16-key MFMAs
+  auto pv16 = [&](const short4_t (&ahi)[NG], const short4_t (&alo)[NG], const short4_t (&vb)[NT]) {
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
 #pragma unroll
@@ -322,6 +325,34 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
       for (int n = 0; n < NT; ++n) o[gi][n] = mfma16(alo[gi], vb[n], o[gi][n]);
     }
   };
+  // P.V of two tiles on 32-key MFMAs (half the instructions): reduction
+  // index 8 q + j is key 4 q + j of the first tile for j < 4 and key
+  // 4 q + j - 4 of the second for j >= 4, in both operands
+  auto cat8 = [](const short4_t& x, const short4_t& y) {
+    const uint2 a = __builtin_bit_cast(uint2, x), b = __builtin_bit_cast(uint2, y);
+    return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
+  };
+  auto pv32 = [&](const short4_t (&ahi0)[NG], const short4_t (&alo0)[NG], const short4_t (&vb0)[NT],
+                  const short4_t (&ahi1)[NG], const short4_t (&alo1)[NG], const short4_t (&vb1)[NT]) {
+    bf16x8_t vv[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) vv[n] = cat8(vb0[n], vb1[n]);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const bf16x8_t ah = cat8(ahi0[gi], ahi1[gi]), al = cat8(alo0[gi], alo1[gi]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[gi][n] = mfma_bf16(ah, vv[n], o[gi][n]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[gi][n] = mfma_bf16(al, vv[n], o[gi][n]);
+    }
+  };
+  // several row groups (the verify pass): a tile's P.V waits for the next
+  // tile's and both go on 32-key MFMAs (pend: wave-uniform).  A single row
+  // group keeps the 16-key form: its step is latency-bound and the extra
+  // registers measured slower there.
+  constexpr bool kPair = NG >= 2;
+  bool pend = false;
+  short4_t phi[kPair ? NG : 1], plo[kPair ? NG : 1], pvb[kPair ? NT : 1];
 
   // steps issued after local step k (their copies may still be in flight)
   auto newer_than = [&](int k) { return (nst - 1 - k) < (S - 1) ? (nst - 1 - k) : (S - 1); };
@@ -362,8 +393,32 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
       const float mx = fmaxf(fmaxf(sv[gi][0], sv[gi][1]), fmaxf(sv[gi][2], sv[gi][3]));
       over = over || (row_ok[gi] && mx > m[gi] + kSlack);
     }
-    if (__builtin_amdgcn_ballot_w64(over) != 0) rescale(sv);
-    accumulate(&cur[0][0], sv);
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+      if constexpr (kPair) {
+        if (pend) {  // the waiting tile is summed against the old reference first
+          pv16(phi, plo, pvb);
+          pend = false;
+        }
+      }
+      rescale(sv);
+    }
+    short4_t ahi[NG], alo[NG], vb[NT];
+    probs(&cur[0][0], sv, ahi, alo, vb);
+    if constexpr (!kPair) {
+      pv16(ahi, alo, vb);
+    } else if (pend) {
+      pv32(phi, plo, pvb, ahi, alo, vb);
+      pend = false;
+    } else {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        phi[gi] = ahi[gi];
+        plo[gi] = alo[gi];
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) pvb[n] = vb[n];
+      pend = true;
+    }
   };
 
   // stage u of the ring
@@ -394,6 +449,8 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
         ++k;
       }
     }
+    if constexpr (kPair)
+      if (pend) pv16(phi, plo, pvb);
   }
 
   // Folding the waves, S row groups per round: each wave parks the partial
