@@ -48,11 +48,12 @@ namespace {
 constexpr int kSparseMaxChunk = 2048;     // rows per workgroup (LDS offset list)
 constexpr float kSlack = 30.0f;
 
+
 // W waves of 64 lanes, S-tile ring per wave, NG groups of 16 query rows.
 // Query rows of kv head h: r = t * G + g for position t < a.n_pos and group
 // member g < G (decode: one position).  CAUSAL: row r sees keys
 // j <= n - n_pos + t (the verify pass); otherwise every key of the set.
-template <int D, int NG, bool SPARSE, bool CAUSAL, int W, int S, bool LIST>
+template <int D, int NG, bool SPARSE, bool CAUSAL, int W, int S, bool LIST, bool SPLIT = false>
 __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a) {
   using TG = TileGeom<D>;
   constexpr int NI = TG::kNI, TB = TG::kTB, PPR = TG::kPPR, KS = TG::kKS, NT = TG::kNT;
@@ -201,12 +202,38 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
   }
 
   const int nsteps = (rows + kStep - 1) / kStep;
-  const int nst = wave < nsteps ? (nsteps - 1 - wave) / W + 1 : 0;  // this wave's steps
+  // Tiles are dealt in rounds of kR: the first wave on each SIMD (waves
+  // 0..3) takes kA tiles of a round, the second (waves 4..7) kB.  In a
+  // one-row-group step the second wave of a SIMD streams more slowly (its
+  // copies queue behind the first wave's): with even shares it finished
+  // 1.2 us (32K sparse step) to 4.9 us (32K dense step) after the first,
+  // with half the CU's copies in flight meanwhile.  SPLIT (chunks of at
+  // least two rounds) deals 2:1 (gathered rows) or 3:2 (dense); verify rows
+  // measured slower with any uneven split.
+  static_assert(!SPLIT || (W == 8 && NG == 1 && !CAUSAL), "uneven shares for one-row-group steps");
+  constexpr int kA = SPLIT ? (SPARSE ? 2 : 3) : 1, kB = SPLIT ? (SPARSE ? 1 : 2) : 1;
+  constexpr int kR = SPLIT ? 4 * (kA + kB) : W;
+  const bool second = SPLIT && wave >= 4;
+  const int wl = second ? wave - 4 : wave;      // position within its half
+  const int per = second ? kB : kA;             // tiles per round
+  const int base = second ? 4 * kA : 0;         // first slot of its half
+  constexpr int kHalf = SPLIT ? 4 : W;            // waves per half
+  auto tile_of = [&](int k) {  // (constant divisors in either half)
+    if constexpr (!SPLIT) return k * W + wave;
+    return second ? (k / kB) * kR + 4 * kA + (k % kB) * 4 + wl : (k / kA) * kR + (k % kA) * 4 + wl;
+  };
+  int nst;  // this wave's steps
+  {
+    const int full = nsteps / kR, rem = nsteps - full * kR;
+    int extra = (rem - base - wl + kHalf - 1) / kHalf;
+    extra = extra < 0 ? 0 : (extra > per ? per : extra);
+    nst = full * per + extra;
+  }
   const float c2 = a.scale_log2;
 
   // copies of local step k (global step wave + W k) into a stage
   auto issue = [&](char (*stg)[2 * TB], int k) {
-    const int j = wave + W * k;
+    const int j = tile_of(k);
     char* dst = &stg[wave][0];
     if constexpr (SPARSE) {
       uint32_t ro[NI];
@@ -268,7 +295,7 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
       for (int r = 0; r < 4; ++r) sv[gi][r] = cs[gi][r] * c2;
     // masks only on a tile that reaches past the chunk or, in the causal
     // pass, past the first row's last key (wave-uniform test)
-    const int j = wave + W * k;
+    const int j = tile_of(k);
     bool edge = (j + 1) * kStep > rows;
     if constexpr (CAUSAL) edge = edge || r0 + (int64_t)(j + 1) * kStep - 1 > a.n - a.n_pos;
     if (edge) {
@@ -603,6 +630,13 @@ hipError_t launch_k(const AttendArgs& a, hipStream_t s) {
   if constexpr (NG == 1 && !CAUSAL) {
     if (a.narrow) {
       hipLaunchKernelGGL((attend_mfma_kernel<D, NG, SPARSE, CAUSAL, 4, 2, false>), grid, dim3(64 * 4), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (NG == 1 && !CAUSAL && W == 8) {
+    constexpr int kR = SPARSE ? 4 * (2 + 1) : 4 * (3 + 2);  // the uneven split's round of tiles
+    if (a.chunk >= 2 * kR * kStep) {
+      hipLaunchKernelGGL((attend_mfma_kernel<D, NG, SPARSE, CAUSAL, W, S, false, true>), grid, dim3(64 * W), 0, s, a);
       return hipGetLastError();
     }
   }
