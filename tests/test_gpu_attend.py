@@ -131,6 +131,43 @@ def test_attend_sparse_matches_oracle(dtype, hq, hkv, d, n, tail, stride):
     assert np.abs(l[~empty] - ref_l[~empty]).max(initial=0) <= tl
 
 
+@pytest.mark.parametrize("kind,n,tail,count", [
+    ("dense", 20007, None, None),    # chunks of 640 rows (two rounds of the 3:2 dealing), a 167-row last chunk
+    ("dense", 40013, None, None),    # chunks of 1280 rows, a ragged last chunk
+    ("sparse", 16000, 15900, 11000),  # chunks of 384 rows (two rounds of the 2:1 dealing), a ragged last chunk
+    ("sparse", 30011, 29900, 20500),
+])
+def test_uneven_wave_shares_match_oracle(kind, n, tail, count):
+    """Chunks long enough for the uneven tile dealing between the two waves of
+    each SIMD (including partial rounds at the end of a chunk) against the
+    oracle, and a repeated call bit-identical."""
+    hq, hkv, d = 32, 8, 128
+    banner(f"uneven shares {kind} n={n} tail={tail} count={count}")
+    q = _rand((hq, d), 40, "bf16")
+    k = _cache(hkv, n, d, 41, "bf16")
+    v = _cache(hkv, n, d, 42, "bf16")
+    qt, kt, vt = dev(q), dev(k), dev(v)
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n)
+    outs = []
+    for _ in range(2):
+        out = torch.full((hq, d), float("nan"), device="cuda")
+        lse = torch.full((hq,), float("nan"), device="cuda")
+        if kind == "dense":
+            skv.skv_attend_dense(qt, kt, vt, n, out, lse, ws)
+        else:
+            idx, cnt = _random_sets(hkv, tail, count, 43, max_count=count)
+            skv.skv_attend_sparse(qt, kt, vt, n, dev(idx), dev(cnt), tail, out, lse, ws)
+        torch.cuda.synchronize()
+        outs.append((out, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    if kind == "dense":
+        ref_o, ref_l = oracle.attend_dense(q, k, v, n)
+    else:
+        ref_o, ref_l = oracle.attend_sparse(q, k, v, n, idx, cnt, tail)
+    assert np.abs(host(outs[0][0]) - ref_o).max() <= TOL["bf16"][0]
+    assert np.abs(host(outs[0][1]) - ref_l).max() <= TOL["bf16"][1]
+
+
 def select_ws(hkv, n):
     return skv.Workspace.for_problem(skv.problem(hkv, hkv, 128, skv.SKV_BF16, 128, 128), n)
 
