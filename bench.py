@@ -47,6 +47,7 @@ bounded sample of the headline step.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -489,6 +490,32 @@ def main():
     details["llama32k_sparse_frac_of_copy_ceiling"] = round(sp_bytes / (sp_us * 1e-6) / 1e9 / ceil_gbps, 4)
     details["llama32k_dense_frac_of_copy_ceiling"] = round(de_bytes / (de_us * 1e-6) / 1e9 / ceil_gbps, 4)
     del src, dst
+    # streaming-read ceiling: libskvprobe's read kernel (one workgroup per CU,
+    # 16-byte non-temporal loads) over two alternating 1 GiB buffers
+    probe = ctypes.CDLL(os.path.join(os.path.dirname(skv.LIB_PATH), "libskvprobe.so"))
+    probe.skv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    rbufs = [torch.ones(1 << 28, dtype=torch.float32, device="cuda") for _ in range(2)]
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+
+    def read_once(i):
+        if probe.skv_probe_read(rbufs[i % 2].data_ptr(), 1 << 30, sink.data_ptr(), 256,
+                                ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("skv_probe_read failed")
+
+    for i in range(4):
+        read_once(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(10):
+        read_once(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    read_gbps = (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    details["read_ceiling_GBps"] = round(read_gbps, 1)
+    details["llama32k_sparse_frac_of_read_ceiling"] = round(sp_bytes / (sp_us * 1e-6) / 1e9 / read_gbps, 4)
+    details["llama32k_dense_frac_of_read_ceiling"] = round(de_bytes / (de_us * 1e-6) / 1e9 / read_gbps, 4)
+    del rbufs, sink
     torch.cuda.empty_cache()
 
     if args.sections != "headline":

@@ -45,5 +45,19 @@ def build(sources=None, jobs: int | None = None) -> str:
     return LIB
 
 
+PROBE_SRC = "probe_read.hip"
+PROBE_LIB = os.path.join(HERE, "libskvprobe.so")
+
+
+def build_probe() -> str:
+    """Compile and link libskvprobe.so (the bench's streaming-read probe)."""
+    os.makedirs(OBJ, exist_ok=True)
+    obj = _compile(PROBE_SRC)
+    tmp = PROBE_LIB + ".tmp"
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, obj], check=True)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     print(build(sys.argv[1:] or None))
