@@ -570,10 +570,13 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
   }
 }
 
-// The (kv head, chunk) pairs of a gathered-rows call that hold rows, in head
-// order: chunks 0 .. nch_h - 1 of head h, nch_h = clamp(ceil(rows_h / chunk),
-// 1, chunks_per_head), rows_h = clamp(count[h]) + (n - tail_start).  One
-// 1024-thread workgroup; each thread owns consecutive heads.
+// The (kv head, chunk) pairs of a gathered-rows call that hold rows: chunks
+// 0 .. nch_h - 1 of head h, nch_h = clamp(ceil(rows_h / chunk), 1,
+// chunks_per_head), rows_h = clamp(count[h]) + (n - tail_start).  The full
+// chunks of every head come first, in head order, then each head's last
+// chunk: workgroup w takes items w, w + grid, ..., so the long items start
+// first (1024 heads of ragged budgets: 38.6 -> 37.5 us against head order).
+// One 1024-thread workgroup; each thread owns consecutive heads.
 __global__ __launch_bounds__(kSelThreads) void attend_items_kernel(const AttendArgs a) {
   __shared__ uint32_t sm_w[kSelWaves + 1];
   const int tid = threadIdx.x;
@@ -587,22 +590,23 @@ __global__ __launch_bounds__(kSelThreads) void attend_items_kernel(const AttendA
     nc = nc < 1 ? 1 : (nc > cph ? cph : nc);
     return (uint32_t)nc;
   };
-  uint32_t mine = 0;
+  uint32_t mine = 0;  // this thread's heads' chunks before their last
   for (int k = 0; k < per; ++k) {
     const int h = tid * per + k;
-    if (h < H) mine += nch_of(h);
+    if (h < H) mine += nch_of(h) - 1u;
   }
-  uint32_t total;
-  uint32_t base = block_excl_scan(mine, sm_w, &total);
+  uint32_t full;
+  uint32_t base = block_excl_scan(mine, sm_w, &full);
   for (int k = 0; k < per; ++k) {
     const int h = tid * per + k;
     if (h < H) {
       const uint32_t nc = nch_of(h);
-      for (uint32_t c = 0; c < nc; ++c) a.items[base + c] = make_int2(h, (int)c);
-      base += nc;
+      for (uint32_t c = 0; c + 1 < nc; ++c) a.items[base + c] = make_int2(h, (int)c);
+      base += nc - 1u;
+      a.items[full + (uint32_t)h] = make_int2(h, (int)nc - 1);
     }
   }
-  if (tid == 0) *a.n_items = (int32_t)total;
+  if (tid == 0) *a.n_items = (int32_t)(full + (uint32_t)H);
 }
 
 // Eight waves with a two-tile ring (one 128 KB workgroup per CU), the
