@@ -341,10 +341,13 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
   constexpr int kCopies = kFit >= 8 ? 8 : (kFit >= 4 ? 4 : (kFit >= 2 ? 2 : 1));
   static_assert(kFit >= 1, "a histogram and the ranked keys fit the ring");
   // the chunk's local histogram of key bits 31..20: scores are probabilities
-  // in the step (keys >= 2^31: bins 2048..4095), of either sign in SEL
+  // in the step (keys >= 2^31: bins 2048..4095), of either sign in SEL; two
+  // copies (a chunk's 4096 or fewer keys spread over its bins: four copies
+  // measured 0.2 us slower in the 128K step and 0.3 us in SEL, from their
+  // clearing and summing)
   constexpr int kHB = SEL ? 4096 : 2048;
-  constexpr int kFitB = (2 * kW * TB / 4) / kHB;
-  constexpr int kCopiesB = SEL ? (kFitB >= 4 ? 4 : (kFitB >= 2 ? 2 : 1)) : kCopies;
+  constexpr int kCopiesB = 2;
+  static_assert(kCopiesB * kHB <= 2 * kW * TB / 4, "the local histograms fit the ring");
   auto hbin = [](uint32_t k) -> uint32_t { return SEL ? k >> 20 : (k >> 20) & 2047u; };
   // barriers of the head so far when C starts: one (the logits' statistics)
   // in the step, none in SEL
@@ -692,13 +695,16 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
       if (tid == 0) sm_base = 0u;
       __syncthreads();
       if (k1) {
+        // bin d1 holds the keys blo .. bhi (the last bin everything above;
+        // a bin reaching past 2^32 - 1 ends there)
+        const uint32_t blo = lo + (d1 << sh), wb = (1u << sh) - 1u;
+        const uint32_t bhi = d1 == 2047u || blo > 0xFFFFFFFFu - wb ? 0xFFFFFFFFu : blo + wb;
         uint32_t hit = 0;  // bit 4 i + j: slot (i, j) lies in the bin
 #pragma unroll
         for (int i = 0; i < kPubW; ++i) {
           const uint32_t kk[4] = {pk[i].x, pk[i].y, pk[i].z, pk[i].w};
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            hit |= (kk[j] >= lo && min((kk[j] - lo) >> sh, 2047u) == d1 ? 1u : 0u) << (4 * i + j);
+          for (int j = 0; j < 4; ++j) hit |= (kk[j] >= blo && kk[j] <= bhi ? 1u : 0u) << (4 * i + j);
         }
         while (hit) {
           const int b = __builtin_ctz(hit);
@@ -754,16 +760,20 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
     if (valid) {
       // published keys of the chunks before this one, above T and equal to T
       // (summed over the workgroup with the kept-row scan)
+      // (a word's four keys come from one chunk: pub_cap is a multiple of 4)
       const uint32_t e_end = (uint32_t)(c * mcap);
 #pragma unroll
       for (int i = 0; i < kPubW; ++i) {
         const uint32_t kk[4] = {pk[i].x, pk[i].y, pk[i].z, pk[i].w};
+        uint32_t ngt = 0, neq = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bool before = 4u * (uint32_t)(tid + kT * i) + j < e_end;
-          pre_gt += (before && kk[j] > T) ? 1u : 0u;
-          pre_eq += (before && kk[j] == T) ? 1u : 0u;
+          ngt += kk[j] > T ? 1u : 0u;
+          neq += kk[j] == T ? 1u : 0u;
         }
+        const bool before = 4u * (uint32_t)(tid + kT * i) < e_end;
+        pre_gt += before ? ngt : 0u;
+        pre_eq += before ? neq : 0u;
       }
       pub_path = true;
     } else {
