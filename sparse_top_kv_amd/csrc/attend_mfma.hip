@@ -65,8 +65,11 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
   __shared__ __attribute__((aligned(1024))) char st2[W][2 * TB];
   __shared__ __attribute__((aligned(1024))) char st3[W][2 * TB];
   __shared__ __attribute__((aligned(16))) uint32_t sm_off[SPARSE ? kSparseMaxChunk : 1];
-  __shared__ float sm_m[S][W][16];
-  __shared__ __attribute__((aligned(16))) float sm_l[S][W][16];
+  // (max, sum) of each wave's rows per parked row group; a third slot for a
+  // third group parked beside the ring (the fold below)
+  constexpr bool kXQ = NG == 3 && S == 2;
+  __shared__ float sm_m[kXQ ? S + 1 : S][W][16];
+  __shared__ __attribute__((aligned(16))) float sm_l[kXQ ? S + 1 : S][W][16];
   static_assert(S >= 2 && S <= 4, "ring of two to four stages");
   static_assert(16 * D * 4 <= 2 * TB, "a wave's 16-row partial fits its first stage");
   static_assert(!(SPARSE && CAUSAL), "the causal pass is dense");
@@ -485,10 +488,32 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
   // group turn the waves' (max, sum) into the row's max, sum and one weight
   // per wave; then the workgroup folds the waves' accumulators.
   constexpr int GPR = S < NG ? S : NG;  // groups per round
+  // Three row groups on a two-tile ring whose third group holds one row quad
+  // or less (35 or 36 rows: five drafts of seven query heads, nine of four)
+  // fold in one round: that quad is parked in a 16 KB buffer of its own
+  // (items u = GPR below).  Two rounds measured 1 us slower in verify.
+  __shared__ __attribute__((aligned(16))) float st_x[kXQ ? W * 4 * D : 4];
+  const bool xq = kXQ && R <= 16 * GPR + 4;  // uniform
   const int64_t slot = (int64_t)h * cph + c;
 #pragma unroll
   for (int g0 = 0; g0 < NG; g0 += GPR) {
-    if (16 * g0 >= R) break;  // uniform
+    if (16 * g0 >= R || (xq && g0 > 0)) break;  // uniform
+    if constexpr (kXQ) {
+      if (xq) {
+        float lg = l[GPR];
+        lg = xor16_sum(lg);
+        lg = xor32_sum(lg);
+        if (lane < 16) {
+          sm_m[GPR][wave][lane] = nst == 0 ? kNegInf : m[GPR];
+          sm_l[GPR][wave][lane] = nst == 0 ? 0.0f : lg;
+        }
+        if (q4 == 0) {  // rows 16 GPR .. 16 GPR + 3, column-major (4 floats per column)
+          float* xw = &st_x[wave * 4 * D];
+#pragma unroll
+          for (int n = 0; n < NT; ++n) *reinterpret_cast<floatx4_t*>(xw + (16 * n + li) * 4) = o[GPR][n];
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < GPR; ++u) {
       const int gi = g0 + u;
@@ -515,7 +540,8 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
       }
     }
     __syncthreads();
-    if (tid < 16 * GPR) {
+    const int gpr = xq ? GPR + 1 : GPR;  // groups folded in this round
+    if (tid < 16 * gpr) {
       const int u = tid >> 4, rr = tid & 15;
       const int row = 16 * (g0 + u) + rr;
       float M = sm_m[u][0][rr];
@@ -536,15 +562,18 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
     __syncthreads();
     // item (u, row quad q, column dd), columns fastest: each wave's quad is
     // one 16-byte LDS read, and a wave's stores are whole row segments
-    for (int e = tid; e < GPR * 4 * D; e += kT) {
+    // (the parked third group: items GPR 4 D .. GPR 4 D + D - 1, quad 0)
+    for (int e = tid; e < GPR * 4 * D + (xq ? D : 0); e += kT) {
       const int dd = e % D, q = (e / D) % 4, u = e / (4 * D);
       const int gi = g0 + u, r0q = 16 * gi + 4 * q;  // first row of the quad
       if (gi < NG && r0q < R) {
+        const bool xu = kXQ && u == GPR;
         const int at = dd * 16 + 4 * (q ^ ((dd >> 1) & 3));
         float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-          const floatx4_t x = *reinterpret_cast<const floatx4_t*>(reinterpret_cast<const float*>(&ring(u)[w][0]) + at);
+          const floatx4_t x = xu ? *reinterpret_cast<const floatx4_t*>(&st_x[(w * D + dd) * 4])
+                                 : *reinterpret_cast<const floatx4_t*>(reinterpret_cast<const float*>(&ring(u)[w][0]) + at);
           const floatx4_t wt = *reinterpret_cast<const floatx4_t*>(&sm_l[u][w][4 * q]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) A[i] += x[i] * wt[i];

@@ -25,6 +25,18 @@ def _rand(shape, seed):
 @pytest.mark.parametrize("gamma,n", [(5, 5), (5, 300), (1, 77), (5, 3001), (8, 1000), (13, 2000), (16, 777)])
 def test_verify_matches_oracle(hq, hkv, d, gamma, n):
     # gamma * G above 64 rows per kv head runs as several passes
+    _check_verify(hq, hkv, d, gamma, n)
+
+
+@pytest.mark.parametrize("hq,hkv,d,gamma,n", [(16, 4, 128, 9, 700), (16, 4, 64, 9, 1500), (28, 4, 64, 5, 1200),
+                                              (28, 4, 128, 6, 900), (16, 2, 128, 5, 2500)])
+def test_verify_fold_rounds(hq, hkv, d, gamma, n):
+    """35 and 36 rows per kv head fold in one round (the third row group's
+    single row quad parked beside the ring); 40 and 42 rows take two."""
+    _check_verify(hq, hkv, d, gamma, n)
+
+
+def _check_verify(hq, hkv, d, gamma, n):
     banner(f"verify hq={hq} hkv={hkv} d={d} gamma={gamma} n={n}")
     q = _rand((gamma, hq, d), 1)
     k = _rand((hkv, n + 2, d), 2)
