@@ -79,7 +79,7 @@ typedef enum { SKV_F32 = 0, SKV_BF16 = 1 } skv_dtype;
 
 typedef struct {
   int32_t n_q_heads;      /* Hq (layers x heads may be flattened into heads)     */
-  int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0; G = Hq / Hkv in {1,2,4,7,8}    */
+  int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0; G = Hq / Hkv in 1..8 or 16    */
   int32_t head_dim;       /* d in {64, 128}                                       */
   int32_t dtype;          /* skv_dtype of q, K, V                                 */
   float scale;            /* softmax scale on q.k; <= 0 selects 1/sqrt(d)         */

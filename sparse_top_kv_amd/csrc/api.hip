@@ -36,7 +36,8 @@ constexpr int kVerifyMaxGamma = 16;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-bool group_supported(int g) { return g == 1 || g == 2 || g == 4 || g == 7 || g == 8; }
+// query heads per kv head: 1 .. 8 and 16 (the kernels are instantiated per size)
+bool group_supported(int g) { return (g >= 1 && g <= 8) || g == 16; }
 
 int env_int(const char* name, int dflt) {
   const char* v = getenv(name);

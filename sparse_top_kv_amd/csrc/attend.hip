@@ -13,11 +13,14 @@
 // the whole group.  Loads go through buffer descriptors of the head's K and V
 // (SGPRs) with 32-bit lane offsets: dense rows need no per-load address
 // arithmetic (the row step sits in the scalar offset), gathered rows one
-// LDS read.  Logits use packed bf16 dot products (v_dot2c_f32_bf16) and a DPP
+// LDS read.  The library runs it on fp32 caches (bf16 caches take the
+// matrix-core kernel, attend_mfma.hip; the template also reads bf16 rows with
+// packed dot products).  Logits are lane-slice dot products and a DPP
 // reduction over the lanes of a row; softmax runs in the log2 domain in fp32
 // against a reference max fixed from each wave's first block (no rescaling
-// in the steady state); only the last iteration of a chunk pays for masking.  Each workgroup owns `chunk` rows of one kv head and
-// folds its 4 waves into one partial per query head.  The merge runs as a
+// in the steady state); only the last iteration of a chunk pays for masking.
+// Each workgroup owns `chunk` rows of one kv head and folds its waves into
+// one partial per query head.  The merge runs as a
 // second kernel: a completion counter inside this kernel would need a
 // device-scope release per workgroup, which on gfx950 is an L2 write-back plus
 // invalidate that serialises across the workgroups of an XCD.
@@ -33,7 +36,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 // Loads per lane per iteration for each of K and V (fewer for large groups,
 // whose accumulators take the registers).
-constexpr int loads_per_iter(int g) { return g >= 7 ? 2 : 4; }
+constexpr int loads_per_iter(int g) { return g >= 16 ? 1 : (g >= 7 ? 2 : 4); }
 constexpr int kMaxChunk = 2048;        // rows per workgroup (LDS offset list)
 // Probabilities are 2^(logit - reference); the fast loop keeps one reference
 // per wave and query head and leaves for a rescaling loop only when a logit
@@ -357,9 +360,13 @@ hipError_t launch2(int g, bool sparse, const AttendArgs& a, hipStream_t s) {
   switch (g) {
     case 1: return launch3<DT, D, 1>(sparse, a, s);
     case 2: return launch3<DT, D, 2>(sparse, a, s);
+    case 3: return launch3<DT, D, 3>(sparse, a, s);
     case 4: return launch3<DT, D, 4>(sparse, a, s);
+    case 5: return launch3<DT, D, 5>(sparse, a, s);
+    case 6: return launch3<DT, D, 6>(sparse, a, s);
     case 7: return launch3<DT, D, 7>(sparse, a, s);
     case 8: return launch3<DT, D, 8>(sparse, a, s);
+    case 16: return launch3<DT, D, 16>(sparse, a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -377,8 +384,7 @@ int attend_waves() { return kWaves; }
 
 hipError_t launch_attend(int dtype, int d, int g, bool sparse, const AttendArgs& a,
                          hipStream_t s) {
-  if (dtype == 1 && d == 128) return launch2<1, 128>(g, sparse, a, s);
-  if (dtype == 1 && d == 64) return launch2<1, 64>(g, sparse, a, s);
+  // fp32 caches only: bf16 caches run the matrix-core kernel (attend_mfma.hip)
   if (dtype == 0 && d == 128) return launch2<0, 128>(g, sparse, a, s);
   if (dtype == 0 && d == 64) return launch2<0, 64>(g, sparse, a, s);
   return hipErrorInvalidValue;

@@ -369,9 +369,13 @@ hipError_t launch_finalize_g(int g, const ScoreStepArgs& a, hipStream_t s) {
   switch (g) {
     case 1: return launch_finalize<1>(a, s);
     case 2: return launch_finalize<2>(a, s);
+    case 3: return launch_finalize<3>(a, s);
     case 4: return launch_finalize<4>(a, s);
+    case 5: return launch_finalize<5>(a, s);
+    case 6: return launch_finalize<6>(a, s);
     case 7: return launch_finalize<7>(a, s);
     case 8: return launch_finalize<8>(a, s);
+    case 16: return launch_finalize<16>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -406,9 +410,13 @@ hipError_t launch_d(int g, const ScoreStepArgs& a, hipStream_t s) {
   switch (g) {
     case 1: return launch_g<DT, D, 1>(a, s);
     case 2: return launch_g<DT, D, 2>(a, s);
+    case 3: return launch_g<DT, D, 3>(a, s);
     case 4: return launch_g<DT, D, 4>(a, s);
+    case 5: return launch_g<DT, D, 5>(a, s);
+    case 6: return launch_g<DT, D, 6>(a, s);
     case 7: return launch_g<DT, D, 7>(a, s);
     case 8: return launch_g<DT, D, 8>(a, s);
+    case 16: return launch_g<DT, D, 16>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -948,7 +948,7 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
     // x; m is the wave's running maximum (rescaled when a batch raises it).
     const int slot = tid / LPR, piece = tid - slot * LPR;
     const char* vb = a.v + (int64_t)h * a.head_stride_b + piece * 16;
-    constexpr int kU = G <= 4 ? 8 : 4;  // rows per slot in flight
+    constexpr int kU = G <= 4 ? 8 : (G <= 8 ? 4 : 2);  // rows per slot in flight
     uint4 vr[kU];
     uint32_t rr[kU];
 #pragma unroll
@@ -1095,9 +1095,13 @@ hipError_t launch_d(int g, const TopkArgs& a, void* scratch, hipStream_t s) {
   switch (g) {
     case 1: return launch_dg<D, 1>(a, scratch, s);
     case 2: return launch_dg<D, 2>(a, scratch, s);
+    case 3: return launch_dg<D, 3>(a, scratch, s);
     case 4: return launch_dg<D, 4>(a, scratch, s);
+    case 5: return launch_dg<D, 5>(a, scratch, s);
+    case 6: return launch_dg<D, 6>(a, scratch, s);
     case 7: return launch_dg<D, 7>(a, scratch, s);
     case 8: return launch_dg<D, 8>(a, scratch, s);
+    case 16: return launch_dg<D, 16>(a, scratch, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1109,9 +1113,13 @@ int max_chunk_d(int g) {
   switch (g) {
     case 1: return Chunk<D, 1>::kMax;
     case 2: return Chunk<D, 2>::kMax;
+    case 3: return Chunk<D, 3>::kMax;
     case 4: return Chunk<D, 4>::kMax;
+    case 5: return Chunk<D, 5>::kMax;
+    case 6: return Chunk<D, 6>::kMax;
     case 7: return Chunk<D, 7>::kMax;
     case 8: return Chunk<D, 8>::kMax;
+    case 16: return Chunk<D, 16>::kMax;
     default: return 0;
   }
 }

@@ -45,7 +45,7 @@ def _dense(p, n=1000, q=FAKE, ws_bytes=1 << 30, ws=FAKE):
 
 def test_problem_validation():
     assert _dense(_p(hq=30, hkv=8)) == skv.SKV_ERR_INVALID_ARG      # Hq % Hkv
-    assert _dense(_p(hq=24, hkv=8)) == skv.SKV_ERR_UNSUPPORTED      # G = 3
+    assert _dense(_p(hq=72, hkv=8)) == skv.SKV_ERR_UNSUPPORTED      # G = 9
     assert _dense(_p(d=96)) == skv.SKV_ERR_UNSUPPORTED
     assert _dense(_p(dtype=7)) == skv.SKV_ERR_INVALID_ARG
     assert _dense(_p(), q=0) == skv.SKV_ERR_INVALID_ARG             # null
@@ -103,7 +103,7 @@ def test_workspace_size_is_monotone_and_zero_for_bad_problems():
     sizes = [skv.skv_workspace_size(p, n, 32) for n in (1, 100, 2048, 32768, 131072)]
     assert all(a <= b for a, b in zip(sizes, sizes[1:]))
     assert sizes[0] >= skv.SKV_WS_HEADER_BYTES
-    assert skv.skv_workspace_size(_p(hq=24), 100, 1) == 0
+    assert skv.skv_workspace_size(_p(hq=72), 100, 1) == 0  # G = 9
 
 
 def test_budgets_entry_point_equals_oracle():
@@ -161,7 +161,7 @@ def test_noalloc_entry_point_validates_and_bounds_its_scratch():
     not fit its fixed scratch (4096 kv heads x 10,000 rows: about 40 MB)."""
     assert _noalloc(_p(), q=0) == skv.SKV_ERR_INVALID_ARG
     assert _noalloc(_p(), tail=1001) == skv.SKV_ERR_INVALID_ARG
-    assert _noalloc(_p(hq=24, hkv=8)) == skv.SKV_ERR_UNSUPPORTED
+    assert _noalloc(_p(hq=72, hkv=8)) == skv.SKV_ERR_UNSUPPORTED
     big = skv.problem(4096, 4096, 128, skv.SKV_BF16, 10000 * 128, 128)
     assert _noalloc(big, n=10000, idx_stride=9968, tail=9968) == skv.SKV_ERR_WORKSPACE
     # the same call with a caller workspace would need more than the fixed size
@@ -187,7 +187,7 @@ def test_topk_step_validation():
     assert _topk(_p(), count=0) == skv.SKV_ERR_INVALID_ARG
     assert _topk(_p(), n=0) == skv.SKV_ERR_INVALID_ARG
     assert _topk(_p(), q=FAKE + 4) == skv.SKV_ERR_INVALID_ARG
-    assert _topk(_p(hq=24, hkv=8)) == skv.SKV_ERR_UNSUPPORTED
+    assert _topk(_p(hq=72, hkv=8)) == skv.SKV_ERR_UNSUPPORTED
 
 
 def test_topk_error_word_offset_matches_the_header():

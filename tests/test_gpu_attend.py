@@ -29,7 +29,9 @@ def _gpu():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 64), (32, 8, 128), (28, 4, 128), (16, 2, 64), (16, 2, 128)])
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 64), (32, 8, 128), (28, 4, 128), (16, 2, 64), (16, 2, 128),
+                                      # groups of 3, 5, 6 and 16 query heads
+                                      (24, 8, 128), (20, 4, 64), (12, 2, 128), (32, 2, 128), (16, 1, 64)])
 @pytest.mark.parametrize("n", [1, 67, 1000, 5003])
 def test_attend_dense_matches_oracle(dtype, hq, hkv, d, n):
     banner(f"dense {dtype} hq={hq} hkv={hkv} d={d} n={n}")
@@ -107,7 +109,7 @@ def _random_sets(hkv, tail_start, stride, seed, max_count=None):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 64), (32, 8, 128), (28, 4, 128)])
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 64), (32, 8, 128), (28, 4, 128), (24, 8, 128), (30, 6, 64), (32, 2, 128)])
 @pytest.mark.parametrize("n,tail,stride", [(3000, 2900, 700), (5000, 5000, 1500), (800, 0, 16), (100, 90, 90)])
 def test_attend_sparse_matches_oracle(dtype, hq, hkv, d, n, tail, stride):
     banner(f"sparse {dtype} hq={hq} hkv={hkv} d={d} n={n} tail={tail} stride={stride}")
@@ -314,7 +316,8 @@ def test_select_ragged_budgets_and_uniform_scores():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("hq,hkv,d,n", [(8, 8, 64, 2048), (32, 8, 128, 5000), (28, 4, 128, 777), (8, 8, 64, 1)])
+@pytest.mark.parametrize("hq,hkv,d,n", [(8, 8, 64, 2048), (32, 8, 128, 5000), (28, 4, 128, 777), (8, 8, 64, 1),
+                                        (24, 8, 128, 3000), (20, 4, 128, 999), (12, 2, 64, 1500), (32, 2, 128, 4000)])
 def test_score_step_matches_oracle(dtype, hq, hkv, d, n):
     banner(f"score step {dtype} hq={hq} hkv={hkv} d={d} n={n}")
     q = _rand((hq, d), 8, dtype)

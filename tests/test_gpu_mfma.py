@@ -29,10 +29,17 @@ def test_verify_matches_oracle(hq, hkv, d, gamma, n):
 
 
 @pytest.mark.parametrize("hq,hkv,d,gamma,n", [(16, 4, 128, 9, 700), (16, 4, 64, 9, 1500), (28, 4, 64, 5, 1200),
-                                              (28, 4, 128, 6, 900), (16, 2, 128, 5, 2500)])
+                                              (28, 4, 128, 6, 900), (16, 2, 128, 5, 2500), (15, 3, 64, 7, 600)])
 def test_verify_fold_rounds(hq, hkv, d, gamma, n):
     """35 and 36 rows per kv head fold in one round (the third row group's
     single row quad parked beside the ring); 40 and 42 rows take two."""
+    _check_verify(hq, hkv, d, gamma, n)
+
+
+@pytest.mark.parametrize("hq,hkv,d,gamma,n", [(32, 2, 128, 4, 500), (32, 2, 128, 9, 1000), (18, 3, 128, 5, 800),
+                                              (24, 8, 64, 13, 700)])
+def test_verify_other_group_sizes(hq, hkv, d, gamma, n):
+    """Groups of 16 (four queries per pass: one pass, then three), 6 and 3."""
     _check_verify(hq, hkv, d, gamma, n)
 
 
@@ -89,7 +96,7 @@ def test_verify_with_every_logit_far_below_zero(hq, hkv, d, gamma, n):
     assert np.abs(host(lse) - ref_l).max() <= 1e-4
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (28, 4, 128), (4, 4, 64), (8, 1, 128)])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (28, 4, 128), (4, 4, 64), (8, 1, 128), (24, 8, 128), (32, 2, 64)])
 @pytest.mark.parametrize("W,n", [(32, 32), (32, 1000), (2, 300), (32, 4097), (20, 257)])
 def test_obs_score_matches_oracle(hq, hkv, d, W, n):
     banner(f"obs score hq={hq} hkv={hkv} d={d} W={W} n={n}")

@@ -95,6 +95,11 @@ def _check(q, k, v, n, S, R, K, dtype, tag):
     # wave reads the lse of every query head
     (32, 8, 128, 131072, 4, 64, 0),
     (32, 8, 128, 70000, 4, 64, 70000),
+    # groups of 3 (11 keys per thread), 5, 6 and 16 query heads
+    (24, 8, 128, 40000, 4, 64, 3000),
+    (20, 4, 64, 30000, 4, 64, 2000),
+    (12, 2, 128, 9000, 4, 32, 700),
+    (32, 2, 128, 20000, 4, 64, 1500),
 ])
 def test_topk_step_matches_oracle(hq, hkv, d, n, S, R, K):
     q = _rand((hq, d), n + 1, "bf16")
