@@ -104,7 +104,8 @@ skv_status skv_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   score[h * score_stride + j] = (1/n_obs) * sum_{g in group h} sum_i P_{g,i}(j)
  * for j < n (0 for keys no window query sees).  n_obs = 1 is the per-step score
  * of the decode query at position n - 1.  Requires 1 <= n_obs <= n,
- * score_stride >= n. */
+ * score_stride >= n.  bf16 windows run as one matrix-core pass; fp32 windows
+ * as n_obs per-step scores over the rows' prefixes, added in row order. */
 skv_status skv_score(const skv_problem* p, const void* q, int32_t n_obs, const void* k,
                      int64_t n, float* score, int64_t score_stride, void* ws,
                      size_t ws_bytes, void* stream);
@@ -204,9 +205,10 @@ skv_status skv_attend_dense(const skv_problem* p, const void* q, const void* k,
  * one pass over the full cache).  The gamma new entries already occupy
  * positions n - gamma .. n - 1; query t (q [gamma][Hq][d]) sits at n - gamma + t
  * and sees keys [0, n - gamma + t].  out [gamma][Hq][d], lse [gamma][Hq] (may be
- * NULL).  Requires bf16 and 1 <= gamma <= min(n, 16).  A kernel pass holds at
+ * NULL).  Requires 1 <= gamma <= min(n, 16).  bf16: a kernel pass holds at
  * most 64 query rows (gamma * G) per kv head; more run as successive passes of
- * floor(64 / G) queries, each over the prefix its queries see. */
+ * floor(64 / G) queries, each over the prefix its queries see.  fp32: one
+ * decode step per query over its prefix. */
 skv_status skv_verify(const skv_problem* p, const void* q, int32_t gamma, const void* k,
                       const void* v, int64_t n, float* out, float* lse, void* ws,
                       size_t ws_bytes, void* stream);

@@ -190,9 +190,21 @@ PartLayout part_layout(const skv_problem* p, int cph, int rows_per_head) {
   return L;
 }
 
+// Chunk counts are not monotone in the row count: one row more can round the
+// chunk up to the next granule and halve the count (4096 rows of 8 kv heads:
+// 32 chunks of 128; 4097 rows: 17 of 256).  Scratch is therefore sized for
+// the larger of a plan's count and the target count per kv head; that bound
+// never decreases with the rows, so a workspace sized for n_max serves every
+// smaller call (a plan's chunks hold at least rows / target rows unless
+// capped, and capped counts grow with the rows).
+int cph_bound(const skv_problem* p, int cph) {
+  const int want = (target_wgs() + p->n_kv_heads - 1) / p->n_kv_heads;
+  return cph > want ? cph : want;
+}
+
 size_t attend_scratch(const skv_problem* p, const ChunkPlan& cp) {
   const int G = p->n_q_heads / p->n_kv_heads;
-  return part_layout(p, cp.cph, G).end - SKV_WS_HEADER_BYTES;
+  return part_layout(p, cph_bound(p, cp.cph), G).end - SKV_WS_HEADER_BYTES;
 }
 
 skv_status launch_partials_merge(const skv_problem* p, char* base, const PartLayout& L, int cph,
@@ -226,7 +238,13 @@ size_t score_step_scratch(const skv_problem* p, int64_t n) {
   const ChunkPlan cp = score_step_plan(p, n);
   const int G = p->n_q_heads / p->n_kv_heads;
   return align_up((size_t)p->n_q_heads * logits_stride(n) * sizeof(float)) +
-         align_up((size_t)p->n_kv_heads * cp.cph * G * 2 * sizeof(float));
+         align_up((size_t)p->n_kv_heads * cph_bound(p, cp.cph) * G * 2 * sizeof(float));
+}
+
+// fp32 window score: the per-step scratch plus one row block [Hkv][n] that
+// holds each window row's score before it is added in.
+size_t score_window_f32_scratch(const skv_problem* p, int64_t n) {
+  return score_step_scratch(p, n) + align_up((size_t)p->n_kv_heads * logits_stride(n) * sizeof(float));
 }
 
 // Window-score row groups: with few (kv head, key block) workgroups the query
@@ -269,7 +287,7 @@ int32_t verify_pass_queries(const skv_problem* p, int32_t gamma) {
 size_t verify_pass_scratch(const skv_problem* p, int64_t n, int32_t g) {
   const ChunkPlan cp = verify_plan(p, n, g);
   const int G = p->n_q_heads / p->n_kv_heads;
-  return part_layout(p, cp.cph, g * G).end - SKV_WS_HEADER_BYTES;
+  return part_layout(p, cph_bound(p, cp.cph), g * G).end - SKV_WS_HEADER_BYTES;
 }
 
 // Scratch of a whole verify call: its passes run one after another on one
@@ -461,6 +479,61 @@ size_t topk_scratch_bound(const skv_problem* p, int64_t n_max) {
   return skv::topk_step_scratch(p->n_kv_heads, (int)P, G, p->head_dim);
 }
 
+// The launches of a checked dense decode call; `base` is a workspace of at
+// least SKV_WS_HEADER_BYTES + attend_scratch(p, attend_plan(p, n, false)) bytes.
+skv_status run_attend_dense(const skv_problem* p, const void* q, const void* k, const void* v, int64_t n,
+                            float* out, float* lse, char* base, hipStream_t stream) {
+  const ChunkPlan cp = attend_plan(p, n, false);
+  const int G = p->n_q_heads / p->n_kv_heads;
+  const PartLayout L = part_layout(p, cp.cph, G);
+  AttendArgs a{};
+  a.q = q;
+  a.k = (const char*)k;
+  a.v = (const char*)v;
+  a.head_stride_b = p->kv_head_stride * elem_size(p);
+  a.pos_stride_b = p->kv_pos_stride * elem_size(p);
+  a.n = n;
+  a.n_kv_heads = p->n_kv_heads;
+  a.chunk = cp.chunk;
+  a.chunks_per_head = cp.cph;
+  a.scale_log2 = scale_log2(p);
+  a.part_ml = (float*)(base + L.ml);
+  a.part_acc = (float*)(base + L.acc);
+  a.nch = (int32_t*)(base + L.nch);
+  a.group = G;
+  a.n_pos = 1;
+  a.narrow = cp.narrow;
+  const skv_status st = hip_status(launch_attend_any(p, false, a, stream));
+  if (st != SKV_OK) return st;
+  return launch_partials_merge(p, base, L, cp.cph, G, false, out, lse, stream);
+}
+
+// The launches of a checked per-step score call (one query row per query
+// head); `base` is a workspace of at least SKV_WS_HEADER_BYTES +
+// score_step_scratch(p, n) bytes.
+skv_status run_score_step(const skv_problem* p, const void* q, const void* k, int64_t n, float* score,
+                          int64_t score_stride, char* base, hipStream_t stream) {
+  const ChunkPlan cp = score_step_plan(p, n);
+  const int G = p->n_q_heads / p->n_kv_heads;
+  skv::ScoreStepArgs a{};
+  a.q = q;
+  a.k = (const char*)k;
+  a.head_stride_b = p->kv_head_stride * elem_size(p);
+  a.pos_stride_b = p->kv_pos_stride * elem_size(p);
+  a.n = n;
+  a.n_kv_heads = p->n_kv_heads;
+  a.chunk = cp.chunk;
+  a.chunks_per_head = cp.cph;
+  a.scale_log2 = scale_log2(p);
+  a.logits = (float*)(base + SKV_WS_HEADER_BYTES);
+  a.logits_stride = logits_stride(n);
+  a.part_ml = (float*)(base + SKV_WS_HEADER_BYTES +
+                       align_up((size_t)p->n_q_heads * a.logits_stride * sizeof(float)));
+  a.score = score;
+  a.score_stride = score_stride;
+  return hip_status(skv::launch_score_step(p->dtype, p->head_dim, G, a, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -493,6 +566,10 @@ size_t skv_workspace_size(const skv_problem* p, int64_t n_max, int32_t rows_max)
   s = s > t ? s : t;
   t = topk_scratch_bound(p, n_max);
   s = s > t ? s : t;
+  if (p->dtype == SKV_F32 && rows_max > 1) {  // the composed fp32 window score
+    t = score_window_f32_scratch(p, n_max);
+    s = s > t ? s : t;
+  }
   if (p->dtype == SKV_BF16) {
     const int32_t w = rows_max < n_max ? rows_max : (int32_t)n_max;
     t = score_obs_scratch(p, n_max, w);
@@ -519,32 +596,9 @@ skv_status skv_attend_dense(const skv_problem* p, const void* q, const void* k, 
   if (st != SKV_OK) return st;
   if (n < 1 || !q || !out || !aligned16(q) || !aligned16(out)) return SKV_ERR_INVALID_ARG;
   if ((st = check_cache(p, k, n)) != SKV_OK || (st = check_cache(p, v, n)) != SKV_OK) return st;
-  const ChunkPlan cp = attend_plan(p, n, false);
-  if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + attend_scratch(p, cp))) != SKV_OK)
+  if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + attend_scratch(p, attend_plan(p, n, false)))) != SKV_OK)
     return st;
-  const int G = p->n_q_heads / p->n_kv_heads;
-  char* base = (char*)ws;
-  const PartLayout L = part_layout(p, cp.cph, G);
-  AttendArgs a{};
-  a.q = q;
-  a.k = (const char*)k;
-  a.v = (const char*)v;
-  a.head_stride_b = p->kv_head_stride * elem_size(p);
-  a.pos_stride_b = p->kv_pos_stride * elem_size(p);
-  a.n = n;
-  a.n_kv_heads = p->n_kv_heads;
-  a.chunk = cp.chunk;
-  a.chunks_per_head = cp.cph;
-  a.scale_log2 = scale_log2(p);
-  a.part_ml = (float*)(base + L.ml);
-  a.part_acc = (float*)(base + L.acc);
-  a.nch = (int32_t*)(base + L.nch);
-  a.group = G;
-  a.n_pos = 1;
-  a.narrow = cp.narrow;
-  if ((st = hip_status(launch_attend_any(p, false, a, (hipStream_t)stream))) != SKV_OK)
-    return st;
-  return launch_partials_merge(p, base, L, cp.cph, G, false, out, lse, (hipStream_t)stream);
+  return run_attend_dense(p, q, k, v, n, out, lse, (char*)ws, (hipStream_t)stream);
 }
 
 skv_status skv_attend_sparse(const skv_problem* p, const void* q, const void* k, const void* v,
@@ -586,26 +640,30 @@ skv_status skv_score(const skv_problem* p, const void* q, int32_t n_obs, const v
   const int G = p->n_q_heads / p->n_kv_heads;
   char* base = (char*)ws;
   if (n_obs == 1) {
-    const ChunkPlan cp = score_step_plan(p, n);
     if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + score_step_scratch(p, n))) != SKV_OK)
       return st;
-    skv::ScoreStepArgs a{};
-    a.q = q;
-    a.k = (const char*)k;
-    a.head_stride_b = p->kv_head_stride * elem_size(p);
-    a.pos_stride_b = p->kv_pos_stride * elem_size(p);
-    a.n = n;
-    a.n_kv_heads = p->n_kv_heads;
-    a.chunk = cp.chunk;
-    a.chunks_per_head = cp.cph;
-    a.scale_log2 = scale_log2(p);
-    a.logits = (float*)(base + SKV_WS_HEADER_BYTES);
-    a.logits_stride = logits_stride(n);
-    a.part_ml = (float*)(base + SKV_WS_HEADER_BYTES +
-                         align_up((size_t)p->n_q_heads * a.logits_stride * sizeof(float)));
-    a.score = score;
-    a.score_stride = score_stride;
-    return hip_status(skv::launch_score_step(p->dtype, p->head_dim, G, a, (hipStream_t)stream));
+    return run_score_step(p, q, k, n, score, score_stride, base, (hipStream_t)stream);
+  }
+  if (p->dtype == SKV_F32) {
+    // fp32 window: window row i (at position n - n_obs + i) runs as a per-step
+    // score over its prefix of n - n_obs + i + 1 keys into a scratch row block;
+    // the rows are added in order with weight 1 / n_obs (the vector kernels
+    // have no causal window rows)
+    if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + score_window_f32_scratch(p, n))) != SKV_OK)
+      return st;
+    float* rows = (float*)(base + SKV_WS_HEADER_BYTES + score_step_scratch(p, n));
+    const int64_t rs = logits_stride(n);
+    const size_t qrow = (size_t)p->n_q_heads * p->head_dim * sizeof(float);
+    const float w = 1.0f / (float)n_obs;
+    for (int32_t i = 0; i < n_obs; ++i) {
+      const int64_t ni = n - n_obs + i + 1;
+      if ((st = run_score_step(p, (const char*)q + i * qrow, k, ni, rows, rs, base, (hipStream_t)stream)) != SKV_OK)
+        return st;
+      if ((st = hip_status(skv::launch_add_rows(score, score_stride, rows, rs, p->n_kv_heads, ni, n, w, i == 0,
+                                                (hipStream_t)stream))) != SKV_OK)
+        return st;
+    }
+    return SKV_OK;
   }
   if (p->dtype != SKV_BF16) return SKV_ERR_UNSUPPORTED;  // window scoring runs on bf16 MFMA
   if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + score_obs_scratch(p, n, n_obs))) != SKV_OK)
@@ -733,13 +791,26 @@ skv_status skv_verify(const skv_problem* p, const void* q, int32_t gamma, const 
                       size_t ws_bytes, void* stream) {
   skv_status st = check_problem(p);
   if (st != SKV_OK) return st;
-  if (p->dtype != SKV_BF16) return SKV_ERR_UNSUPPORTED;
   if (gamma < 1 || gamma > kVerifyMaxGamma || n < gamma || !q || !out || !aligned16(q) ||
       !aligned16(out))
     return SKV_ERR_INVALID_ARG;
   const int G = p->n_q_heads / p->n_kv_heads;
   if (n > INT32_MAX) return SKV_ERR_UNSUPPORTED;
   if ((st = check_cache(p, k, n)) != SKV_OK || (st = check_cache(p, v, n)) != SKV_OK) return st;
+  if (p->dtype == SKV_F32) {
+    // fp32 caches: drafted position t runs as a decode step over its prefix of
+    // n - gamma + t + 1 entries (the vector kernel has no causal rows); the
+    // dense scratch bound is monotone in the rows, so the longest prefix sizes it
+    if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + attend_scratch(p, attend_plan(p, n, false)))) != SKV_OK)
+      return st;
+    const size_t qrow = (size_t)p->n_q_heads * p->head_dim;
+    for (int32_t t = 0; t < gamma; ++t)
+      if ((st = run_attend_dense(p, (const float*)q + t * qrow, k, v, n - gamma + t + 1, out + t * qrow,
+                                 lse ? lse + (size_t)t * p->n_q_heads : nullptr, (char*)ws,
+                                 (hipStream_t)stream)) != SKV_OK)
+        return st;
+    return SKV_OK;
+  }
   if ((st = check_ws(ws, ws_bytes, SKV_WS_HEADER_BYTES + verify_scratch(p, n, gamma))) != SKV_OK)
     return st;
   // Passes of at most qc queries: pass [t0, t0 + g) holds queries at positions

@@ -143,6 +143,10 @@ size_t select_ws_bytes(int32_t n_kv_heads, int64_t n);
 
 // Fill count words with zero (a kernel, so it may sit in a captured graph).
 hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t stream);
+// y[r][j] += w x[r][j] (j < nx) over `rows` rows; `first` writes instead and
+// clears j in [nx, ny)
+hipError_t launch_add_rows(float* y, int64_t ys, const float* x, int64_t xs, int rows, int64_t nx, int64_t ny,
+                           float w, bool first, hipStream_t stream);
 
 // Verifier-guided top-P retention + uniform fill (skv_select_topp).
 struct ToppArgs {

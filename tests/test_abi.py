@@ -78,12 +78,13 @@ def test_sparse_select_score_verify_validation():
                          _vp(0)) == skv.SKV_ERR_INVALID_ARG
     assert lib.skv_score(b, _vp(FAKE), 101, _vp(FAKE), 100, _vp(FAKE), 100, _vp(FAKE), big,
                          _vp(0)) == skv.SKV_ERR_INVALID_ARG
-    # window scoring and verify need bf16
+    # fp32 window scoring and verify (composed from the vector kernels) check
+    # their workspace before anything is enqueued
     pf = _p(dtype=skv.SKV_F32)
-    assert lib.skv_score(ctypes.byref(pf), _vp(FAKE), 4, _vp(FAKE), 100, _vp(FAKE), 100, _vp(FAKE), big,
-                         _vp(0)) == skv.SKV_ERR_UNSUPPORTED
+    assert lib.skv_score(ctypes.byref(pf), _vp(FAKE), 4, _vp(FAKE), 100, _vp(FAKE), 100, _vp(FAKE), 4096,
+                         _vp(0)) == skv.SKV_ERR_WORKSPACE
     assert lib.skv_verify(ctypes.byref(pf), _vp(FAKE), 4, _vp(FAKE), _vp(FAKE), 100, _vp(FAKE), _vp(0),
-                          _vp(FAKE), big, _vp(0)) == skv.SKV_ERR_UNSUPPORTED
+                          _vp(FAKE), 4096, _vp(0)) == skv.SKV_ERR_WORKSPACE
     # gamma > n, gamma above 16
     assert lib.skv_verify(b, _vp(FAKE), 8, _vp(FAKE), _vp(FAKE), 5, _vp(FAKE), _vp(0), _vp(FAKE), big,
                           _vp(0)) == skv.SKV_ERR_INVALID_ARG

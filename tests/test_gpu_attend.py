@@ -55,6 +55,40 @@ def test_attend_dense_matches_oracle(dtype, hq, hkv, d, n):
     assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_workspace_for_n_max_serves_shorter_calls(dtype):
+    """Chunk counts are not monotone in the rows (8 kv heads: 4096 rows plan
+    32 chunks, 4097 rows 17): a workspace sized for n_max = 4097 must still
+    serve dense, score and verify calls over 4096 rows."""
+    banner(f"workspace bound {dtype}")
+    hq, hkv, d, n_max, n = 32, 8, 128, 4097, 4096
+    q = _rand((hq, d), 50, dtype)
+    k = _cache(hkv, n_max, d, 51, dtype)
+    v = _cache(hkv, n_max, d, 52, dtype)
+    qt, kt, vt = dev(q), dev(k), dev(v)
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n_max, 4)
+    out = torch.full((hq, d), float("nan"), device="cuda")
+    lse = torch.full((hq,), float("nan"), device="cuda")
+    skv.skv_attend_dense(qt, kt, vt, n, out, lse, ws)
+    score = torch.full((hkv, n + 3), float("nan"), device="cuda")
+    skv.skv_score(qt, kt, n, score, ws)
+    q4 = _rand((4, hq, d), 53, dtype)
+    q4t = dev(q4)
+    vo = torch.full((4, hq, d), float("nan"), device="cuda")
+    vl = torch.full((4, hq), float("nan"), device="cuda")
+    skv.skv_verify(q4t, kt, vt, n, vo, vl, ws)
+    torch.cuda.synchronize()
+    to, tl = TOL[dtype]
+    ref_o, ref_l = oracle.attend_dense(q, k, v, n)
+    assert np.abs(host(out) - ref_o).max() <= to
+    assert np.abs(host(lse) - ref_l).max() <= tl
+    s64, _ = oracle.score(q[None], k, n)
+    assert np.all(np.abs(host(score)[:, :n] - s64) <= 1e-4 * s64 + 1e-12)
+    vo_ref, vl_ref = oracle.verify(q4, k, v, n)
+    assert np.abs(host(vo) - vo_ref).max() <= to
+    assert np.abs(host(vl) - vl_ref).max() <= tl
+
+
 @pytest.mark.parametrize("sparse", [False, True])
 def test_softmax_reference_comes_from_this_calls_keys(sparse):
     """Regression: each wave fixes its softmax reference from its first tile.

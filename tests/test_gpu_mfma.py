@@ -160,3 +160,44 @@ def test_window_select_end_to_end_near_ties():
         for j in gs ^ os_:
             assert abs(s64[h, j] - tau) <= 1e-5 * tau + np.finfo(np.float32).tiny
         assert set(w.extra["heavy"][h].tolist()) <= gs
+
+
+@pytest.mark.parametrize("hq,hkv,d,gamma,n", [(28, 4, 128, 5, 300), (32, 8, 64, 16, 777), (8, 8, 128, 1, 77),
+                                              (32, 2, 128, 9, 1000)])
+def test_verify_f32_matches_oracle(hq, hkv, d, gamma, n):
+    """fp32 caches: one decode step per drafted query over its prefix."""
+    banner(f"verify f32 hq={hq} hkv={hkv} d={d} gamma={gamma} n={n}")
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((gamma, hq, d)).astype(np.float32)
+    k = rng.standard_normal((hkv, n + 2, d)).astype(np.float32)
+    v = rng.standard_normal((hkv, n + 2, d)).astype(np.float32)
+    ref_o, ref_l = oracle.verify(q, k, v, n)
+    qt, kt, vt = dev(q), dev(k), dev(v)
+    out = torch.full((gamma, hq, d), float("nan"), device="cuda")
+    lse = torch.full((gamma, hq), float("nan"), device="cuda")
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n, gamma)
+    skv.skv_verify(qt, kt, vt, n, out, lse, ws)
+    torch.cuda.synchronize()
+    assert np.abs(host(out) - ref_o).max() <= 1e-5
+    assert np.abs(host(lse) - ref_l).max() <= 1e-5
+
+
+@pytest.mark.parametrize("hq,hkv,d,W,n", [(32, 8, 128, 32, 1000), (28, 4, 64, 20, 257), (8, 1, 128, 2, 300),
+                                          (16, 1, 64, 5, 4097), (24, 8, 128, 7, 7)])
+def test_obs_score_f32_matches_oracle(hq, hkv, d, W, n):
+    """fp32 window: one per-step score per window row over its prefix, added
+    in row order."""
+    banner(f"obs score f32 hq={hq} hkv={hkv} d={d} W={W} n={n}")
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((W, hq, d)).astype(np.float32)
+    k = rng.standard_normal((hkv, n, d)).astype(np.float32)
+    s64, _ = oracle.score(q, k, n)
+    qt, kt = dev(q), dev(k)
+    score = torch.full((hkv, n + 3), float("nan"), device="cuda")
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n, W)
+    skv.skv_score(qt, kt, n, score, ws)
+    torch.cuda.synchronize()
+    g = host(score)[:, :n]
+    assert np.all(np.isfinite(g))
+    assert np.all(np.abs(g - s64) <= 1e-4 * s64 + 1e-12)
+    np.testing.assert_allclose(g.sum(1), hq // hkv, rtol=1e-4)
