@@ -127,15 +127,19 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
     const int t = row_ok[gi] ? r / G : 0;
     lim[gi] = (int)(a.n - a.n_pos) + t;
   }
+  // (staged rows: loaded here, written to LDS once the first tiles' copies
+  // are issued, so the two loads overlap)
+  constexpr int kQIt = kQInLds ? (NG * 16 * (D / 8) + kT - 1) / kT : 1;
+  uint4 qv[kQIt];
   if constexpr (kQInLds) {
-    for (int e = tid; e < NG * 16 * (D / 8); e += kT) {
-      const int r = e / (D / 8), pc = e - r * (D / 8);
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (r < R) {
+#pragma unroll
+    for (int i = 0; i < kQIt; ++i) {
+      const int e = tid + i * kT, r = e / (D / 8), pc = e - r * (D / 8);
+      qv[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (e < NG * 16 * (D / 8) && r < R) {
         const int t = r / G, g = r - t * G;
-        v = ld16(reinterpret_cast<const char*>(a.q) + (((int64_t)t * Hq + h * G + g) * D + pc * 8) * 2);
+        qv[i] = ld16(reinterpret_cast<const char*>(a.q) + (((int64_t)t * Hq + h * G + g) * D + pc * 8) * 2);
       }
-      *reinterpret_cast<uint4*>(sm_q + r * D * 2 + ((pc ^ swz_q<D>(r)) * 16)) = v;
     }
   } else {
     const int r = li;
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
       }
     }
   }
-  if constexpr (SPARSE || kQInLds) __syncthreads();
+  if constexpr (SPARSE) __syncthreads();  // the row offsets (staged query rows: after the prologue)
 
   const uint32_t span = (uint32_t)(a.n * a.pos_stride_b);
   const BufRsrc rk = make_rsrc(a.k + (int64_t)h * a.head_stride_b, span);
@@ -457,9 +461,29 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
     if (S > 2 && u == 2) return st2;
     return u == 1 ? st1 : st0;
   };
+  // (with staged query rows every prologue copy is issued, also past the
+  // wave's tiles: their count is then known where the rows are written, so
+  // that write waits for the query loads alone; copies past the kv head's
+  // rows read zeros, and a wave with fewer tiles never reads those stages)
 #pragma unroll
   for (int u = 0; u < S - 1; ++u)
-    if (u < nst) issue(ring(u), u);
+    if (kQInLds || u < nst) issue(ring(u), u);
+  // the query rows staged in LDS, behind a barrier taken once the first
+  // tiles' copies are on their way (their addresses need nothing staged), so
+  // the two loads overlap
+  if constexpr (kQInLds) {
+#pragma unroll
+    for (int i = 0; i < kQIt; ++i) {
+      const int e = tid + i * kT, r = e / (D / 8), pc = e - r * (D / 8);
+      if (e < NG * 16 * (D / 8)) *reinterpret_cast<uint4*>(sm_q + r * D * 2 + ((pc ^ swz_q<D>(r)) * 16)) = qv[i];
+    }
+    // an LDS-only barrier: this wave's rows are written (lgkmcnt 0), the
+    // copies keep flying (a full barrier would wait for every wave's tiles)
+    wait_lgkm0();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
   if (nst > 0) {
     // reference: the first tile's max per row; -inf for a row with no
     // visible key there (causal pass), which the first tile that shows the
@@ -488,6 +512,9 @@ __global__ __launch_bounds__(64 * W) void attend_mfma_kernel(const AttendArgs a)
   // group turn the waves' (max, sum) into the row's max, sum and one weight
   // per wave; then the workgroup folds the waves' accumulators.
   constexpr int GPR = S < NG ? S : NG;  // groups per round
+  // (a wave without tiles may still have prologue copies in flight into the
+  // stages the fold parks in)
+  if constexpr (kQInLds) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // Three row groups on a two-tile ring whose third group holds one row quad
   // or less (35 or 36 rows: five drafts of seven query heads, nine of four)
   // fold in one round: that quad is parked in a 16 KB buffer of its own
