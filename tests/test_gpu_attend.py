@@ -57,11 +57,12 @@ def test_attend_dense_matches_oracle(dtype, hq, hkv, d, n):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_workspace_for_n_max_serves_shorter_calls(dtype):
-    """Chunk counts are not monotone in the rows (8 kv heads: 4096 rows plan
-    32 chunks, 4097 rows 17): a workspace sized for n_max = 4097 must still
-    serve dense, score and verify calls over 4096 rows."""
+    """Chunk counts are not monotone in the rows (one kv head: 16384 rows
+    plan 256 chunks of 64, 16385 rows 129 of 128): a workspace sized for
+    n_max = 16385 must still serve dense, score and verify calls over 16384
+    rows."""
     banner(f"workspace bound {dtype}")
-    hq, hkv, d, n_max, n = 32, 8, 128, 4097, 4096
+    hq, hkv, d, n_max, n = 8, 1, 128, 16385, 16384
     q = _rand((hq, d), 50, dtype)
     k = _cache(hkv, n_max, d, 51, dtype)
     v = _cache(hkv, n_max, d, 52, dtype)
