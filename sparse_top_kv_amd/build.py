@@ -18,12 +18,17 @@ SOURCES = ["api.hip", "attend.hip", "attend_mfma.hip", "score_step.hip", "score_
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+# Per-source additions.  topk_step.hip: its single-lane device-scope atomics
+# stay plain atomics (the atomic optimizer would fold each into a wave-wide
+# one whose answer is broadcast at once, waiting for the round trip where the
+# kernel means to read it much later).
+EXTRA_FLAGS = {"topk_step.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _compile(src: str, extra_sources=()) -> str:
     path = src if os.path.isabs(src) else os.path.join(CSRC, src)
     obj = os.path.join(OBJ, os.path.basename(path) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", path, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(os.path.basename(path), []), "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

@@ -863,6 +863,15 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
     // earlier chunks (the selection before this chunk).
     // the forced rows of this thread: sinks and the recent run
     const uint32_t forcedm = interior ? 0u : (run_mask(-r0, nsink - r0) | run_mask(tail - r0, rows));
+    // The selection alone: this workgroup's final arrival goes out now (every
+    // barrier of the head is behind it), its answer is read at the end, and
+    // the scan below takes an LDS-only barrier so that nothing waits for it
+    // meanwhile.  The head's last arrival clears its counters.
+    // (set in thread 0 only: no value for the other lanes to merge with, so
+    // nothing waits for the answer before its use)
+    uint32_t arrived;
+    if constexpr (SEL)
+      if (tid == 0) arrived = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t n_gt = 0, n_eq = 0;
     const uint32_t n_f = (uint32_t)__builtin_popcount(forcedm);
 #pragma unroll
@@ -880,7 +889,14 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
         sm_w2[kW + wave] = x1;
         sm_w[wave] = x2;
       }
-      __syncthreads();
+      if constexpr (SEL) {
+        wait_lgkm0();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      } else {
+        __syncthreads();
+      }
       uint32_t b0 = 0, b1 = 0, t0 = 0, t1 = 0, t2 = 0;
 #pragma unroll
       for (int v = 0; v < kW; ++v) {
@@ -929,14 +945,9 @@ __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const T
         for (int64_t i = tid; i < nsink; i += kT) orow[i] = (int32_t)i;
         if (tid == 0) a.count[h] = (int32_t)(nsink + K);
       }
-      // the head's last arrival (after its last barrier) clears its counters
-      __syncthreads();
-      if (tid == 0) {
-        const uint32_t fin = (nb + 1u) * (uint32_t)P;
-        if (__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == fin - 1u) {
-          st_dev(ctr, 0u);
-          st_dev(ctr + 16, 0u);
-        }
+      if (tid == 0 && arrived == (nb + 1u) * (uint32_t)P - 1u) {
+        st_dev(ctr, 0u);
+        st_dev(ctr + 16, 0u);
       }
       return;
     }
