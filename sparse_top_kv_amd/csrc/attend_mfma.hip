@@ -48,7 +48,6 @@ namespace {
 constexpr int kSparseMaxChunk = 2048;     // rows per workgroup (LDS offset list)
 constexpr float kSlack = 30.0f;
 
-
 // W waves of 64 lanes, S-tile ring per wave, NG groups of 16 query rows.
 // Query rows of kv head h: r = t * G + g for position t < a.n_pos and group
 // member g < G (decode: one position).  CAUSAL: row r sees keys

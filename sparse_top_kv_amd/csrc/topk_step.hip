@@ -316,7 +316,8 @@ __device__ __forceinline__ uint4 buf_load16_dev(BufRsrc r, uint32_t voff) {
 
 // SEL: the selection alone over a given score row (skv_select on long rows
 // with few kv heads): no K stream, no attention; the same exchange and
-// threshold search, with keys of any sign.
+// threshold search, with keys of any sign.  With no merge launch after it,
+// the head's last workgroup to arrive clears the head's counters.
 template <int D, int G, bool SEL>
 __global__ __launch_bounds__(kT) void topk_step_kernel(const TopkArgs a, const TopkWs w) {
   using TG = TileGeom<D>;
