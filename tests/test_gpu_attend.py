@@ -511,3 +511,26 @@ def test_attend_sparse_128k_thirty_percent_long_chunks(kind):
     assert np.abs(host(out) - ref_o).max() <= to
     assert np.abs(host(lse) - ref_l).max() <= tl
     assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [700, 2000, 4000, 8000, 20000])
+def test_merge_load_batches(dtype, n):
+    """One kv head splits the dense key set into up to 256 chunks, so the
+    merge sees every load batch (1, 2, 4 and 8 chunks per lane) and, past
+    64 chunks, several rounds with the running rescale."""
+    banner(f"merge batches {dtype} n={n}")
+    hq, hkv, d = 4, 1, 128
+    q = _rand((hq, d), 60, dtype)
+    k = _cache(hkv, n, d, 61, dtype)
+    v = _cache(hkv, n, d, 62, dtype)
+    ref_o, ref_l = oracle.attend_dense(q, k, v, n)
+    qt, kt, vt = dev(q), dev(k), dev(v)
+    out = torch.full((hq, d), float("nan"), device="cuda")
+    lse = torch.full((hq,), float("nan"), device="cuda")
+    ws = skv.Workspace.for_problem(skv.problem_for(qt, kt), n)
+    skv.skv_attend_dense(qt, kt, vt, n, out, lse, ws)
+    torch.cuda.synchronize()
+    to, tl = TOL[dtype]
+    assert np.abs(host(out) - ref_o).max() <= to
+    assert np.abs(host(lse) - ref_l).max() <= tl
