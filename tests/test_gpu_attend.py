@@ -438,7 +438,8 @@ def test_sparse_with_full_set_equals_dense_and_is_deterministic():
 
 
 @pytest.mark.parametrize("hq,hkv,n,tail,d", [(600, 600, 3000, 2968, 128), (1024, 512, 2100, 2100, 128),
-                                             (700, 700, 1500, 1400, 64)])
+                                             (700, 700, 1500, 1400, 64), (1024, 1024, 2500, 2400, 128),
+                                             (1500, 1500, 1200, 1100, 64)])
 def test_attend_sparse_many_heads_ragged_counts(hq, hkv, n, tail, d):
     """Many kv heads with very uneven kept counts (SparseMM-style budgets,
     empty heads included): the call runs from a device-built work list of
