@@ -48,12 +48,11 @@
  *     enqueued; on a validation error nothing is enqueued.  A failed launch
  *     returns SKV_ERR_HIP.
  *   - Determinism: identical inputs give bit-identical outputs (fixed
- *     reduction orders, no floating-point atomics).
- *   - Tuning: the environment variable SKV_TARGET_WGS (read once, default
- *     256, clamped to [1, 65536]) sets the workgroup count the split-K plans
- *     aim for.  It changes how a key set is cut into chunks, hence the
- *     summation order: results stay deterministic for a fixed setting and
- *     may differ in the last bits between settings.
+ *     reduction orders, no floating-point atomics).  How a key set is cut
+ *     into split-K chunks, hence the summation order, depends only on the
+ *     call's shapes, and for skv_topk_step and the one-launch path of
+ *     skv_select also on the device's compute-unit count (no environment
+ *     variable enters it).
  */
 #ifndef SPARSEKV_H
 #define SPARSEKV_H

@@ -39,20 +39,11 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // query heads per kv head: 1 .. 8 and 16 (the kernels are instantiated per size)
 bool group_supported(int g) { return (g >= 1 && g <= 8) || g == 16; }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
-}
-
 // Workgroup count the split-K attention aims for: one per CU on 256 CUs
 // (measured best on MI355X for 32K-128K; more chunks only add merge work).
-int target_wgs() {
-  static const int t = [] {
-    const int v = env_int("SKV_TARGET_WGS", 256);
-    return v < 1 ? 1 : (v > 65536 ? 65536 : v);
-  }();
-  return t;
-}
+// A constant, so a plan -- and with it the summation order -- depends on the
+// call's shapes alone.
+constexpr int target_wgs() { return 256; }
 
 struct ChunkPlan {
   int chunk;  // rows per workgroup
