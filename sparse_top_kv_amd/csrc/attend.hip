@@ -61,8 +61,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(const AttendArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int cph = a.chunks_per_head;
-  const int h = blockIdx.x / cph;
-  const int c = blockIdx.x - h * cph;
+  const int h = blockIdx.x % a.n_kv_heads;  // a kv head's chunks on one XCD (as the merge)
+  const int c = blockIdx.x / a.n_kv_heads;
 
   // Sparse: the index entries this chunk may use are read in the same round
   // trip as the head's count (entries below idx_stride are always allocated).

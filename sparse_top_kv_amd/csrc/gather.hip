@@ -22,8 +22,8 @@ constexpr int kGatherPieces = kGatherThreads * kGatherIt;   // 16-byte pieces pe
 // of the head's output (row-major, row_bytes / 16 pieces per row): all loads
 // are issued before the first store.
 __global__ __launch_bounds__(kGatherThreads) void gather_kernel(const GatherArgs a, int nblk) {
-  const int h = blockIdx.x / nblk;
-  const int b = blockIdx.x - h * nblk;
+  const int h = blockIdx.x % a.n_kv_heads;  // a kv head's blocks on one XCD
+  const int b = blockIdx.x / a.n_kv_heads;
   // clamped to the rows the output holds (entries are unique and below tail_start)
   int64_t cnt = a.count[h];
   cnt = cnt < 0 ? 0 : (cnt > a.count_max ? a.count_max : cnt);

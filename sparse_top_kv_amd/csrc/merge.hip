@@ -40,8 +40,8 @@ __global__ __launch_bounds__(2 * D) void merge_kernel(const MergeArgs a) {
       a.clear_ctr[32 * i + 16] = 0u;
     }
   const int Rh = a.rows_per_head;
-  const int h = blockIdx.x / Rh;
-  const int r = blockIdx.x - h * Rh;
+  const int h = blockIdx.x % a.n_kv_heads;  // kv head h on the XCD that ran its chunks
+  const int r = blockIdx.x / a.n_kv_heads;
   const int c8 = lane >> 3, col = wave * 8 + (lane & 7);  // col: float4 column
   const float* ml = a.part_ml + ((int64_t)h * a.cph * Rh + r) * 2;   // chunk stride Rh*2
   const float* pa = a.part_acc + ((int64_t)h * a.cph * Rh + r) * D;  // chunk stride Rh*D

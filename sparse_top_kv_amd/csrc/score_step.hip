@@ -35,8 +35,8 @@ __global__ __launch_bounds__(kThreads) void score_logits_kernel(const ScoreStepA
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cph = a.chunks_per_head;
-  const int h = blockIdx.x / cph;
-  const int c = blockIdx.x - h * cph;
+  const int h = blockIdx.x % a.n_kv_heads;  // a kv head's chunks on one XCD
+  const int c = blockIdx.x / a.n_kv_heads;
   const int64_t r0 = (int64_t)c * a.chunk;
   const int64_t rem = a.n - r0;
   const int rows = (int)(rem < 0 ? 0 : (rem > a.chunk ? a.chunk : rem));
@@ -141,8 +141,8 @@ __global__ __launch_bounds__(kThreads) void score_finalize_kernel(const ScoreSte
   static_assert(kFinalizeKeys == kThreads * 8, "eight keys per thread");
   __shared__ float sm_lse2[G];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.x / nblk;
-  const int b = blockIdx.x - h * nblk;
+  const int h = blockIdx.x % a.n_kv_heads;  // on the XCD that ran the head's chunks
+  const int b = blockIdx.x / a.n_kv_heads;
   const int cph = a.chunks_per_head;
   const int64_t nchunks = (a.n + a.chunk - 1) / a.chunk;
   // this thread's eight keys of every head of the group, loaded first (the
@@ -224,8 +224,8 @@ __global__ __launch_bounds__(64 * W) void score_mfma_kernel(const ScoreStepArgs 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, li = lane & 15;
   const int cph = a.chunks_per_head;
-  const int h = blockIdx.x / cph;
-  const int c = blockIdx.x - h * cph;
+  const int h = blockIdx.x % a.n_kv_heads;  // a kv head's chunks on one XCD
+  const int c = blockIdx.x / a.n_kv_heads;
   const int64_t r0 = (int64_t)c * a.chunk;
   const int64_t rem = a.n - r0;
   const int rows = (int)(rem < 0 ? 0 : (rem > a.chunk ? a.chunk : rem));

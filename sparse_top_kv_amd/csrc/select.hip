@@ -459,7 +459,7 @@ __device__ __forceinline__ void pick_bin(const uint32_t (&c)[PER], uint32_t krem
 __global__ __launch_bounds__(kSelThreads) void sel_hist1_kernel(const SelectArgs a) {
   __shared__ uint32_t hist[kBins1];
   const SelWs w = sel_ws(a.ws, a.totals, a.n_kv_heads, a.n);
-  const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
+  const int h = blockIdx.x % a.n_kv_heads, b = blockIdx.x / a.n_kv_heads;  // a head's blocks on one XCD
   const SelGeom g = sel_geom(a, h);
   if (b >= g.nb || !sel_radix(g)) return;
   const int tid = threadIdx.x;
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect_kernel(const SelectAr
   __shared__ uint32_t sm_w[kSelWaves + 1];
   __shared__ uint32_t sm_digit, sm_krem, sm_base;
   const SelWs w = sel_ws(a.ws, a.totals, a.n_kv_heads, a.n);
-  const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
+  const int h = blockIdx.x % a.n_kv_heads, b = blockIdx.x / a.n_kv_heads;  // a head's blocks on one XCD
   const SelGeom g = sel_geom(a, h);
   if (b >= g.nb || !sel_radix(g)) return;
   const int tid = threadIdx.x;
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_write_kernel(const SelectArgs
   __shared__ uint32_t sm_off[kSelThreads + 1];
   __shared__ uint32_t sm_ck[kStageMem];  // bin-d1 keys when they fit (the usual case)
   const SelWs w = sel_ws(a.ws, a.totals, a.n_kv_heads, a.n);
-  const int h = blockIdx.x / w.nbm, b = blockIdx.x - h * w.nbm;
+  const int h = blockIdx.x % a.n_kv_heads, b = blockIdx.x / a.n_kv_heads;  // a head's blocks on one XCD
   const SelGeom g = sel_geom(a, h);
   if (b > 0 && b >= g.nb) return;
   const int tid = threadIdx.x;
